@@ -1,0 +1,27 @@
+"""Compile the CPU oracle (plain C, gcc) into oracle/liboracle.so.
+
+Test infrastructure: the oracle checks the HIP library and is never part of
+it.  Building it here is building the checker, not using it.
+"""
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "kvpop_oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+
+def build(verbose: bool = False) -> str:
+    # -O2 without fast-math: IEEE semantics (NaN compares, exact double sums)
+    cmd = ["gcc", "-std=c11", "-O2", "-fno-fast-math", "-fPIC", "-shared", "-pthread",
+           "-Wall", "-Wextra", "-o", LIB + ".tmp", SRC, "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))
