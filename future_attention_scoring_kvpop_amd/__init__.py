@@ -1,0 +1,234 @@
+"""libkvpop Python binding: argument marshalling over the C ABI in include/kvpop.h.
+
+Every step of the hot path runs in the HIP kernels of ``libkvpop.so``; this
+module only turns torch tensors into device pointers, allocates outputs with
+torch (device memory is torch's plumbing) and passes torch's current stream.
+There is no fallback: if the library is not built, every call raises.
+
+KVpop (arXiv 2607.05061v2), paperlayer.ai summary: App. D.1-D.4 (future
+attention target), App. B.1-B.2 (aggregation, count normalisation), Sec. 3
+and App. C.1 (fixed-budget retention), App. E.2 and E.4 (scorer, delayed
+readout).
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvpop.so")
+
+OK = 0
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
+          3: "workspace too small", 4: "device error"}
+AGG = {"sum": 0, "mean": 1, "max": 2}
+OP_FUTURE_TARGET = 0
+OP_DECODE = 1
+
+EXPORTS = ("kvpop_abi_version", "kvpop_status_string", "kvpop_workspace_bytes", "kvpop_fwd_lse",
+           "kvpop_future_attn_target", "kvpop_evict_select", "kvpop_decode_attend",
+           "kvpop_score_mlp", "kvpop_cache_step")
+
+
+class KvpopError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn}: {STATUS.get(status, status)} (status {status})")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int), ("n_q_heads", ctypes.c_int), ("n_kv_heads", ctypes.c_int),
+                ("seq_len", ctypes.c_int), ("head_dim", ctypes.c_int), ("scale", ctypes.c_float)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libkvpop.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libkvpop.so not built at {LIB_PATH}: run __graft_entry__.build() "
+                               "or python future_attention_scoring_kvpop_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        DP = ctypes.POINTER(Dims)
+        sig = {
+            "kvpop_abi_version": (I, []),
+            "kvpop_status_string": (ctypes.c_char_p, [I]),
+            "kvpop_workspace_bytes": (Z, [I, DP, I]),
+            "kvpop_fwd_lse": (I, [DP, P, P, P, P]),
+            "kvpop_future_attn_target": (I, [DP, P, P, P, I, I, I, I, P, P, P, Z, P]),
+            "kvpop_evict_select": (I, [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P]),
+            "kvpop_decode_attend": (I, [DP, P, P, P, P, P, I, P, P, Z, P]),
+            "kvpop_score_mlp": (I, [I, I, I, I, I, P, P, P, P, P, P, P]),
+            "kvpop_cache_step": (I, [I, I, I, I, I, I, I, I, P, P, P, P, P, P, I, P, P, P, P, P, P]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(fn, st):
+    if st != OK:
+        raise KvpopError(fn, st)
+
+
+def _need(t, dtype, name, ndim=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name}: expected a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name}: expected {ndim} dims, got {t.dim()}")
+
+
+def dims(B, Hq, Hkv, S, D, scale=0.0):
+    return Dims(B, Hq, Hkv, S, D, float(scale))
+
+
+def workspace_bytes(op, d, window=0):
+    return int(lib().kvpop_workspace_bytes(op, ctypes.byref(d), int(window)))
+
+
+def fwd_lse(q, k, scale=0.0, out=None):
+    """Dense causal log-normalizers LSE [B,Hq,S] fp32 (App. D.1, D.4)."""
+    _need(q, torch.bfloat16, "q", 4)
+    _need(k, torch.bfloat16, "k", 4)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, S, D):
+        raise ValueError("k shape mismatch")
+    lse = out if out is not None else torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    _need(lse, torch.float32, "lse")
+    d = dims(B, Hq, Hkv, S, D, scale)
+    _check("kvpop_fwd_lse", lib().kvpop_fwd_lse(ctypes.byref(d), _p(q), _p(k), _p(lse), _stream()))
+    return lse
+
+
+def future_attn_target(q, k, lse, window, lookahead=-1, agg="sum", count_normalize=False,
+                       per_qhead=False, scale=0.0, out=None, workspace=None):
+    """Future-attention mass [B,Hkv,S] (and per-query-head [B,Hq,S]) (App. D.2, B.1-B.2)."""
+    _need(q, torch.bfloat16, "q", 4)
+    _need(k, torch.bfloat16, "k", 4)
+    _need(lse, torch.float32, "lse", 3)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, S, D) or tuple(lse.shape) != (B, Hq, S):
+        raise ValueError("shape mismatch")
+    d = dims(B, Hq, Hkv, S, D, scale)
+    mass = out if out is not None else torch.empty((B, Hkv, S), dtype=torch.float32, device=q.device)
+    ph = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device) if per_qhead else None
+    nbytes = workspace_bytes(OP_FUTURE_TARGET, d, window)
+    ws = workspace if workspace is not None else torch.empty(max(nbytes, 256), dtype=torch.uint8,
+                                                             device=q.device)
+    st = lib().kvpop_future_attn_target(ctypes.byref(d), _p(q), _p(k), _p(lse), int(window),
+                                        int(lookahead), AGG[agg], int(bool(count_normalize)),
+                                        _p(mass), _p(ph), _p(ws), ws.numel() * ws.element_size(),
+                                        _stream())
+    _check("kvpop_future_attn_target", st)
+    return (mass, ph) if per_qhead else mass
+
+
+def evict_select(scores, n_sink, window, budget, k=None, v=None, want_score=True,
+                 out_pos=None, out_score=None, out_k=None, out_v=None):
+    """Retention (Sec. 3, App. C.1): slot_pos [B,Hkv,budget] int32, slot_score, and the
+    compacted bf16 caches when k, v are given."""
+    _need(scores, torch.float32, "scores", 3)
+    B, Hkv, S = scores.shape
+    dev = scores.device
+    D = 0
+    if k is not None:
+        _need(k, torch.bfloat16, "k", 4)
+        _need(v, torch.bfloat16, "v", 4)
+        D = k.shape[-1]
+    sp = out_pos if out_pos is not None else torch.empty((B, Hkv, budget), dtype=torch.int32, device=dev)
+    ss = out_score if out_score is not None else (
+        torch.empty((B, Hkv, budget), dtype=torch.float32, device=dev) if want_score else None)
+    kc = vc = None
+    if k is not None:
+        kc = out_k if out_k is not None else torch.empty((B, Hkv, budget, D), dtype=torch.bfloat16, device=dev)
+        vc = out_v if out_v is not None else torch.empty((B, Hkv, budget, D), dtype=torch.bfloat16, device=dev)
+    st = lib().kvpop_evict_select(B, Hkv, S, D, int(n_sink), int(window), int(budget), _p(scores),
+                                  _p(k), _p(v), _p(sp), _p(ss), _p(kc), _p(vc), _stream())
+    _check("kvpop_evict_select", st)
+    return sp, ss, kc, vc
+
+
+def decode_attend(q, k_cache, v_cache, slot_pos, out_dtype=torch.float32, want_lse=True,
+                  scale=0.0, out=None, out_lse=None, workspace=None):
+    """Decode attention over the bounded cache (Sec. 3, App. C.1): o [B,Hq,D], lse [B,Hq]."""
+    _need(q, torch.bfloat16, "q", 3)
+    _need(k_cache, torch.bfloat16, "k_cache", 4)
+    _need(v_cache, torch.bfloat16, "v_cache", 4)
+    _need(slot_pos, torch.int32, "slot_pos", 3)
+    B, Hq, D = q.shape
+    Hkv, n = k_cache.shape[1], k_cache.shape[2]
+    d = dims(B, Hq, Hkv, n, D, scale)
+    o = out if out is not None else torch.empty((B, Hq, D), dtype=out_dtype, device=q.device)
+    lse = out_lse if out_lse is not None else (
+        torch.empty((B, Hq), dtype=torch.float32, device=q.device) if want_lse else None)
+    nbytes = workspace_bytes(OP_DECODE, d)
+    ws = workspace if workspace is not None else (
+        torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None)
+    st = lib().kvpop_decode_attend(ctypes.byref(d), _p(q), _p(k_cache), _p(v_cache), _p(slot_pos),
+                                   _p(o), 1 if o.dtype == torch.bfloat16 else 0, _p(lse), _p(ws),
+                                   0 if ws is None else ws.numel(), _stream())
+    _check("kvpop_decode_attend", st)
+    return o, lse
+
+
+def score_mlp(keys, w1, b1, w2, b2, out=None):
+    """Headwise MLP scores of keys [B,Hkv,n,D] -> [B,Hkv,n] fp32 (App. E.2)."""
+    _need(keys, torch.bfloat16, "keys", 4)
+    for t, n in ((w1, "w1"), (b1, "b1"), (w2, "w2"), (b2, "b2")):
+        _need(t, torch.float32, n)
+    B, Hkv, n, D = keys.shape
+    hidden = w1.shape[1]
+    sc = out if out is not None else torch.empty((B, Hkv, n), dtype=torch.float32, device=keys.device)
+    st = lib().kvpop_score_mlp(B, Hkv, n, D, hidden, _p(keys), _p(w1), _p(b1), _p(w2), _p(b2),
+                               _p(sc), _stream())
+    _check("kvpop_score_mlp", st)
+    return sc
+
+
+def cache_step(k_cache, v_cache, slot_pos, slot_score, k_new, v_new, pos_q, n_sink, window,
+               delay, mlp=None, scores_r=None):
+    """One bounded-cache decode step in place (Sec. 3, App. C.1, App. E.4).
+
+    mlp: (w1, b1, w2, b2) to score token pos_q - delay from its cached key, or
+    scores_r [B,Hkv] fp32 to supply that score directly.
+    """
+    _need(k_cache, torch.bfloat16, "k_cache", 4)
+    _need(v_cache, torch.bfloat16, "v_cache", 4)
+    _need(slot_pos, torch.int32, "slot_pos", 3)
+    _need(slot_score, torch.float32, "slot_score", 3)
+    _need(k_new, torch.bfloat16, "k_new", 3)
+    _need(v_new, torch.bfloat16, "v_new", 3)
+    B, Hkv, budget, D = k_cache.shape
+    w1 = b1 = w2 = b2 = None
+    hidden = 0
+    if mlp is not None:
+        w1, b1, w2, b2 = mlp
+        hidden = w1.shape[1]
+    if scores_r is not None:
+        _need(scores_r, torch.float32, "scores_r")
+    st = lib().kvpop_cache_step(B, Hkv, D, int(n_sink), int(window), budget, int(delay), int(pos_q),
+                                _p(k_new), _p(v_new), _p(w1), _p(b1), _p(w2), _p(b2), hidden,
+                                _p(scores_r), _p(k_cache), _p(v_cache), _p(slot_pos),
+                                _p(slot_score), _stream())
+    _check("kvpop_cache_step", st)

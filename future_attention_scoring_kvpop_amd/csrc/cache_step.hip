@@ -1,0 +1,257 @@
+// cache_step.hip -- headwise MLP scorer and the bounded-cache decode step.
+//
+// KVpop summary (arXiv 2607.05061v2):
+//   * App. E.2: stateless headwise MLP scorers score each token on its own
+//     from cached quantities; here the input is the token's key, and the
+//     scorer is W1 (hidden x D), GELU, then a scalar output layer.
+//   * Sec. 3 and App. E.4: a token need not be scored when it enters the
+//     cache; scoring may be deferred while it sits in the protected window,
+//     and the keep-or-drop decision is taken when it leaves the window (at
+//     query q the newly eligible token is u = q - w).
+//   * App. C.1: the cache holds B = s + w + k entries per head.
+//
+// gfx950 mapping
+//   * The MLP of one token runs on one wave: lane j owns hidden units j,
+//     j+64, ...; W1 is staged through LDS with a padded row so the lane-
+//     varying reads are conflict free; the output layer is a fixed xor
+//     butterfly, so every kernel that scores a token produces the same bits.
+//   * The decode step is one 256-thread workgroup per (b, h): a strided scan
+//     of the long-range slots finds the first empty slot and the worst kept
+//     token, one thread applies the decision, and the same threads move the
+//     exiting row and write the new row (16 bytes each), so no thread reads
+//     global memory another thread of the step has written.
+#include "common.h"
+#include "launch.h"
+
+namespace kvpop {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float gelu_erf(float x) {
+  return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+}
+
+// Score of one key by one wave.  key: D floats in LDS; w1s: LDS copy of the
+// head's W1 with row stride D+1.  Returns the same value in every lane.
+__device__ __forceinline__ float mlp_wave(const float* key, const float* w1s, int D, int hidden,
+                                          const float* __restrict__ b1,
+                                          const float* __restrict__ w2, float b2, int lane) {
+  float part = 0.f;
+  for (int j = lane; j < hidden; j += 64) {
+    const float* wr = w1s + j * (D + 1);
+    float a = b1[j];
+    for (int cc = 0; cc < D; ++cc) a = fmaf(wr[cc], key[cc], a);
+    part = fmaf(w2[j], gelu_erf(a), part);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) part = part + __shfl_xor(part, off);
+  return part + b2;
+}
+
+// LDS written by lanes of one wave becomes visible to the other lanes of the
+// same wave (no workgroup barrier: waves of a block walk different tokens).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ void stage_w1(float* w1s, const float* __restrict__ w1, int D,
+                                         int hidden) {
+  for (int e = threadIdx.x; e < hidden * D; e += blockDim.x) {
+    const int j = e / D, cc = e % D;
+    w1s[j * (D + 1) + cc] = w1[e];
+  }
+}
+
+// Prefix scorer: one workgroup per (b, h, block of tokens); each wave walks
+// its tokens one at a time.
+__global__ __launch_bounds__(kThreads) void score_mlp_kernel(
+    const bf16_t* __restrict__ keys, const float* __restrict__ w1, const float* __restrict__ b1,
+    const float* __restrict__ w2, const float* __restrict__ b2, float* __restrict__ scores,
+    int Hkv, int n_tok, int D, int hidden, int tok_per_block, int blocks_per_row) {
+  extern __shared__ float smem[];
+  float* w1s = smem;                               // hidden * (D+1)
+  float* keyb = smem + hidden * (D + 1);           // 4 waves * D
+  const int bh = blockIdx.x / blocks_per_row;
+  const int blk = blockIdx.x % blocks_per_row;
+  const int h = bh % Hkv;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  stage_w1(w1s, w1 + (size_t)h * hidden * D, D, hidden);
+  __syncthreads();
+  const int t_begin = blk * tok_per_block;
+  const int t_end = min(n_tok, t_begin + tok_per_block);
+  float* kw = keyb + wave * D;
+  for (int t = t_begin + wave; t < t_end; t += 4) {
+    const bf16_t* kr = keys + ((size_t)bh * n_tok + t) * D;
+    for (int cc = lane; cc < D; cc += 64) kw[cc] = __uint_as_float((uint32_t)kr[cc] << 16);
+    wave_lds_sync();
+    const float sc = mlp_wave(kw, w1s, D, hidden, b1 + (size_t)h * hidden, w2 + (size_t)h * hidden,
+                              b2[h], lane);
+    if (lane == 0) scores[(size_t)bh * n_tok + t] = sc;
+    wave_lds_sync();  // kw is rewritten by the next token of this wave
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void cache_step_kernel(
+    int D, int n_sink, int window, int budget, int delay, int pos_q,
+    const bf16_t* __restrict__ k_new, const bf16_t* __restrict__ v_new,
+    const float* __restrict__ w1, const float* __restrict__ b1, const float* __restrict__ w2,
+    const float* __restrict__ b2, int hidden, const float* __restrict__ scores_r,
+    bf16_t* __restrict__ kc, bf16_t* __restrict__ vc, int32_t* __restrict__ slot_pos,
+    float* __restrict__ slot_score, int Hkv) {
+  extern __shared__ float smem[];
+  __shared__ int red_empty[kThreads / 64];
+  __shared__ int red_worst[kThreads / 64];
+  __shared__ int sh_dst;
+
+  const long row = blockIdx.x;  // b * Hkv + h
+  const int h = (int)(row % Hkv);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kk = budget - n_sink - window;
+  int32_t* sp = slot_pos + row * budget;
+  float* ss = slot_score + row * budget;
+  bf16_t* kr = kc + row * (size_t)budget * D;
+  bf16_t* vr = vc + row * (size_t)budget * D;
+  const int cpr = D / 8;
+  const int q = pos_q;
+
+  // ---- (a) the token leaving the window ----
+  const int u = q - window;
+  if (u >= n_sink) {
+    const int ring_u = n_sink + kk + (u % window);
+    int first_empty = 0x7fffffff, worst = -1;
+    uint32_t wkey = 0;
+    int wpos = 0;
+    for (int j = n_sink + tid; j < n_sink + kk; j += kThreads) {
+      const int p = sp[j];
+      if (p < 0) {
+        first_empty = min(first_empty, j);
+      } else {
+        const uint32_t key = rank_key(ss[j]);
+        if (worst < 0 || key < wkey || (key == wkey && p > wpos)) {
+          worst = j;
+          wkey = key;
+          wpos = p;
+        }
+      }
+    }
+    // wave reduction, then across waves
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const int fe = __shfl_xor(first_empty, off);
+      first_empty = min(first_empty, fe);
+      const int ow = __shfl_xor(worst, off);
+      const uint32_t ok = (uint32_t)__shfl_xor((int)wkey, off);
+      const int op = __shfl_xor(wpos, off);
+      if (ow >= 0 && (worst < 0 || ok < wkey || (ok == wkey && op > wpos))) {
+        worst = ow;
+        wkey = ok;
+        wpos = op;
+      }
+    }
+    if (lane == 0) {
+      red_empty[wave] = first_empty;
+      red_worst[wave] = worst;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int fe = 0x7fffffff, wv = -1;
+      uint32_t wk = 0;
+      int wp = 0;
+      for (int w = 0; w < kThreads / 64; ++w) {
+        fe = min(fe, red_empty[w]);
+        const int cand = red_worst[w];
+        if (cand >= 0) {
+          const uint32_t ck = rank_key(ss[cand]);
+          const int cp = sp[cand];
+          if (wv < 0 || ck < wk || (ck == wk && cp > wp)) {
+            wv = cand;
+            wk = ck;
+            wp = cp;
+          }
+        }
+      }
+      int dst = -1;
+      if (fe != 0x7fffffff) {
+        dst = fe;
+      } else if (wv >= 0) {
+        const uint32_t uk = rank_key(ss[ring_u]);
+        if (uk > wk || (uk == wk && u < wp)) dst = wv;
+      }
+      if (dst >= 0) {
+        sp[dst] = sp[ring_u];
+        ss[dst] = ss[ring_u];
+      }
+      sh_dst = dst;
+    }
+    __syncthreads();
+    const int dst = sh_dst;
+    if (dst >= 0) {
+      if (tid < cpr) stg16(kr + (size_t)dst * D + tid * 8, ldg16(kr + (size_t)ring_u * D + tid * 8));
+      else if (tid < 2 * cpr)
+        stg16(vr + (size_t)dst * D + (tid - cpr) * 8, ldg16(vr + (size_t)ring_u * D + (tid - cpr) * 8));
+    }
+  }
+
+  // ---- (b) append the new token ----
+  const int slot = q < n_sink ? q : n_sink + kk + (q % window);
+  if (tid < cpr) stg16(kr + (size_t)slot * D + tid * 8, ldg16(k_new + row * D + tid * 8));
+  else if (tid < 2 * cpr)
+    stg16(vr + (size_t)slot * D + (tid - cpr) * 8, ldg16(v_new + row * D + (tid - cpr) * 8));
+  if (tid == 0) {
+    sp[slot] = q;
+    ss[slot] = __uint_as_float(0x7fc00000u);
+  }
+
+  // ---- (c) delayed scoring of token r = q - delay ----
+  const int r = q - delay;
+  if (r >= n_sink) {
+    const int rslot = n_sink + kk + (r % window);
+    float sc;
+    if (w1 == nullptr) {
+      sc = scores_r[row];
+    } else {
+      float* w1s = smem;
+      float* key = smem + hidden * (D + 1);
+      stage_w1(w1s, w1 + (size_t)h * hidden * D, D, hidden);
+      const bf16_t* ksrc = r == q ? k_new + row * D : kr + (size_t)rslot * D;
+      for (int cc = tid; cc < D; cc += kThreads) key[cc] = __uint_as_float((uint32_t)ksrc[cc] << 16);
+      __syncthreads();
+      sc = 0.f;
+      if (wave == 0) sc = mlp_wave(key, w1s, D, hidden, b1 + (size_t)h * hidden, w2 + (size_t)h * hidden, b2[h], lane);
+    }
+    if (tid == 0) ss[rslot] = sc;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_score_mlp(int B, int Hkv, int n_tok, int D, int hidden, const void* keys,
+                            const float* w1, const float* b1, const float* w2, const float* b2,
+                            float* scores, hipStream_t st) {
+  if (n_tok == 0) return hipSuccess;
+  const int tok_per_block = 256;
+  const int bpr = (n_tok + tok_per_block - 1) / tok_per_block;
+  const size_t smem = sizeof(float) * ((size_t)hidden * (D + 1) + 4 * D);
+  hipLaunchKernelGGL(score_mlp_kernel, dim3(B * Hkv * bpr), dim3(kThreads), smem, st,
+                     (const bf16_t*)keys, w1, b1, w2, b2, scores, Hkv, n_tok, D, hidden,
+                     tok_per_block, bpr);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_step(int B, int Hkv, int D, int n_sink, int window, int budget,
+                             int delay, int pos_q, const void* k_new, const void* v_new,
+                             const float* w1, const float* b1, const float* w2,
+                             const float* b2, int hidden, const float* scores_r, void* kc,
+                             void* vc, int32_t* slot_pos, float* slot_score, hipStream_t st) {
+  const size_t smem = w1 ? sizeof(float) * ((size_t)hidden * (D + 1) + D) : 0;
+  hipLaunchKernelGGL(cache_step_kernel, dim3(B * Hkv), dim3(kThreads), smem, st, D, n_sink,
+                     window, budget, delay, pos_q, (const bf16_t*)k_new, (const bf16_t*)v_new, w1,
+                     b1, w2, b2, hidden, scores_r, (bf16_t*)kc, (bf16_t*)vc, slot_pos, slot_score,
+                     Hkv);
+  return hipGetLastError();
+}
+
+}  // namespace kvpop

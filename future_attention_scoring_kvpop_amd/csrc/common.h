@@ -1,0 +1,69 @@
+// common.h -- device helpers shared by the libkvpop HIP kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvpop {
+
+typedef uint16_t bf16_t;  // raw bf16 bits in memory
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// 16 contiguous bytes (8 bf16) as an MFMA operand fragment.
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
+  bf16x8 r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+}
+
+__device__ __forceinline__ uint4 ldg16(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+__device__ __forceinline__ void stg16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// 32x32x16 bf16 MFMA, fp32 accumulate.  Operand fragments: lane l holds
+// A[m = l%32][8*(l/32) .. +8) and B[8*(l/32) .. +8)[n = l%32]; the result
+// register r of lane l is D[8*(r/4) + 4*(l/32) + r%4][l%32].
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Blocks are dispatched round-robin over the 8 XCDs (block i runs on XCD
+// i % 8).  Renumber so that each XCD receives one contiguous range of
+// logical work items: neighbouring items then share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int i, int n) {
+  const int q = n >> 3, r = n & 7;
+  const int x = i & 7, j = i >> 3;
+  return x * q + (x < r ? x : r) + j;
+}
+
+// Order-preserving map of fp32 onto uint32 for ranking: larger key = ranks
+// first.  -0.0 and +0.0 share one key; every NaN maps to 0, below -inf.
+__device__ __forceinline__ uint32_t rank_key(float f) {
+  if (f != f) return 0u;
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) == 0u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace kvpop

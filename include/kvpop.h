@@ -1,0 +1,205 @@
+/*
+ * kvpop.h -- C ABI of libkvpop, the MI355X (gfx950) hot path of KVpop.
+ *
+ * Method: "KVpop -- Key-Value Cache Compression with Predictive Online
+ * Pruning" (arXiv 2607.05061v2), as summarised on paperlayer.ai.  Section
+ * names below are that page's.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers are DEVICE pointers owned by the caller; the library never
+ *   allocates, frees, synchronises or keeps a pointer past the call.  Every
+ *   call is asynchronous on `stream` (0 = the null stream): buffers must stay
+ *   alive until the stream has finished the work.
+ * - Layouts are dense and row-major, head-major:
+ *     Q   [B][Hq][S][D]   bf16          K, V [B][Hkv][S][D] bf16
+ *     LSE [B][Hq][S]      fp32 (natural log)
+ *   Query head g reads KV head g / (Hq / Hkv) (grouped-query attention).
+ * - bf16 is the raw 16-bit brain-float format; fp32 is IEEE binary32.
+ * - Device pointers must be 16-byte aligned (fp32 score/mass/LSE arrays
+ *   4-byte aligned).
+ * - Errors: all argument checks run on the host before any launch and
+ *   return KVPOP_ERR_INVALID_ARGUMENT / KVPOP_ERR_UNSUPPORTED /
+ *   KVPOP_ERR_WORKSPACE_TOO_SMALL without touching the GPU.  A failed launch
+ *   returns KVPOP_ERR_DEVICE.  Faults during execution surface at the next
+ *   stream synchronisation, as for any HIP work.
+ * - Calls keep no global state and may be issued concurrently on different
+ *   streams with disjoint outputs.
+ * - Supported head dims: 64 and 128.  Hq must be a multiple of Hkv and
+ *   128 must be a multiple of Hq/Hkv (group sizes 1, 2, 4, ..., 128).
+ */
+#ifndef KVPOP_H
+#define KVPOP_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVPOP_ABI_VERSION 1
+
+typedef enum {
+    KVPOP_OK = 0,
+    KVPOP_ERR_INVALID_ARGUMENT = 1,
+    KVPOP_ERR_UNSUPPORTED = 2,
+    KVPOP_ERR_WORKSPACE_TOO_SMALL = 3,
+    KVPOP_ERR_DEVICE = 4
+} kvpop_status;
+
+/* Aggregation of the per-query-head future mass over a KV-head group
+ * (App. B.1: max is the paper's default, a probability-space mean the
+ * alternative; SUM is the plain total over the group). */
+typedef enum { KVPOP_AGG_SUM = 0, KVPOP_AGG_MEAN = 1, KVPOP_AGG_MAX = 2 } kvpop_agg;
+
+typedef enum { KVPOP_OUT_F32 = 0, KVPOP_OUT_BF16 = 1 } kvpop_out_dtype;
+
+typedef struct {
+    int batch;       /* B   */
+    int n_q_heads;   /* Hq  */
+    int n_kv_heads;  /* Hkv */
+    int seq_len;     /* S (for decode: the number of cache slots) */
+    int head_dim;    /* D: 64 or 128 */
+    float scale;     /* softmax scale; <= 0 selects 1/sqrt(D) */
+} kvpop_dims;
+
+/* Workspace sizes (bytes) for the calls that take one. */
+#define KVPOP_OP_FUTURE_TARGET 0
+#define KVPOP_OP_DECODE 1
+
+int kvpop_abi_version(void);
+const char* kvpop_status_string(kvpop_status s);
+
+/*
+ * kvpop_fwd_lse -- main causal pass, log-normalizers only.
+ * App. D.1 (dense target identity) and D.4, first step: the main attention
+ * pass yields one log-normalizer per query.
+ *   LSE[b][g][d] = log sum_{t <= d} exp(scale * Q[b][g][d] . K[b][g/G][t])
+ * (the diagonal t = d is included, so no row is empty).  No S x S matrix is
+ * formed.  q, k: bf16 as laid out above; lse: fp32 [B][Hq][S], written in
+ * full.  Accumulation is fp32.
+ */
+kvpop_status kvpop_fwd_lse(const kvpop_dims* dims, const void* q, const void* k, float* lse,
+                           hipStream_t stream);
+
+/*
+ * kvpop_future_attn_target -- transposed future-attention pass.
+ * App. D.1-D.2 and D.4: keys take the role of queries; the original
+ * log-normalizer is subtracted and queries d < t + w are masked, so for key
+ * t and query head g
+ *   m_t^(g) = sum_{d = t+w}^{end_t} exp(scale * Q[g][d] . K[h][t] - LSE[g][d])
+ * with end_t = S-1 when lookahead < 0, else min(S-1, t+w+lookahead)
+ * (App. B.2 finite lookahead).  Keys t >= S - w receive 0.
+ * The group of G query heads of KV head h is aggregated (App. B.1) by `agg`;
+ * with count_normalize != 0 the result is divided by the number of
+ * contributing queries N_t = clip(S - t - w, 0, lookahead + 1) (App. B.2;
+ * N_t = 0 gives 0).
+ *   lse:            fp32 [B][Hq][S] from kvpop_fwd_lse (natural log).
+ *   mass:           fp32 [B][Hkv][S], written in full.
+ *   mass_per_qhead: nullable fp32 [B][Hq][S]: the per-query-head m_t^(g)
+ *                   (count-normalised when count_normalize != 0).
+ *   workspace:      at least kvpop_workspace_bytes(KVPOP_OP_FUTURE_TARGET,
+ *                   dims, window) bytes, 256-byte aligned; contents are
+ *                   scratch and need no initialisation.
+ * The result is deterministic (fixed-order reduction of partial sums).
+ */
+kvpop_status kvpop_future_attn_target(const kvpop_dims* dims, const void* q, const void* k,
+                                      const float* lse, int window, int lookahead, kvpop_agg agg,
+                                      int count_normalize, float* mass, float* mass_per_qhead,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * kvpop_evict_select -- fixed-budget retention and compaction.
+ * Sec. 3 (sinks + protected recent window + per-head top-k long-range
+ * tokens; attention over the retained set only), App. C.1 (budget
+ * B = s + w + k), App. F (ranking and selection in fp32).
+ * Per (b, h) row of S fp32 scores: eligible positions E = [s, S - w);
+ * keep the k = budget - s - w best of E, where a higher score ranks first,
+ * equal scores rank by lower position, NaN ranks below every number and
+ * -0.0 equals +0.0.  Scores at sink and window positions are ignored.
+ * Canonical slot layout of slot_pos [B][Hkv][budget] (int32, -1 = empty):
+ *   [0, s)        sink p at slot p
+ *   [s, s+k)      kept long-range positions, ascending, then -1 padding
+ *   [s+k, budget) window ring: position p in [max(S-w, s), S) at slot
+ *                 s + k + (p mod w)
+ *   slot_score: nullable fp32 [B][Hkv][budget]: scores[slot_pos], -inf when
+ *               empty.
+ *   k, v:       nullable together: bf16 [B][Hkv][S][head_dim].
+ *   k_cache, v_cache: nullable together (must be non-null when k, v are):
+ *               bf16 [B][Hkv][budget][head_dim]; row j is a bitwise copy
+ *               of row slot_pos[j], zero when empty.
+ * The output is bit-exact and deterministic.
+ */
+kvpop_status kvpop_evict_select(int batch, int n_kv_heads, int seq_len, int head_dim, int n_sink,
+                                int window, int budget, const float* scores, const void* k,
+                                const void* v, int32_t* slot_pos, float* slot_score, void* k_cache,
+                                void* v_cache, hipStream_t stream);
+
+/*
+ * kvpop_decode_attend -- one decoding query per head over the bounded cache.
+ * Sec. 3 and App. C.1: decoding attends only over the retained entries.
+ *   q:        bf16 [B][Hq][D]
+ *   k_cache, v_cache: bf16 [B][Hkv][n_slots][D], n_slots = dims->seq_len
+ *   slot_pos: int32 [B][Hkv][n_slots]; slots with slot_pos < 0 are skipped
+ *   o:        [B][Hq][D], fp32 or bf16 (round to nearest even) per o_dtype
+ *   lse:      nullable fp32 [B][Hq], natural log of the softmax denominator
+ *   workspace: kvpop_workspace_bytes(KVPOP_OP_DECODE, dims, 0) bytes.
+ * A head with no valid slot gets o = 0 and lse = -inf.
+ */
+kvpop_status kvpop_decode_attend(const kvpop_dims* dims, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* slot_pos, void* o,
+                                 kvpop_out_dtype o_dtype, float* lse, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * kvpop_score_mlp -- stateless headwise MLP scorer (App. E.2), on keys:
+ *   score = b2[h] + sum_j w2[h][j] * gelu(b1[h][j] + sum_c W1[h][j][c] k[c])
+ *   gelu(x) = 0.5 x (1 + erf(x / sqrt 2))
+ *   keys: bf16 [B][Hkv][n_tok][D]; w1 fp32 [Hkv][hidden][D]; b1, w2 fp32
+ *   [Hkv][hidden]; b2 fp32 [Hkv]; scores fp32 [B][Hkv][n_tok].
+ *   1 <= hidden <= 64.  Accumulation is fp32.
+ */
+kvpop_status kvpop_score_mlp(int batch, int n_kv_heads, int n_tok, int head_dim, int hidden,
+                             const void* keys, const float* w1, const float* b1, const float* w2,
+                             const float* b2, float* scores, hipStream_t stream);
+
+/*
+ * kvpop_cache_step -- one decoding step of the bounded per-head cache.
+ * Sec. 3 (a token is scored while in the protected window and judged when it
+ * leaves it), App. E.4 (at query q the newly eligible token is u = q - w),
+ * App. C.1 (B = s + w + k).  Slot layout as for kvpop_evict_select.
+ * For the new token at position pos_q, for every (b, h):
+ *  (a) exit: if u = pos_q - w >= s, token u leaves its ring slot.  It takes
+ *      the lowest empty long-range slot if there is one; otherwise it
+ *      replaces the worst kept token v (lowest score; among equal scores the
+ *      highest position; NaN lowest) when it ranks strictly before v, else
+ *      it is dropped.
+ *  (b) append: pos_q is written to sink slot pos_q when pos_q < s, else to
+ *      ring slot s + k + (pos_q mod w), its score set to quiet NaN.
+ *  (c) delayed scoring: token r = pos_q - delay (when r >= s) receives its
+ *      score in its ring slot: the MLP of kvpop_score_mlp on its cached key
+ *      when w1 != NULL, else scores_r[b][h].
+ *   k_new, v_new: bf16 [B][Hkv][D]; the cache state (k_cache, v_cache bf16
+ *   [B][Hkv][budget][D], slot_pos int32 and slot_score fp32
+ *   [B][Hkv][budget]) is updated in place.  Requires w >= 1,
+ *   0 <= delay < w, and exactly one of {w1 (with b1, w2, b2, hidden)} and
+ *   scores_r.
+ * Bit-exact and deterministic given the same scores.
+ */
+kvpop_status kvpop_cache_step(int batch, int n_kv_heads, int head_dim, int n_sink, int window,
+                              int budget, int delay, int pos_q, const void* k_new,
+                              const void* v_new, const float* w1, const float* b1,
+                              const float* w2, const float* b2, int hidden,
+                              const float* scores_r, void* k_cache, void* v_cache,
+                              int32_t* slot_pos, float* slot_score, hipStream_t stream);
+
+/* Bytes of workspace needed by `op` for these dims (0 if none). */
+size_t kvpop_workspace_bytes(int op, const kvpop_dims* dims, int window);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVPOP_H */

@@ -1,0 +1,130 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function
+include/kvpop.h declares, and rejects invalid arguments on the host before
+any launch (no GPU is touched: every call below fails validation).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import future_attention_scoring_kvpop_amd as kv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvpop.h")
+P = ctypes.c_void_p
+GOOD = P(0x10000)  # aligned, never dereferenced: validation fails first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kv.LIB_PATH):
+        from future_attention_scoring_kvpop_amd import build
+        build.build()
+    return kv.lib()
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b(kvpop_[a-z_]+)\s*\(", text))
+
+
+def test_exports_match_header(lib):
+    names = declared()
+    assert names == set(kv.EXPORTS), names ^ set(kv.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.kvpop_abi_version() == 1
+    for s in range(5):
+        assert lib.kvpop_status_string(s)
+
+
+def test_dims_validation(lib):
+    def fwd(d):
+        return lib.kvpop_fwd_lse(ctypes.byref(d), GOOD, GOOD, GOOD, None)
+
+    assert lib.kvpop_fwd_lse(None, GOOD, GOOD, GOOD, None) == 1
+    assert fwd(kv.dims(0, 32, 8, 4096, 128)) == 1
+    assert fwd(kv.dims(1, 32, 8, 0, 128)) == 1
+    assert fwd(kv.dims(1, 30, 8, 4096, 128)) == 1   # Hq % Hkv
+    assert fwd(kv.dims(1, 24, 8, 4096, 128)) == 2   # group of 3
+    assert fwd(kv.dims(1, 32, 8, 4096, 96)) == 2    # head dim
+    assert fwd(kv.dims(1, 32, 8, 4096, 128, float("nan"))) == 1
+    d = kv.dims(1, 32, 8, 4096, 128)
+    assert lib.kvpop_fwd_lse(ctypes.byref(d), None, GOOD, GOOD, None) == 1
+    assert lib.kvpop_fwd_lse(ctypes.byref(d), P(0x10008), GOOD, GOOD, None) == 1  # misaligned
+
+
+def test_target_validation(lib):
+    d = kv.dims(1, 32, 8, 4096, 128)
+    need = kv.workspace_bytes(kv.OP_FUTURE_TARGET, d, 128)
+    assert need > 0
+
+    def call(window=128, agg=0, ws=GOOD, nbytes=need, mass=GOOD):
+        return lib.kvpop_future_attn_target(ctypes.byref(d), GOOD, GOOD, GOOD, window, -1, agg, 0,
+                                            mass, None, ws, nbytes, None)
+
+    assert call(window=-1) == 1
+    assert call(agg=3) == 1
+    assert call(mass=None) == 1
+    assert call(ws=None) == 1
+    assert call(ws=P(0x10010)) == 1           # workspace must be 256-byte aligned
+    assert call(nbytes=need - 4) == 3
+
+
+def test_select_validation(lib):
+    def call(B=1, H=8, S=4096, D=128, s=4, w=128, budget=1024, scores=GOOD, k=None, v=None,
+             kc=None, vc=None, pos=GOOD):
+        return lib.kvpop_evict_select(B, H, S, D, s, w, budget, scores, k, v, pos, None, kc, vc, None)
+
+    assert call(budget=100) == 1              # budget < s + w
+    assert call(s=-1) == 1
+    assert call(w=-1) == 1
+    assert call(scores=None) == 1
+    assert call(pos=None) == 1
+    assert call(k=GOOD) == 1                  # k without v
+    assert call(k=GOOD, v=GOOD) == 1          # no cache outputs
+    assert call(kc=GOOD, vc=GOOD) == 1        # cache outputs without inputs
+    assert call(k=GOOD, v=GOOD, kc=GOOD, vc=GOOD, D=96) == 2
+
+
+def test_decode_validation(lib):
+    d = kv.dims(64, 32, 8, 4096, 128)
+    need = kv.workspace_bytes(kv.OP_DECODE, d)
+    assert need > 0
+
+    def call(o_dtype=0, ws=GOOD, nbytes=need, sp=GOOD):
+        return lib.kvpop_decode_attend(ctypes.byref(d), GOOD, GOOD, GOOD, sp, GOOD, o_dtype, None,
+                                       ws, nbytes, None)
+
+    assert call(o_dtype=2) == 1
+    assert call(sp=None) == 1
+    assert call(ws=None) == 1
+    assert call(nbytes=need - 1) == 3
+
+
+def test_mlp_and_cache_step_validation(lib):
+    assert lib.kvpop_score_mlp(1, 8, 10, 128, 65, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, None) == 2
+    assert lib.kvpop_score_mlp(1, 8, 10, 96, 64, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, None) == 2
+    assert lib.kvpop_score_mlp(1, 8, 10, 128, 64, None, GOOD, GOOD, GOOD, GOOD, GOOD, None) == 1
+
+    def step(window=256, delay=16, budget=4096, w1=None, sr=GOOD, hidden=64, pos=40000):
+        return lib.kvpop_cache_step(64, 8, 128, 4, window, budget, delay, pos, GOOD, GOOD, w1, GOOD,
+                                    GOOD, GOOD, hidden, sr, GOOD, GOOD, GOOD, GOOD, None)
+
+    assert step(window=0) == 1
+    assert step(delay=256) == 1               # delay must stay inside the window
+    assert step(delay=-1) == 1
+    assert step(budget=200) == 1
+    assert step(pos=-1) == 1
+    assert step(w1=GOOD) == 1                 # both an MLP and given scores
+    assert step(w1=None, sr=None) == 1        # neither
+    assert step(w1=GOOD, sr=None, hidden=65) == 2
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        kv.fwd_lse(torch.zeros(1, 2, 4, 64, dtype=torch.bfloat16),
+                   torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16))
