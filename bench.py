@@ -1,0 +1,299 @@
+"""Benchmark of the KVpop hot path on one MI355X.
+
+Timed step (the metric's first half): one pass of the whole hot path over the
+Qwen3-4B-shaped layer (B=1, 32 query / 8 KV heads, D=128, S=4096, RoPE,
+w=128, s=4, budget 1024): causal LSE pass -> transposed future-attention
+target (SUM over the group) -> retention + compaction of K/V -> one
+bounded-cache decode step (delayed MLP scoring) -> decode attention.
+value = KV-head keys scored per second = B*Hkv*S / step time.
+
+Also reported: the bounded-cache decode workload (64 sequences, 36 layers,
+budget 4096 per KV head, 512 steps: per layer and step one cache step with
+the delayed MLP scorer and one GQA decode attention) in steps/s with its
+HBM roofline, the roofline of the dominant kernel, and the CPU oracle timed
+on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import torch  # noqa: E402
+
+import synth  # noqa: E402
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+METRIC = "future-attn target keys/s + MFMA util; bounded-cache decode steps/s + HBM util"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def target_flops(w):
+    """Algorithmic flops of the two attention passes (QK^T only, masked pairs
+    excluded): causal pass 2*D*S(S+1)/2*Hq*B; transposed pass
+    2*D*(S-w)(S-w+1)/2*Hq*B."""
+    f_fwd = 2.0 * w.D * w.S * (w.S + 1) / 2 * w.Hq * w.B
+    n = max(w.S - w.window, 0)
+    f_tr = 2.0 * w.D * n * (n + 1) / 2 * w.Hq * w.B
+    return f_fwd, f_tr
+
+
+class TargetStep:
+    """Buffers and one step of the hot path on the layer workload."""
+
+    def __init__(self, kv, w, seed=7, hidden=64, delay=16):
+        dev = torch.device("cuda")
+        self.kv, self.w, self.delay = kv, w, delay
+        self.q, self.k, self.v = synth.attention_inputs(w, seed=seed, device=dev)
+        self.lse = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device=dev)
+        self.mass = torch.empty((w.B, w.Hkv, w.S), dtype=torch.float32, device=dev)
+        d = kv.dims(w.B, w.Hq, w.Hkv, w.S, w.D)
+        self.ws = torch.empty(kv.workspace_bytes(kv.OP_FUTURE_TARGET, d, w.window), dtype=torch.uint8,
+                              device=dev)
+        self.sp = torch.empty((w.B, w.Hkv, w.budget), dtype=torch.int32, device=dev)
+        self.ss = torch.empty((w.B, w.Hkv, w.budget), dtype=torch.float32, device=dev)
+        self.kc = torch.empty((w.B, w.Hkv, w.budget, w.D), dtype=torch.bfloat16, device=dev)
+        self.vc = torch.empty_like(self.kc)
+        self.mlp = [t.to(dev) for t in synth.mlp_weights(w.Hkv, w.D, hidden, seed=seed)]
+        self.k_new = synth.bf16(synth.normal((w.B, w.Hkv, w.D), seed + 11, dev, w.std))
+        self.v_new = synth.bf16(synth.normal((w.B, w.Hkv, w.D), seed + 12, dev, w.std))
+        self.q_new = synth.bf16(synth.normal((w.B, w.Hq, w.D), seed + 13, dev, w.std))
+        self.o = torch.empty((w.B, w.Hq, w.D), dtype=torch.bfloat16, device=dev)
+        dd = kv.dims(w.B, w.Hq, w.Hkv, w.budget, w.D)
+        nb = kv.workspace_bytes(kv.OP_DECODE, dd)
+        self.dws = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+
+    def run(self, ev=None):
+        kv, w = self.kv, self.w
+        if ev:
+            ev[0].record()
+        kv.fwd_lse(self.q, self.k, out=self.lse)
+        if ev:
+            ev[1].record()
+        kv.future_attn_target(self.q, self.k, self.lse, w.window, agg="sum", out=self.mass,
+                              workspace=self.ws)
+        if ev:
+            ev[2].record()
+        kv.evict_select(self.mass, w.n_sink, w.window, w.budget, self.k, self.v, out_pos=self.sp,
+                        out_score=self.ss, out_k=self.kc, out_v=self.vc)
+        kv.cache_step(self.kc, self.vc, self.sp, self.ss, self.k_new, self.v_new, w.S, w.n_sink,
+                      w.window, self.delay, mlp=self.mlp)
+        kv.decode_attend(self.q_new, self.kc, self.vc, self.sp, out_dtype=torch.bfloat16,
+                         want_lse=False, out=self.o, workspace=self.dws)
+        if ev:
+            ev[3].record()
+
+
+def bench_target(kv, steps, warmup):
+    w = synth.QWEN4B
+    st = TargetStep(kv, w)
+    for _ in range(warmup):
+        st.run()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(steps):
+        st.run(evs[i])
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    t_fwd = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    t_tr = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    t_rest = sum(e[2].elapsed_time(e[3]) for e in evs) / steps
+    f_fwd, f_tr = target_flops(w)
+    return w, ms, t_fwd, t_tr, t_rest, f_fwd, f_tr
+
+
+def decode_bytes_per_step(w, layers):
+    """Algorithmic HBM bytes of one decode step over all layers: the whole
+    bounded K/V cache read once, the appended K/V rows written, the exiting
+    row copied (read + write, upper bound), q read and o written (bf16)."""
+    units = w.B * w.Hkv * layers
+    cache = units * 2 * w.budget * w.D * 2
+    append = units * 2 * w.D * 2
+    exit_copy = units * 2 * 2 * w.D * 2
+    qo = w.B * layers * w.Hq * w.D * 2 * 2
+    return cache + append + exit_copy + qo
+
+
+def bench_decode(kv, steps, layers, seed=5):
+    w = synth.DECODE
+    dev = torch.device("cuda")
+    hidden, delay = w.extra["hidden"], w.extra["delay"]
+    B, Hq, Hkv, D, S, bud = w.B, w.Hq, w.Hkv, w.D, w.S, w.budget
+    log(f"decode setup: {layers} layers, prefix {S} -> budget {bud}")
+    caches = []
+    mlps = []
+    for layer in range(layers):
+        ls = 1000 * 5 + layer
+        kp = synth.bf16(synth.normal((B, Hkv, S, D), ls * 3 + 1, dev, w.std))
+        vp = synth.bf16(synth.normal((B, Hkv, S, D), ls * 3 + 2, dev, w.std))
+        mlp = [t.to(dev) for t in synth.mlp_weights(Hkv, D, hidden, seed=ls)]
+        sc = kv.score_mlp(kp, *mlp)
+        sp, ss, kc, vc = kv.evict_select(sc, w.n_sink, w.window, bud, kp, vp)
+        del kp, vp, sc
+        caches.append([kc, vc, sp, ss])
+        mlps.append(mlp)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    qs = torch.randn((steps, layers, B, Hq, D), generator=g, device=dev).mul_(w.std).to(torch.bfloat16)
+    ks = torch.randn((steps, layers, B, Hkv, D), generator=g, device=dev).mul_(w.std).to(torch.bfloat16)
+    vs = torch.randn((steps, layers, B, Hkv, D), generator=g, device=dev).mul_(w.std).to(torch.bfloat16)
+    o = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+    dd = kv.dims(B, Hq, Hkv, bud, D)
+    dws = torch.empty(kv.workspace_bytes(kv.OP_DECODE, dd), dtype=torch.uint8, device=dev)
+
+    def one_step(i):
+        pos = S + i
+        for layer in range(layers):
+            kc, vc, sp, ss = caches[layer]
+            kv.cache_step(kc, vc, sp, ss, ks[i, layer], vs[i, layer], pos, w.n_sink, w.window, delay,
+                          mlp=mlps[layer])
+            kv.decode_attend(qs[i, layer], kc, vc, sp, out_dtype=torch.bfloat16, want_lse=False,
+                             out=o, workspace=dws)
+
+    # attention-only timing of one layer (events on the launch stream)
+    ea = torch.cuda.Event(enable_timing=True)
+    eb = torch.cuda.Event(enable_timing=True)
+    kc, vc, sp, ss = caches[0]
+    for _ in range(3):
+        kv.decode_attend(qs[0, 0], kc, vc, sp, out_dtype=torch.bfloat16, want_lse=False, out=o,
+                         workspace=dws)
+    n_att = 50
+    ea.record()
+    for _ in range(n_att):
+        kv.decode_attend(qs[0, 0], kc, vc, sp, out_dtype=torch.bfloat16, want_lse=False, out=o,
+                         workspace=dws)
+    eb.record()
+    torch.cuda.synchronize()
+    t_att_ms = ea.elapsed_time(eb) / n_att
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        one_step(i)
+        if (i + 1) % 128 == 0:
+            log(f"decode: {i + 1}/{steps} steps issued")
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1)
+    sps = steps / (ms / 1e3)
+    by = decode_bytes_per_step(w, layers)
+    att_bytes = B * Hkv * 2 * bud * D * 2 + B * Hq * D * 2 * 2
+    return {
+        "workload": w.name, "sequences": B, "layers": layers, "steps": steps, "budget": bud,
+        "prefix": S, "delay": delay, "value": sps, "unit": "steps/s", "ms_per_step": ms / steps,
+        "wall_s": wall, "bytes_per_step": by,
+        "hbm": {"achieved": by * sps / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": by * sps / 1e9 / HBM_PEAK_GBS},
+        "attend_kernel": {"ms": t_att_ms, "bytes": att_bytes,
+                          "achieved": att_bytes / (t_att_ms / 1e3) / 1e9, "unit": "GB/s",
+                          "frac": att_bytes / (t_att_ms / 1e3) / 1e9 / HBM_PEAK_GBS},
+    }
+
+
+def cpu_baseline():
+    """The oracle (plain C, double, all host threads) on the target work of
+    the layer workload: LSE of all 32 query heads and the future mass of all
+    8 x 4096 keys, then the oracle's selection."""
+    import numpy as np
+
+    import oracle
+
+    w = synth.QWEN4B
+    q, k, _ = synth.attention_inputs(w, seed=7)
+    qf = np.ascontiguousarray(q.float().numpy())
+    kf = np.ascontiguousarray(k.float().numpy())
+    threads = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    lse = oracle.lse(qf, kf, nthreads=threads)
+    m = oracle.future_mass(qf, kf, lse, w.window, nthreads=threads)
+    oracle.select(m.astype(np.float32), w.n_sink, w.window, w.budget)
+    dt = time.perf_counter() - t0
+    keys = w.B * w.Hkv * w.S
+    return {"value": keys / dt, "unit": "keys/s", "cores": threads, "kind": "oracle",
+            "sample": f"one full {w.name} step's target work (LSE of {w.Hq} query heads, future "
+                      f"mass of {keys} keys, selection), no decode step; {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=512)
+    ap.add_argument("--decode-layers", type=int, default=36)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the KVpop hot path is sharded by (batch, KV head) with no "
+              "communication, and this build runs on a single MI355X; use --gpus 1.", flush=True)
+        sys.exit(2)
+
+    import future_attention_scoring_kvpop_amd as kv
+
+    if not os.path.exists(kv.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    torch.cuda.set_device(0)
+
+    log(f"target step: {a.warmup} warmup + {a.steps} timed")
+    w, ms, t_fwd, t_tr, t_rest, f_fwd, f_tr = bench_target(kv, a.steps, a.warmup)
+    keys = w.B * w.Hkv * w.S
+    value = keys / (ms / 1e3)
+    log(f"target step {ms:.4f} ms (fwd_lse {t_fwd:.4f}, future target {t_tr:.4f}, "
+        f"select+gather+decode {t_rest:.4f})")
+    achieved_tr = f_tr / (t_tr / 1e3) / 1e12
+    achieved_fwd = f_fwd / (t_fwd / 1e3) / 1e12
+    out = {
+        "metric": METRIC, "value": value, "unit": "keys/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
+                   "head_dim": w.D, "seq_len": w.S, "window": w.window, "sinks": w.n_sink,
+                   "budget": w.budget, "aggregation": "sum", "rope_theta": synth.ROPE_THETA,
+                   "step": "fwd_lse + future_attn_target + evict_select(+gather) + cache_step + "
+                           "decode_attend"},
+        "roofline": {"bound": "mfma", "kernel": "kvpop_future_attn_target (transposed pass + merge)",
+                     "achieved": achieved_tr, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved_tr / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                     "flops_per_launch": f_tr, "ms_per_launch": t_tr},
+        "kernels": {"fwd_lse": {"ms": t_fwd, "tflops": achieved_fwd,
+                                "frac": achieved_fwd / MFMA_BF16_PEAK_TFLOPS},
+                    "future_attn_target": {"ms": t_tr, "tflops": achieved_tr,
+                                           "frac": achieved_tr / MFMA_BF16_PEAK_TFLOPS},
+                    "select_gather_decode": {"ms": t_rest}},
+    }
+    if not a.no_decode:
+        log(f"decode: {a.decode_steps} steps x {a.decode_layers} layers")
+        out["decode"] = bench_decode(kv, a.decode_steps, a.decode_layers)
+        if a.decode_layers != 36 or a.decode_steps != 512:
+            out["decode"]["reduced"] = True
+    if not a.no_cpu:
+        log("cpu baseline: oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

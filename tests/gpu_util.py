@@ -73,16 +73,17 @@ def group_problem(q, k, b, h):
 
 
 def oracle_group_target(q, k, b, h, window, t_lo, t_hi, lookahead=-1, agg="sum",
-                        count_normalize=False, scale=None):
+                        count_normalize=False, scale=None, all_rows=False):
     """Oracle LSE rows and per-key mass for keys [t_lo, t_hi) of one group.
 
-    Only the normalizer rows those keys need (d >= t_lo + w) are computed;
-    every other row is left NaN so an accidental read would show.
+    Only the normalizer rows those keys need (d >= t_lo + w) are computed
+    unless all_rows; every other row is left NaN so an accidental read would
+    show.
     Returns (lse_sub [G,S] with NaN gaps, mass [t_hi-t_lo], per_head [n,G]).
     """
     qs, ks = group_problem(q, k, b, h)
     G, S = qs.shape[1], qs.shape[2]
-    d_lo = min(S, t_lo + window)
+    d_lo = 0 if all_rows else min(S, t_lo + window)
     rows = np.array([g * S + d for g in range(G) for d in range(d_lo, S)], np.int64)
     lse_sub = np.full((1, G, S), np.nan)
     if rows.size:
