@@ -48,6 +48,42 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// Direct global -> LDS loads (no staging registers).  Lane i of the wave
+// writes its bytes at lds_base + size * i; lds_base must be wave-uniform.
+// Completion is tracked by the wave's vmcnt like any vector memory load.
+__device__ __forceinline__ void dma16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
+}
+
+// Wait until at most N vector memory operations of this wave are in flight
+// (gfx9 s_waitcnt encoding: vmcnt bits [3:0] and [15:14]; expcnt and
+// lgkmcnt left at their "no wait" maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Wait until this wave's LDS (and scalar memory) operations have completed.
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// also drain the wave's in-flight prefetches); callers order LDS traffic
+// with explicit waits.  The empty asm statements keep the compiler from
+// moving memory accesses across the barrier.
+__device__ __forceinline__ void bare_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Blocks are dispatched round-robin over the 8 XCDs (block i runs on XCD
 // i % 8).  Renumber so that each XCD receives one contiguous range of
 // logical work items: neighbouring items then share that XCD's L2.

@@ -10,43 +10,116 @@
 //   m_t^(g) = sum_{d=t+w}^{end_t} exp2(s_dt * scale*log2e - LSE_d * log2e)
 //
 // gfx950 mapping
-//   * A work item is (b, KV head h, 256-key block, query chunk).  Its four
-//     waves each keep 64 keys resident as MFMA A fragments (two interleaved
-//     32-key sub-tiles: keys t0+32w.. and t0+128+32w.., so every wave meets
-//     the window diagonal at about the same query) and stream the chunk's
-//     queries of all G heads of the group through double-buffered LDS as B
-//     fragments: v_mfma_f32_32x32x16_bf16 yields S^T[key][query].
-//   * Each lane owns one query column and 16 key rows per sub-tile, so the
-//     per-key sums accumulate in registers across every query tile and head
-//     and are reduced across lanes once per item (through padded LDS).
+//   * A work item is (b, KV head h, 128-key block, query chunk).  Each of its
+//     four waves keeps 32 keys resident as MFMA A fragments and streams the
+//     chunk's queries of all G heads of the group as B fragments:
+//     v_mfma_f32_32x32x16_bf16 yields S^T[key][query].  Few registers per
+//     wave (about 90) keep five waves per SIMD resident, so the MFMA phase
+//     of one wave overlaps the exp2/accumulate phase of the others.
+//   * Query tiles (32 queries) reach LDS by direct global->LDS DMA into a
+//     ring of stages, requested two tiles ahead; rows are stored unpadded
+//     with their 16-byte chunks XOR-swizzled by row so the fragment reads
+//     are bank-conflict free.  A bare s_barrier plus explicit vmcnt/lgkmcnt
+//     waits orders the ring without draining the prefetches.
+//   * Each lane owns one query column and 16 key rows, so per-key sums stay
+//     in registers across every query tile and head; they are reduced
+//     across lanes once per item by a register transpose-reduce.
 //   * Tiles whose 32x32 (key, query) square lies fully inside the allowed
 //     region take a mask-free path (one FMA, one exp2, one add per pair);
 //     fully masked squares are skipped; only the diagonal squares mask.
 //   * Items write partial sums per (chunk, key); a second kernel sums the
 //     chunks of each key in a fixed order (deterministic), aggregates the
 //     group and applies count normalisation.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
 namespace kvpop {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kQT = 32;        // queries per LDS tile
-constexpr int kRedStride = 65; // padded LDS row for the final lane reduction
+// Work split: query chunks shrink from the maximum (powers of two) until the
+// launch holds enough items to fill the chip, but not below the minimum.
+#ifndef KVPOP_TGT_MAX_CHUNK
+#define KVPOP_TGT_MAX_CHUNK 2048
+#endif
+#ifndef KVPOP_TGT_MIN_CHUNK
+#define KVPOP_TGT_MIN_CHUNK 128
+#endif
+#ifndef KVPOP_TGT_MIN_ITEMS
+#define KVPOP_TGT_MIN_ITEMS 8192
+#endif
+#ifndef KVPOP_TGT_STAGES
+#define KVPOP_TGT_STAGES 3
+#endif
+#ifndef KVPOP_TGT_MIN_BLOCKS
+#define KVPOP_TGT_MIN_BLOCKS 2  // workgroups per CU the register budget must allow
+#endif
+
+#ifndef KVPOP_TGT_WAVES
+#define KVPOP_TGT_WAVES 8
+#endif
+constexpr int kWaves = KVPOP_TGT_WAVES;  // waves per workgroup (all share each query tile)
+constexpr int kThreads = 64 * kWaves;
+constexpr int kQT = 32;                    // queries per LDS tile
+constexpr int kStages = KVPOP_TGT_STAGES;  // query tiles in the LDS ring
+static_assert(kStages >= 2 && kStages <= 4, "stage count");
+constexpr int kSub = kKeyBlock / (32 * kWaves);  // 32-key sub-tiles per wave
+static_assert(kSub == 1 || kSub == 2, "a wave holds one or two 32-key sub-tiles");
+
+// One step of the register transpose-reduce: every lane holds 2M values;
+// lanes with bit M set keep the upper half, the others the lower half, each
+// adding its partner's copy of the half it keeps.
+template <int M>
+__device__ __forceinline__ void xreduce_step(float* v, int lane) {
+  const bool up = (lane & M) != 0;
+#pragma unroll
+  for (int j = 0; j < M; ++j) {
+    const float a = v[j], b = v[j + M];
+    v[j] = (up ? b : a) + __shfl_xor(up ? a : b, M);
+  }
+}
+
+// Wait until at most n of this wave's DMA instructions are in flight
+// (n is wave-uniform: later tiles x this wave's instructions per tile).
+__device__ __forceinline__ void wait_inflight(int n) {
+  if (n <= 0) wait_vmcnt<0>();
+  else if (n == 1) wait_vmcnt<1>();
+  else if (n == 2) wait_vmcnt<2>();
+  else if (n == 3) wait_vmcnt<3>();
+  else if (n == 4) wait_vmcnt<4>();
+  else if (n == 5) wait_vmcnt<5>();
+  else wait_vmcnt<6>();
+}
 
 template <int D, bool PER_HEAD>
-__global__ __launch_bounds__(kThreads, 2) void future_target_kernel(
+__global__ __launch_bounds__(kThreads, KVPOP_TGT_MIN_BLOCKS) void future_target_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const float* __restrict__ lse,
     float* __restrict__ partial, int Hq, int Hkv, int S, int window, int lookahead, float c,
     int chunk, int n_chunks, int n_kb, int n_items) {
-  constexpr int NS = D / 16;
-  constexpr int STRIDE = D + 8;
-  constexpr int CPR = D / 8;
-  constexpr int PER_T = kQT * CPR / kThreads;  // 2 (D=128) or 1 (D=64)
-  __shared__ __attribute__((aligned(16))) bf16_t qs[2][kQT * STRIDE];
-  __shared__ float ls[2][kQT];
-  __shared__ float red[4][32 * kRedStride];
+  constexpr int NS = D / 16;                // MFMA k-slices
+  constexpr int CPR = D / 8;                // 16-byte chunks per row
+  constexpr int ROWB = D * 2;               // bytes per query row
+  constexpr int TILE = kQT * ROWB;          // bytes per query tile
+  constexpr int NQI = TILE / 1024;          // 1 KB DMA instructions per query tile
+  constexpr int QPW = NQI >= kWaves ? NQI / kWaves : 1;  // per loading wave
+  constexpr int Q_WAVES = NQI >= kWaves ? kWaves : NQI;  // waves that load query rows
+  constexpr int ROWS_PER_LOAD = 1024 / ROWB;
+  static_assert(NQI % Q_WAVES == 0, "tile split over waves");
+  // One LDS object per ring stage: every access below names its stage at
+  // compile time, so the compiler can tell a DMA into one stage from reads of
+  // another and does not drain the in-flight prefetches before each read.
+  __shared__ __attribute__((aligned(1024))) uint8_t qs0[TILE], qs1[TILE], qs2[kStages > 2 ? TILE : 16],
+      qs3[kStages > 3 ? TILE : 16];
+  __shared__ __attribute__((aligned(256))) float ls0[64], ls1[64], ls2[64], ls3[64];
+  auto qst = [&](auto J) -> uint8_t* {
+    constexpr int j = decltype(J)::value;
+    return j == 0 ? qs0 : j == 1 ? qs1 : j == 2 ? qs2 : qs3;
+  };
+  auto lst = [&](auto J) -> float* {
+    constexpr int j = decltype(J)::value;
+    return j == 0 ? ls0 : j == 1 ? ls1 : j == 2 ? ls2 : ls3;
+  };
 
   const int G = Hq / Hkv;
   const int item = xcd_remap(blockIdx.x, n_items);
@@ -68,127 +141,165 @@ __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(
   const int n_qt = (d_hi - dt0 + kQT - 1) / kQT;
   const int n_iter = G * n_qt;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int col = lane & 31, half = lane >> 5;
-  int ts[2];
-  ts[0] = t0 + 32 * wave;
-  ts[1] = t0 + 128 + 32 * wave;
+  // this wave's keys: sub-tile u covers ts[u] .. ts[u]+31 (interleaved so all
+  // waves meet the window diagonal at about the same query)
+  int ts[kSub];
+#pragma unroll
+  for (int u = 0; u < kSub; ++u) ts[u] = t0 + 32 * kWaves * u + 32 * wave;
+  // this wave's share of each tile's DMA: query rows and/or the normalizers
+  const bool loads_q = wave < Q_WAVES;
+  const bool loads_l = wave == kWaves - 1;
+  const int per_tile = (loads_q ? QPW : 0) + (loads_l ? 1 : 0);
 
-  bf16x8 ka[2][NS];
-#pragma unroll
-  for (int sub = 0; sub < 2; ++sub) {
-    const int t = ts[sub] + col;
-    const bf16_t* krow = k + (((size_t)b * Hkv + h) * S + (t < S ? t : 0)) * D + 8 * half;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) ka[sub][s] = as_bf16x8(t < S ? ldg16(krow + 16 * s) : make_uint4(0, 0, 0, 0));
-  }
-
-  float macc[2][16];
-#pragma unroll
-  for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) macc[sub][r] = 0.f;
-
-  uint4 pre[PER_T];
-  float pre_l = 0.f;
-  auto load_tile = [&](int it) {
+  // DMA of query tile `it` (head-major, then position) into stage J.
+  auto issue = [&](auto J, int it) {
+    uint8_t* qd = qst(J);
+    float* ld = lst(J);
     const int gl = it / n_qt;
-    const int d0 = dt0 + (it % n_qt) * kQT;
+    const int d0 = dt0 + (it - gl * n_qt) * kQT;
     const size_t head = (size_t)b * Hq + h * G + gl;
     const bf16_t* qb = q + head * S * D;
+    if (loads_q) {
 #pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int ch = tid + i * kThreads;
-      const int row = ch / CPR, cc = ch % CPR;
-      const int d = d0 + row;
-      pre[i] = d < S ? ldg16(qb + (size_t)d * D + cc * 8) : make_uint4(0, 0, 0, 0);
+      for (int j = 0; j < QPW; ++j) {
+        const int I = wave * QPW + j;
+        const int row = I * ROWS_PER_LOAD + lane / CPR;
+        const int pc = lane % CPR;              // physical chunk written by this lane
+        const int lc = pc ^ (row & (CPR - 1));  // logical chunk it holds
+        const int d = min(d0 + row, S - 1);
+        dma16(qb + (size_t)d * D + lc * 8, qd + I * 1024);
+      }
     }
-    if (tid < kQT) {
-      const int d = d0 + tid;
-      pre_l = d < S ? lse[head * S + d] * kLog2e : 0.f;
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int ch = tid + i * kThreads;
-      const int row = ch / CPR, cc = ch % CPR;
-      *reinterpret_cast<uint4*>(&qs[buf][row * STRIDE + cc * 8]) = pre[i];
-    }
-    if (tid < kQT) ls[buf][tid] = pre_l;
+    if (loads_l && lane < kQT) dma4(lse + head * S + min(d0 + lane, S - 1), ld);
   };
 
-  // Reduce each key's per-lane partial sums across the 32 lanes that share
-  // its rows and write one float per key of the block.
+  bf16x8 ka[kSub][NS];
+#pragma unroll
+  for (int u = 0; u < kSub; ++u) {
+    const int t = ts[u] + col;
+    const bf16_t* krow = k + (((size_t)b * Hkv + h) * S + (t < S ? t : 0)) * D + 8 * half;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) ka[u][s] = as_bf16x8(t < S ? ldg16(krow + 16 * s) : make_uint4(0, 0, 0, 0));
+  }
+  float macc[kSub][16];
+#pragma unroll
+  for (int u = 0; u < kSub; ++u)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) macc[u][r] = 0.f;
+
+  // Sum each key's per-lane partials over the 32 lanes sharing its row and
+  // write one float per key of this wave's tile.
   auto flush = [&](int gout) {
-    float* rw = red[wave];
+    float v[16 * kSub];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
+    for (int u = 0; u < kSub; ++u)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) rw[(sub * 16 + r) * kRedStride + lane] = macc[sub][r];
-    __syncthreads();
-    const int sub = lane >> 5, row = lane & 31;
-    const int hf = (row >> 2) & 1, r = ((row >> 3) << 2) | (row & 3);
-    const float* src = rw + (sub * 16 + r) * kRedStride + hf * 32;
-    float sum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) sum += src[i];
-    const int t = ts[sub] + row;
-    if (t < S) {
+      for (int r = 0; r < 16; ++r) v[16 * u + r] = macc[u][r];
+    if (kSub == 2) xreduce_step<16>(v, lane);
+    xreduce_step<8>(v, lane);
+    xreduce_step<4>(v, lane);
+    xreduce_step<2>(v, lane);
+    xreduce_step<1>(v, lane);
+    // lane col now holds register col (two sub-tiles) or col & 15 (one)
+    if (kSub == 1) v[0] += __shfl_xor(v[0], 16);
+    const int u = kSub == 2 ? col >> 4 : 0;
+    const int r = col & 15;
+    const int t = ts[u] + 8 * (r >> 2) + 4 * half + (r & 3);
+    if ((kSub == 2 || col < 16) && t < S) {
       const size_t base = PER_HEAD ? ((size_t)bh * G + gout) : (size_t)bh;
-      partial[(base * n_chunks + cidx) * S + t] = sum;
+      partial[(base * n_chunks + cidx) * S + t] = v[0];
     }
-    __syncthreads();
   };
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int it = 0; it < n_iter; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < n_iter) load_tile(it + 1);
-    const int d0 = dt0 + (it % n_qt) * kQT;
-    const float L2 = ls[buf][col];
-    const bf16_t* brow = &qs[buf][col * STRIDE + 8 * half];
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  // prologue: tiles 0 .. kStages-2 into stages 0 .. kStages-2
+  if (0 < n_iter && kStages > 1) issue(I0{}, 0);
+  if (1 < n_iter && kStages > 2) issue(I1{}, 1);
+  if (2 < n_iter && kStages > 3) issue(I2{}, 2);
+
+  // One iteration on tile `it`, which lives in stage J; the stage of tile
+  // it-1 (J-1 mod kStages) is refilled with tile it+kStages-1.
+  auto step = [&](auto J, int it) {
+    constexpr int j = decltype(J)::value;
+    constexpr int jn = (j + kStages - 1) % kStages;
+    wait_inflight(per_tile * min(kStages - 2, n_iter - 1 - it));
+    wait_lgkmcnt0();  // this wave's reads of earlier stages have completed
+    bare_barrier();   // tile `it` is in LDS for every wave; tile it-1's stage is free
+    if (it + kStages - 1 < n_iter) issue(std::integral_constant<int, jn>{}, it + kStages - 1);
+    const int gl = it / n_qt;
+    const int d0 = dt0 + (it - gl * n_qt) * kQT;
+    bool skip[kSub], any = false;
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int tsub = ts[sub];
-      const bool skip = tsub >= S || d0 + kQT - 1 < tsub + window ||
-                        (lookahead >= 0 && d0 > tsub + 31 + window + lookahead);
-      if (skip) continue;
-      const bool full = d0 >= tsub + 31 + window && d0 + kQT - 1 < S &&
-                        (lookahead < 0 || d0 + kQT - 1 <= tsub + window + lookahead);
-      f32x16 acc;
+    for (int u = 0; u < kSub; ++u) {
+      skip[u] = ts[u] >= S || d0 + kQT - 1 < ts[u] + window ||
+                (lookahead >= 0 && d0 > ts[u] + 31 + window + lookahead);
+      any = any || !skip[u];
+    }
+    if (any) {
+      const float L2 = lst(J)[col] * kLog2e;
+      const uint8_t* tile = qst(J) + col * ROWB;
+      const int sw = col & (CPR - 1);
+      f32x16 acc[kSub];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+      for (int u = 0; u < kSub; ++u)
 #pragma unroll
-      for (int s = 0; s < NS; ++s)
-        acc = mfma32(ka[sub][s], as_bf16x8(*reinterpret_cast<const uint4*>(brow + 16 * s)), acc);
-      if (full) {
+        for (int r = 0; r < 16; ++r) acc[u][r] = 0.f;
+      if (kSub == 1 || (!skip[0] && !skip[1 % kSub])) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) macc[sub][r] += fast_exp2(fmaf(acc[r], c, -L2));
+        for (int s = 0; s < NS; ++s) {
+          const bf16x8 bv = as_bf16x8(*reinterpret_cast<const uint4*>(tile + (((2 * s + half) ^ sw) << 4)));
+#pragma unroll
+          for (int u = 0; u < kSub; ++u) acc[u] = mfma32(ka[u][s], bv, acc[u]);
+        }
       } else {
-        // d - t - w for r = 0; row r adds 8*(r/4) + r%4 to t
-        const int d = d0 + col;
-        const int base = d - tsub - 4 * half - window;
+        const int u = skip[0] ? 1 : 0;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int off = 8 * (r >> 2) + (r & 3);
-          const int diff = base - off;  // d - (t + w)
-          const bool ok = diff >= 0 && d < S && (lookahead < 0 || diff <= lookahead);
-          if (ok) macc[sub][r] += fast_exp2(fmaf(acc[r], c, -L2));
+        for (int s = 0; s < NS; ++s)
+          acc[u] = mfma32(ka[u][s], as_bf16x8(*reinterpret_cast<const uint4*>(tile + (((2 * s + half) ^ sw) << 4))), acc[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < kSub; ++u) {
+        if (skip[u]) continue;
+        const int tu = ts[u];
+        const bool full = d0 >= tu + 31 + window && d0 + kQT - 1 < S &&
+                          (lookahead < 0 || d0 + kQT - 1 <= tu + window + lookahead);
+        if (full) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) macc[u][r] += fast_exp2(fmaf(acc[u][r], c, -L2));
+        } else {
+          // d - t - w for row r = base - (8*(r/4) + r%4)
+          const int d = d0 + col;
+          const int base = d - tu - 4 * half - window;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int diff = base - (8 * (r >> 2) + (r & 3));
+            const bool ok = diff >= 0 && d < S && (lookahead < 0 || diff <= lookahead);
+            const float p = fast_exp2(fmaf(acc[u][r], c, -L2));
+            macc[u][r] += ok ? p : 0.f;
+          }
         }
       }
     }
-    if (it + 1 < n_iter) store_tile(buf ^ 1);
-    __syncthreads();
-    if (PER_HEAD && (it % n_qt) == n_qt - 1) {
-      flush(it / n_qt);
+    if (PER_HEAD && it - gl * n_qt == n_qt - 1) {
+      flush(gl);
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
+      for (int u = 0; u < kSub; ++u)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) macc[sub][r] = 0.f;
+        for (int r = 0; r < 16; ++r) macc[u][r] = 0.f;
     }
+  };
+
+  for (int it = 0; it < n_iter; it += kStages) {
+    step(I0{}, it);
+    if (it + 1 < n_iter) step(I1{}, it + 1);
+    if (kStages > 2 && it + 2 < n_iter) step(I2{}, it + 2);
+    if (kStages > 3 && it + 3 < n_iter) step(I3{}, it + 3);
   }
   if (!PER_HEAD) flush(0);
 }
@@ -251,8 +362,8 @@ TargetPlan plan_target(const AttnShape& s, int window) {
     }
     return items * s.B * s.Hkv;
   };
-  int C = 2048;
-  while (C > 256 && count_items(C) < 4096) C >>= 1;
+  int C = KVPOP_TGT_MAX_CHUNK;
+  while (C > KVPOP_TGT_MIN_CHUNK && count_items(C) < KVPOP_TGT_MIN_ITEMS) C >>= 1;
   p.chunk = C;
   p.n_chunks = (s.S + C - 1) / C;
   const int G = s.Hq / s.Hkv;

@@ -25,7 +25,10 @@ struct TargetPlan {
   int n_kb;       // key blocks of kKeyBlock keys
   size_t partial_floats;  // workspace floats (per-query-head partials)
 };
-constexpr int kKeyBlock = 256;
+#ifndef KVPOP_TGT_KEY_BLOCK
+#define KVPOP_TGT_KEY_BLOCK 256
+#endif
+constexpr int kKeyBlock = KVPOP_TGT_KEY_BLOCK;  // keys per work item (32 or 64 per wave)
 TargetPlan plan_target(const AttnShape& s, int window);
 hipError_t launch_future_target(const AttnShape& s, const void* q, const void* k,
                                 const float* lse, int window, int lookahead, int agg,
