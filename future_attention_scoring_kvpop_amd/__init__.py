@@ -24,6 +24,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
 AGG = {"sum": 0, "mean": 1, "max": 2}
 OP_FUTURE_TARGET = 0
 OP_DECODE = 1
+OP_FWD_LSE = 2
 
 EXPORTS = ("kvpop_abi_version", "kvpop_status_string", "kvpop_workspace_bytes", "kvpop_fwd_lse",
            "kvpop_future_attn_target", "kvpop_evict_select", "kvpop_decode_attend",
@@ -58,7 +59,7 @@ def lib():
             "kvpop_abi_version": (I, []),
             "kvpop_status_string": (ctypes.c_char_p, [I]),
             "kvpop_workspace_bytes": (Z, [I, DP, I]),
-            "kvpop_fwd_lse": (I, [DP, P, P, P, P]),
+            "kvpop_fwd_lse": (I, [DP, P, P, P, P, Z, P]),
             "kvpop_future_attn_target": (I, [DP, P, P, P, I, I, I, I, P, P, P, Z, P]),
             "kvpop_evict_select": (I, [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P]),
             "kvpop_decode_attend": (I, [DP, P, P, P, P, P, I, P, P, Z, P]),
@@ -105,7 +106,7 @@ def workspace_bytes(op, d, window=0):
     return int(lib().kvpop_workspace_bytes(op, ctypes.byref(d), int(window)))
 
 
-def fwd_lse(q, k, scale=0.0, out=None):
+def fwd_lse(q, k, scale=0.0, out=None, workspace=None):
     """Dense causal log-normalizers LSE [B,Hq,S] fp32 (App. D.1, D.4)."""
     _need(q, torch.bfloat16, "q", 4)
     _need(k, torch.bfloat16, "k", 4)
@@ -116,7 +117,12 @@ def fwd_lse(q, k, scale=0.0, out=None):
     lse = out if out is not None else torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
     _need(lse, torch.float32, "lse")
     d = dims(B, Hq, Hkv, S, D, scale)
-    _check("kvpop_fwd_lse", lib().kvpop_fwd_lse(ctypes.byref(d), _p(q), _p(k), _p(lse), _stream()))
+    nbytes = workspace_bytes(OP_FWD_LSE, d)
+    ws = workspace if workspace is not None else (
+        torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None)
+    st = lib().kvpop_fwd_lse(ctypes.byref(d), _p(q), _p(k), _p(lse), _p(ws),
+                             0 if ws is None else ws.numel() * ws.element_size(), _stream())
+    _check("kvpop_fwd_lse", st)
     return lse
 
 

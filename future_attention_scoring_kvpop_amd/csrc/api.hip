@@ -69,17 +69,23 @@ size_t kvpop_workspace_bytes(int op, const kvpop_dims* dims, int window) {
     return kvpop::plan_target(s, window).partial_floats * sizeof(float);
   }
   if (op == KVPOP_OP_DECODE) return kvpop::plan_decode(s).workspace_floats * sizeof(float);
+  if (op == KVPOP_OP_FWD_LSE) return kvpop::plan_fwd(s).partial_floats * sizeof(float);
   return 0;
 }
 
 kvpop_status kvpop_fwd_lse(const kvpop_dims* dims, const void* q, const void* k, float* lse,
-                           hipStream_t stream) {
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
   AttnShape s;
   kvpop_status st = check_dims(dims, &s);
   if (st != KVPOP_OK) return st;
   if (!q || !k || !lse) return KVPOP_ERR_INVALID_ARGUMENT;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(lse, 4)) return KVPOP_ERR_INVALID_ARGUMENT;
-  return from_hip(kvpop::launch_fwd_lse(s, q, k, lse, stream));
+  const kvpop::FwdPlan p = kvpop::plan_fwd(s);
+  if (p.partial_floats) {
+    if (!workspace || !aligned(workspace, 16)) return KVPOP_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < p.partial_floats * sizeof(float)) return KVPOP_ERR_WORKSPACE_TOO_SMALL;
+  }
+  return from_hip(kvpop::launch_fwd_lse(s, q, k, lse, (float*)workspace, stream));
 }
 
 kvpop_status kvpop_future_attn_target(const kvpop_dims* dims, const void* q, const void* k,

@@ -6,53 +6,114 @@
 //   LSE[b][g][d] = log sum_{t <= d} exp(scale * q_d . k_t)
 //
 // gfx950 mapping
-//   * One workgroup (4 waves) owns P = 128/G consecutive query positions of
+//   * A workgroup (4 waves) owns P = 128/G consecutive query positions of
 //     every query head of one KV-head group, so all 128 of its query rows
-//     share the same causal key range and every K tile is read once per
+//     share one causal key range and every K tile is read once per
 //     workgroup for the whole group.
-//   * Each wave keeps 32 query rows resident as MFMA B fragments (bf16) and
-//     streams 64-key tiles of K from LDS (double buffered, one barrier per
-//     tile) as A fragments: v_mfma_f32_32x32x16_bf16 gives S^T[key][query].
+//   * Each wave keeps 32 query rows resident as MFMA B fragments and streams
+//     64-key tiles of K as A fragments: v_mfma_f32_32x32x16_bf16 gives
+//     S^T[key][query].  K tiles reach LDS by direct global->LDS DMA into a
+//     ring of stages (one LDS object per stage, rows XOR-swizzled), requested
+//     one tile ahead; the register budget allows four workgroups per CU.
 //   * Softmax statistics are kept per lane (a lane owns one query column and
 //     16 key rows of each 32-key sub-tile), in base 2 with the scale folded
-//     into one FMA: p = exp2(s * scale*log2e - m * scale*log2e).  The two
-//     half-waves holding the same column merge once at the end.
-//   * Workgroups are issued longest-row first and renumbered so that each
-//     XCD works through whole KV heads (their K stays in that XCD's L2).
+//     into one FMA; the two half-waves of a column merge at the end.
+//   * Causal rows grow with position, so when the launch holds too few row
+//     blocks to occupy the chip the key range of long rows is split into
+//     pieces of at most kmax keys; each piece writes a partial (max, sum) and
+//     a small kernel merges them.
+//   * Work items are issued longest first and renumbered so that each XCD
+//     works through whole KV heads (their K stays in that XCD's L2).
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
 namespace kvpop {
 namespace {
 
+#ifndef KVPOP_FWD_STAGES
+#define KVPOP_FWD_STAGES 2
+#endif
+#ifndef KVPOP_FWD_MIN_BLOCKS
+#define KVPOP_FWD_MIN_BLOCKS 4
+#endif
+// Row blocks below which long causal rows are split into pieces (only
+// launches that cannot occupy the chip gain from the extra merge).
+#ifndef KVPOP_FWD_TARGET_ITEMS
+#define KVPOP_FWD_TARGET_ITEMS 256
+#endif
+
 constexpr int kKT = 64;        // keys per LDS tile
 constexpr int kThreads = 256;  // 4 waves
+constexpr int kStages = KVPOP_FWD_STAGES;
+static_assert(kStages >= 2 && kStages <= 4, "stage count");
+
+// Wait until at most n of this wave's DMA instructions are in flight.
+__device__ __forceinline__ void wait_inflight(int n) {
+  if (n <= 0) wait_vmcnt<0>();
+  else if (n <= 4) wait_vmcnt<4>();
+  else if (n <= 8) wait_vmcnt<8>();
+  else wait_vmcnt<12>();
+}
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void fwd_lse_kernel(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, float* __restrict__ lse, int Hq,
-    int Hkv, int S, float c, float scale, int n_pb, int n_items) {
-  constexpr int NS = D / 16;      // MFMA k-slices per 32x32 product
-  constexpr int STRIDE = D + 8;   // LDS row stride in bf16 (16-byte pad)
-  constexpr int CPR = D / 8;      // 16-byte chunks per K row
-  constexpr int PER_T = kKT * CPR / kThreads;
-  __shared__ __attribute__((aligned(16))) bf16_t ks[2][kKT * STRIDE];
+__global__ __launch_bounds__(kThreads, KVPOP_FWD_MIN_BLOCKS) void fwd_lse_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, float* __restrict__ lse,
+    float2* __restrict__ part, int B, int Hq, int Hkv, int S, float c, float scale, int n_pb,
+    int kmax, int n_pieces, int n_items) {
+  constexpr int NS = D / 16;           // MFMA k-slices
+  constexpr int CPR = D / 8;           // 16-byte chunks per row
+  constexpr int ROWB = D * 2;          // bytes per K row
+  constexpr int TILE = kKT * ROWB;     // bytes per K tile
+  constexpr int LPW = TILE / 1024 / (kThreads / 64);  // 1 KB DMA instructions per wave
+  constexpr int ROWS_PER_LOAD = 1024 / ROWB;
+  static_assert(LPW >= 1, "tile split over waves");
+  __shared__ __attribute__((aligned(1024))) uint8_t ks0[TILE], ks1[TILE], ks2[kStages > 2 ? TILE : 16],
+      ks3[kStages > 3 ? TILE : 16];
+  auto kst = [&](auto J) -> uint8_t* {
+    constexpr int j = decltype(J)::value;
+    return j == 0 ? ks0 : j == 1 ? ks1 : j == 2 ? ks2 : ks3;
+  };
 
   const int G = Hq / Hkv;
   const int P = 128 / G;
   const int item = xcd_remap(blockIdx.x, n_items);
-  const int bh = item / n_pb;
-  const int pb = n_pb - 1 - (item % n_pb);
+  const int bh = item / (n_pb * n_pieces);
+  const int rest = item - bh * (n_pb * n_pieces);
+  const int pb = n_pb - 1 - rest / n_pieces;  // longest rows first
+  const int piece = rest % n_pieces;
   const int b = bh / Hkv, h = bh % Hkv;
   const int p0 = pb * P;
+  const int n_keys = min(S, p0 + P);
+  const int k_begin = piece * kmax;
+  if (k_begin >= n_keys) return;  // this row block needs fewer pieces
+  const int k_end = min(n_keys, k_begin + kmax);
+  const int kt0 = k_begin / kKT;
+  const int n_kt = (k_end - k_begin + kKT - 1) / kKT;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
   const int ci = wave * 32 + col;
   const int gl = ci / P;
   const int dpos = p0 + (ci % P);
   const bool valid = dpos < S;
   const int g = h * G + gl;
+
+  const bf16_t* kbase = k + ((size_t)b * Hkv + h) * (size_t)S * D;
+  auto issue = [&](auto J, int kt) {
+    uint8_t* dst = kst(J);
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      const int I = wave * LPW + j;
+      const int row = I * ROWS_PER_LOAD + lane / CPR;
+      const int pc = lane % CPR;
+      const int lc = pc ^ (row & (CPR - 1));
+      const int t = min(kt * kKT + row, S - 1);
+      dma16(kbase + (size_t)t * D + lc * 8, dst + I * 1024);
+    }
+  };
 
   bf16x8 bq[NS];
   {
@@ -61,54 +122,43 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_lse_kernel(
     for (int s = 0; s < NS; ++s) bq[s] = as_bf16x8(valid ? ldg16(qrow + 16 * s) : make_uint4(0, 0, 0, 0));
   }
 
-  const int n_keys = min(S, p0 + P);
-  const int n_kt = (n_keys + kKT - 1) / kKT;
-  const bf16_t* kbase = k + ((size_t)b * Hkv + h) * (size_t)S * D;
-
-  uint4 pre[PER_T];
-  auto load_tile = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int ch = tid + i * kThreads;
-      const int row = ch / CPR, cc = ch % CPR;
-      const int t = kt * kKT + row;
-      pre[i] = t < S ? ldg16(kbase + (size_t)t * D + cc * 8) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int ch = tid + i * kThreads;
-      const int row = ch / CPR, cc = ch % CPR;
-      *reinterpret_cast<uint4*>(&ks[buf][row * STRIDE + cc * 8]) = pre[i];
-    }
-  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  if (0 < n_kt) issue(I0{}, kt0);
+  if (1 < n_kt && kStages > 2) issue(I1{}, kt0 + 1);
+  if (2 < n_kt && kStages > 3) issue(I2{}, kt0 + 2);
 
   float m = -INFINITY, l = 0.f;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < n_kt) load_tile(kt + 1);
-    const int t0 = kt * kKT;
+  const int sw = col & (CPR - 1);
+  auto step = [&](auto J, int i) {
+    constexpr int j = decltype(J)::value;
+    constexpr int jn = (j + kStages - 1) % kStages;
+    wait_inflight(LPW * min(kStages - 2, n_kt - 1 - i));
+    wait_lgkmcnt0();
+    bare_barrier();  // tile i is in LDS for every wave; tile i-1's stage is free
+    if (i + kStages - 1 < n_kt) issue(std::integral_constant<int, jn>{}, kt0 + i + kStages - 1);
+    const int t0 = (kt0 + i) * kKT;
+    const uint8_t* tile = kst(J);
     f32x16 acc[2];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[sub][r] = 0.f;
-      const bf16_t* arow = &ks[buf][(sub * 32 + col) * STRIDE + 8 * half];
+      const uint8_t* arow = tile + (sub * 32 + col) * ROWB;
 #pragma unroll
       for (int s = 0; s < NS; ++s)
-        acc[sub] = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(arow + 16 * s)), bq[s], acc[sub]);
+        acc[sub] = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(arow + (((2 * s + half) ^ sw) << 4))),
+                          bq[s], acc[sub]);
     }
-    if (t0 + kKT - 1 > p0) {  // tile reaches the diagonal (or past S): causal mask
+    if (t0 + kKT - 1 > p0 || t0 + kKT > k_end) {  // diagonal, past S or past the piece
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int t = t0 + sub * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (t > dpos) acc[sub][r] = -INFINITY;
+          acc[sub][r] = (t > dpos || t >= k_end) ? -INFINITY : acc[sub][r];
         }
     }
     float mx = m;
@@ -126,8 +176,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_lse_kernel(
       l = l * fast_exp2(fmaf(m, c, -mc)) + ts;
       m = mx;
     }
-    if (kt + 1 < n_kt) store_tile(buf ^ 1);
-    __syncthreads();
+  };
+  for (int i = 0; i < n_kt; i += kStages) {
+    step(I0{}, i);
+    if (i + 1 < n_kt) step(I1{}, i + 1);
+    if (kStages > 2 && i + 2 < n_kt) step(I2{}, i + 2);
+    if (kStages > 3 && i + 3 < n_kt) step(I3{}, i + 3);
   }
 
   // merge the two half-waves that share a query column
@@ -140,25 +194,74 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_lse_kernel(
     L = (m > -INFINITY ? l * fast_exp2(fmaf(m, c, -Mc)) : 0.f) +
         (mo > -INFINITY ? lo * fast_exp2(fmaf(mo, c, -Mc)) : 0.f);
   }
-  if (half == 0 && valid) lse[((size_t)b * Hq + g) * S + dpos] = M * scale + logf(L);
+  if (half == 0 && valid) {
+    const size_t row = ((size_t)b * Hq + g) * S + dpos;
+    if (n_pieces == 1) lse[row] = M * scale + logf(L);
+    else part[(size_t)piece * B * Hq * S + row] = make_float2(M, L);
+  }
+}
+
+// Combine the pieces of each row: LSE = scale*M + ln(sum_j L_j 2^((M_j - M) c)).
+__global__ __launch_bounds__(256) void fwd_lse_merge_kernel(const float2* __restrict__ part,
+                                                            float* __restrict__ lse, int B, int Hq,
+                                                            int S, float c, float scale, int P,
+                                                            int kmax) {
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long rows = (long)B * Hq * S;
+  if (idx >= rows) return;
+  const int d = (int)(idx % S);
+  const int n_keys = min(S, (d / P + 1) * P);
+  const int n = (n_keys + kmax - 1) / kmax;
+  float M = -INFINITY;
+  for (int j = 0; j < n; ++j) M = fmaxf(M, part[(size_t)j * rows + idx].x);
+  float L = 0.f;
+  for (int j = 0; j < n; ++j) {
+    const float2 v = part[(size_t)j * rows + idx];
+    if (v.x > -INFINITY) L += v.y * fast_exp2((v.x - M) * c);
+  }
+  lse[idx] = M * scale + logf(L);
 }
 
 }  // namespace
 
-hipError_t launch_fwd_lse(const AttnShape& s, const void* q, const void* k, float* lse,
-                          hipStream_t st) {
+FwdPlan plan_fwd(const AttnShape& s) {
+  FwdPlan p;
   const int G = s.Hq / s.Hkv;
-  const int P = 128 / G;
-  const int n_pb = (s.S + P - 1) / P;
-  const int n_items = s.B * s.Hkv * n_pb;
+  p.P = 128 / G;
+  p.n_pb = (s.S + p.P - 1) / p.P;
+  const long rowblocks = (long)s.B * s.Hkv * p.n_pb;
+  long want = (KVPOP_FWD_TARGET_ITEMS + rowblocks - 1) / rowblocks;
+  const long cap = (s.S + 511) / 512;
+  if (want > cap) want = cap;
+  if (want < 1) want = 1;
+  int kmax = (int)((s.S + want - 1) / want);
+  kmax = (kmax + kKT - 1) / kKT * kKT;
+  p.kmax = kmax;
+  p.n_pieces = (s.S + kmax - 1) / kmax;
+  p.partial_floats = p.n_pieces > 1 ? (size_t)2 * p.n_pieces * s.B * s.Hq * (size_t)s.S : 0;
+  return p;
+}
+
+hipError_t launch_fwd_lse(const AttnShape& s, const void* q, const void* k, float* lse,
+                          float* workspace, hipStream_t st) {
+  const FwdPlan p = plan_fwd(s);
+  const int n_items = s.B * s.Hkv * p.n_pb * p.n_pieces;
   const float c = s.scale * kLog2e;
   dim3 grid(n_items), block(kThreads);
+  float2* part = reinterpret_cast<float2*>(workspace);
   if (s.D == 128)
     hipLaunchKernelGGL(fwd_lse_kernel<128>, grid, block, 0, st, (const bf16_t*)q, (const bf16_t*)k,
-                       lse, s.Hq, s.Hkv, s.S, c, s.scale, n_pb, n_items);
+                       lse, part, s.B, s.Hq, s.Hkv, s.S, c, s.scale, p.n_pb, p.kmax, p.n_pieces,
+                       n_items);
   else
     hipLaunchKernelGGL(fwd_lse_kernel<64>, grid, block, 0, st, (const bf16_t*)q, (const bf16_t*)k,
-                       lse, s.Hq, s.Hkv, s.S, c, s.scale, n_pb, n_items);
+                       lse, part, s.B, s.Hq, s.Hkv, s.S, c, s.scale, p.n_pb, p.kmax, p.n_pieces,
+                       n_items);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.n_pieces == 1) return e;
+  const long rows = (long)s.B * s.Hq * s.S;
+  hipLaunchKernelGGL(fwd_lse_merge_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st,
+                     part, lse, s.B, s.Hq, s.S, c, s.scale, p.P, p.kmax);
   return hipGetLastError();
 }
 

@@ -15,20 +15,26 @@ struct AttnShape {
 };
 
 // ---- main causal pass (log-normalizers only) ----
+struct FwdPlan {
+  int P;          // query positions per row block (128 / G)
+  int n_pb;       // row blocks per (b, KV head)
+  int kmax;       // keys per piece of a split row (multiple of 64)
+  int n_pieces;   // pieces of the longest row; 1 = no split
+  size_t partial_floats;  // workspace floats (0 without split)
+};
+FwdPlan plan_fwd(const AttnShape& s);
 hipError_t launch_fwd_lse(const AttnShape& s, const void* q, const void* k, float* lse,
-                          hipStream_t st);
+                          float* workspace, hipStream_t st);
 
 // ---- transposed future-attention pass ----
 struct TargetPlan {
+  int waves;      // waves per workgroup: 4 (128-key blocks) or 8 (256-key blocks)
+  int key_block;  // keys per work item (32 per wave)
   int chunk;      // query positions per work item (multiple of 32)
   int n_chunks;   // ceil(S / chunk)
-  int n_kb;       // key blocks of kKeyBlock keys
+  int n_kb;       // key blocks
   size_t partial_floats;  // workspace floats (per-query-head partials)
 };
-#ifndef KVPOP_TGT_KEY_BLOCK
-#define KVPOP_TGT_KEY_BLOCK 256
-#endif
-constexpr int kKeyBlock = KVPOP_TGT_KEY_BLOCK;  // keys per work item (32 or 64 per wave)
 TargetPlan plan_target(const AttnShape& s, int window);
 hipError_t launch_future_target(const AttnShape& s, const void* q, const void* k,
                                 const float* lse, int window, int lookahead, int agg,

@@ -68,6 +68,7 @@ typedef struct {
 /* Workspace sizes (bytes) for the calls that take one. */
 #define KVPOP_OP_FUTURE_TARGET 0
 #define KVPOP_OP_DECODE 1
+#define KVPOP_OP_FWD_LSE 2
 
 int kvpop_abi_version(void);
 const char* kvpop_status_string(kvpop_status s);
@@ -80,9 +81,13 @@ const char* kvpop_status_string(kvpop_status s);
  * (the diagonal t = d is included, so no row is empty).  No S x S matrix is
  * formed.  q, k: bf16 as laid out above; lse: fp32 [B][Hq][S], written in
  * full.  Accumulation is fp32.
+ *   workspace: kvpop_workspace_bytes(KVPOP_OP_FWD_LSE, dims, 0) bytes (zero
+ *   for shapes with many row blocks; then it may be NULL), 16-byte aligned,
+ *   no initialisation needed.  It holds partial (max, sum) pairs when long
+ *   causal rows are split to balance the launch.
  */
 kvpop_status kvpop_fwd_lse(const kvpop_dims* dims, const void* q, const void* k, float* lse,
-                           hipStream_t stream);
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * kvpop_future_attn_target -- transposed future-attention pass.

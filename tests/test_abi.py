@@ -42,18 +42,24 @@ def test_exports_match_header(lib):
 
 def test_dims_validation(lib):
     def fwd(d):
-        return lib.kvpop_fwd_lse(ctypes.byref(d), GOOD, GOOD, GOOD, None)
+        return lib.kvpop_fwd_lse(ctypes.byref(d), GOOD, GOOD, GOOD, None, 0, None)
 
-    assert lib.kvpop_fwd_lse(None, GOOD, GOOD, GOOD, None) == 1
+    assert lib.kvpop_fwd_lse(None, GOOD, GOOD, GOOD, None, 0, None) == 1
     assert fwd(kv.dims(0, 32, 8, 4096, 128)) == 1
     assert fwd(kv.dims(1, 32, 8, 0, 128)) == 1
     assert fwd(kv.dims(1, 30, 8, 4096, 128)) == 1   # Hq % Hkv
     assert fwd(kv.dims(1, 24, 8, 4096, 128)) == 2   # group of 3
     assert fwd(kv.dims(1, 32, 8, 4096, 96)) == 2    # head dim
     assert fwd(kv.dims(1, 32, 8, 4096, 128, float("nan"))) == 1
-    d = kv.dims(1, 32, 8, 4096, 128)
-    assert lib.kvpop_fwd_lse(ctypes.byref(d), None, GOOD, GOOD, None) == 1
-    assert lib.kvpop_fwd_lse(ctypes.byref(d), P(0x10008), GOOD, GOOD, None) == 1  # misaligned
+    d = kv.dims(1, 2, 1, 4096, 128)
+    need = kv.workspace_bytes(kv.OP_FWD_LSE, d)
+    assert need > 0  # few row blocks: long causal rows are split
+    assert lib.kvpop_fwd_lse(ctypes.byref(d), None, GOOD, GOOD, GOOD, need, None) == 1
+    assert lib.kvpop_fwd_lse(ctypes.byref(d), P(0x10008), GOOD, GOOD, GOOD, need, None) == 1  # misaligned
+    assert lib.kvpop_fwd_lse(ctypes.byref(d), GOOD, GOOD, GOOD, None, need, None) == 1
+    assert lib.kvpop_fwd_lse(ctypes.byref(d), GOOD, GOOD, GOOD, GOOD, need - 8, None) == 3
+    for big in (kv.dims(1, 32, 8, 32768, 128), kv.dims(1, 32, 8, 4096, 128)):
+        assert kv.workspace_bytes(kv.OP_FWD_LSE, big) == 0  # enough row blocks: no split
 
 
 def test_target_validation(lib):

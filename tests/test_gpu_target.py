@@ -89,6 +89,22 @@ def test_ragged_and_degenerate_shapes(kv, B, Hq, Hkv, S, D, window):
         assert not f32(m).any()
 
 
+@pytest.mark.parametrize("agg,lookahead,count_normalize", [("sum", -1, False), ("max", 300, True)])
+def test_many_keys_launch_full_parity(kv, agg, lookahead, count_normalize):
+    """B*Hkv*S = 67584 keys: above the size where the transposed pass switches
+    from 128-key to 256-key work items; every key compared with the oracle."""
+    B, Hq, Hkv, S, D, window = 11, 6, 3, 2048, 64, 100
+    q = synth.bf16(synth.normal((B, Hq, S, D), 21)).cuda()
+    k = synth.bf16(synth.normal((B, Hkv, S, D), 22)).cuda()
+    lse, m, ph = _run(kv, q, k, window, agg=agg, lookahead=lookahead,
+                      count_normalize=count_normalize)
+    olse, om, oph = _full_oracle(q, k, window, agg=agg, lookahead=lookahead,
+                                 count_normalize=count_normalize)
+    assert_close(f32(lse), olse, LSE_ATOL, 0, "lse")
+    assert_close(f32(m), om, MASS_ATOL, MASS_RTOL, "mass")
+    assert_close(f32(ph), _per_qhead(oph), MASS_ATOL, MASS_RTOL, "per-head")
+
+
 def test_deterministic(kv):
     w = synth.QWEN4B
     q, k, _ = synth.attention_inputs(w, seed=3, device="cuda")
