@@ -31,6 +31,15 @@ import synth  # noqa: E402
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+
+# HBM bytes of one kvpop_future_attn_target call (transposed pass + merge) on
+# the Qwen3-4B layer workload, from two rocprofv3 --pmc runs (FETCH_SIZE, then
+# WRITE_SIZE, KiB per dispatch) each scaled by what the same counter reads for
+# a torch copy of known size (`bench.py --calibrate-copy`).  Valid only for
+# the kernel sources it was taken on: bench reports null once they change.
+TRAFFIC_SOURCES = ("future_target.hip", "common.h", "launch.h")
+TRAFFIC = {"sha256": "57d627d713c32b4f51b3518b47bebc3f765aa4e21b076bfc6e91433553874db3",
+           "fetch_bytes": 2 * (20165.4 + 543.0) * 1024, "write_bytes": (1024.0 + 128.0) * 1024}
 METRIC = "future-attn target keys/s + MFMA util; bounded-cache decode steps/s + HBM util"
 
 
@@ -211,10 +220,13 @@ def bench_decode(kv, steps, layers, seed=5):
     }
 
 
-def cpu_baseline():
+def cpu_baseline(min_seconds=10.0):
     """The oracle (plain C, double, all host threads) on the target work of
-    the layer workload: LSE of all 32 query heads and the future mass of all
-    8 x 4096 keys, then the oracle's selection."""
+    the layer workload -- LSE of all 32 query heads, the future mass of all
+    8 x 4096 keys, then the oracle's selection -- repeated until at least
+    `min_seconds` have passed; plus the oracle's decode step (cache step with
+    given scores + decode attention) on a few (sequence, layer) units of the
+    bounded-decode workload, scaled to whole steps."""
     import numpy as np
 
     import oracle
@@ -224,15 +236,101 @@ def cpu_baseline():
     qf = np.ascontiguousarray(q.float().numpy())
     kf = np.ascontiguousarray(k.float().numpy())
     threads = len(os.sched_getaffinity(0))
+    reps = 0
     t0 = time.perf_counter()
-    lse = oracle.lse(qf, kf, nthreads=threads)
-    m = oracle.future_mass(qf, kf, lse, w.window, nthreads=threads)
-    oracle.select(m.astype(np.float32), w.n_sink, w.window, w.budget)
-    dt = time.perf_counter() - t0
+    while True:
+        lse = oracle.lse(qf, kf, nthreads=threads)
+        m = oracle.future_mass(qf, kf, lse, w.window, nthreads=threads)
+        oracle.select(m.astype(np.float32), w.n_sink, w.window, w.budget)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
     keys = w.B * w.Hkv * w.S
-    return {"value": keys / dt, "unit": "keys/s", "cores": threads, "kind": "oracle",
-            "sample": f"one full {w.name} step's target work (LSE of {w.Hq} query heads, future "
-                      f"mass of {keys} keys, selection), no decode step; {dt:.1f} s"}
+    out = {"value": keys * reps / dt, "unit": "keys/s", "cores": threads, "kind": "oracle",
+           "sample": f"{reps} full {w.name} steps' target work (LSE of {w.Hq} query heads, future "
+                     f"mass of {keys} keys, selection), no decode step; {dt:.1f} s"}
+    out["decode"] = cpu_decode_baseline(threads)
+    return out
+
+
+def cpu_decode_baseline(threads, units=4, steps=16):
+    """Oracle decode steps/s on the bounded-decode workload, from `units`
+    (sequence, layer) pairs advanced `steps` steps (one cache step with given
+    scores and one decode attention each), scaled by the fraction of the
+    64 x 36 units of a whole step."""
+    import numpy as np
+
+    import oracle
+
+    w = synth.DECODE
+    Hq, Hkv, D, bud, S = w.Hq, w.Hkv, w.D, w.budget, w.S
+    g = np.random.default_rng(5)
+    n_sink, window, delay = w.n_sink, w.window, w.extra["delay"]
+    k_sel = bud - n_sink - window
+
+    def bf16_bits(shape):  # N(0, 0.5^2) truncated to bf16 bit patterns
+        x = (g.standard_normal(shape) * w.std).astype(np.float32)
+        return (x.view(np.uint32) >> 16).astype(np.uint16)
+
+    t_total = 0.0
+    for u in range(units):
+        # a full cache as the prefix selection leaves it: sinks, the k
+        # selected tokens (ascending), the window ring
+        sel = np.sort(g.choice(np.arange(n_sink, S - window), k_sel, replace=False))
+        pos = np.concatenate([np.arange(n_sink), sel, np.zeros(window, np.int64)])
+        ring = np.arange(S - window, S)
+        pos[n_sink + k_sel + ring % window] = ring
+        sp = np.broadcast_to(pos.astype(np.int32), (1, Hkv, bud)).copy()
+        ss = g.standard_normal((1, Hkv, bud)).astype(np.float32)
+        state = {"slot_pos": sp, "slot_score": ss, "kc": bf16_bits((1, Hkv, bud, D)),
+                 "vc": bf16_bits((1, Hkv, bud, D))}
+        for i in range(steps):
+            kn = bf16_bits((1, Hkv, D))
+            vn = bf16_bits((1, Hkv, D))
+            sr = g.standard_normal((1, Hkv)).astype(np.float32)
+            qn = g.standard_normal((1, Hq, D)).astype(np.float32)
+            t0 = time.perf_counter()
+            oracle.cache_step(state, kn, vn, sr, n_sink, window, delay, S + i)
+            oracle.decode_attend(qn, oracle.bf16_bits_to_f32(state["kc"]),
+                                 oracle.bf16_bits_to_f32(state["vc"]), state["slot_pos"],
+                                 nthreads=threads)
+            t_total += time.perf_counter() - t0
+    per_unit_step = t_total / (units * steps)
+    whole = w.B * 36 * per_unit_step
+    return {"value": 1.0 / whole, "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"{units} (sequence, layer) units x {steps} steps of the {w.name} workload "
+                      f"(cache step with given scores + decode attention), {t_total:.1f} s, scaled "
+                      f"by 64 x 36 units per step"}
+
+
+def traffic_bytes():
+    """The recorded HBM traffic of the target call, or None when the kernel
+    sources differ from those it was measured on."""
+    import hashlib
+
+    if TRAFFIC is None:
+        return None
+    h = hashlib.sha256()
+    for name in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "future_attention_scoring_kvpop_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != TRAFFIC["sha256"]:
+        return None
+    return TRAFFIC["fetch_bytes"] + TRAFFIC["write_bytes"]
+
+
+def calibrate_copy(mib):
+    """A plain device copy of known size for scaling the FETCH_SIZE and
+    WRITE_SIZE counters: 5 launches of torch's copy kernel over `mib` MiB."""
+    n = mib << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}), flush=True)
 
 
 def main():
@@ -244,11 +342,17 @@ def main():
     ap.add_argument("--decode-layers", type=int, default=36)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, metavar="MIB", default=0,
+                    help="only run a plain copy of MIB MiB (counter calibration)")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the KVpop hot path is sharded by (batch, KV head) with no "
               "communication, and this build runs on a single MI355X; use --gpus 1.", flush=True)
         sys.exit(2)
+
+    if a.calibrate_copy:
+        calibrate_copy(a.calibrate_copy)
+        return
 
     import future_attention_scoring_kvpop_amd as kv
 
@@ -276,7 +380,7 @@ def main():
                            "decode_attend"},
         "roofline": {"bound": "mfma", "kernel": "kvpop_future_attn_target (transposed pass + merge)",
                      "achieved": achieved_tr, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved_tr / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                     "frac": achieved_tr / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic_bytes(),
                      "flops_per_launch": f_tr, "ms_per_launch": t_tr},
         "kernels": {"fwd_lse": {"ms": t_fwd, "tflops": achieved_fwd,
                                 "frac": achieved_fwd / MFMA_BF16_PEAK_TFLOPS},
