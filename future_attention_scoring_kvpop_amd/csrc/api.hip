@@ -66,7 +66,7 @@ size_t kvpop_workspace_bytes(int op, const kvpop_dims* dims, int window) {
   if (check_dims(dims, &s) != KVPOP_OK) return 0;
   if (op == KVPOP_OP_FUTURE_TARGET) {
     if (window < 0) return 0;
-    return kvpop::plan_target(s, window).partial_floats * sizeof(float);
+    return kvpop::plan_target(s, window).workspace_bytes;
   }
   if (op == KVPOP_OP_DECODE) return kvpop::plan_decode(s).workspace_floats * sizeof(float);
   if (op == KVPOP_OP_FWD_LSE) return kvpop::plan_fwd(s).partial_floats * sizeof(float);
@@ -104,7 +104,7 @@ kvpop_status kvpop_future_attn_target(const kvpop_dims* dims, const void* q, con
       !aligned(workspace, 256) || (mass_per_qhead && !aligned(mass_per_qhead, 4)))
     return KVPOP_ERR_INVALID_ARGUMENT;
   if ((double)s.S + window + 512.0 > 2.0e9) return KVPOP_ERR_UNSUPPORTED;
-  if (workspace_bytes < kvpop::plan_target(s, window).partial_floats * sizeof(float))
+  if (workspace_bytes < kvpop::plan_target(s, window).workspace_bytes)
     return KVPOP_ERR_WORKSPACE_TOO_SMALL;
   const int la = (lookahead < 0 || lookahead >= s.S) ? -1 : lookahead;  // >= S-1 has no effect
   return from_hip(kvpop::launch_future_target(s, q, k, lse, window, la, (int)agg,

@@ -10,12 +10,19 @@
 //   m_t^(g) = sum_{d=t+w}^{end_t} exp2(s_dt * scale*log2e - LSE_d * log2e)
 //
 // gfx950 mapping
-//   * A work item is (b, KV head h, key block, query chunk).  Each wave of
-//     the item's workgroup keeps 32 keys resident as MFMA A fragments and
-//     streams the chunk's queries of all G heads of the group as B
-//     fragments: v_mfma_f32_32x32x16_bf16 yields S^T[key][query].  About 120
-//     registers per wave keep four waves per SIMD resident, so the MFMA phase
-//     of one wave overlaps the exp2/accumulate phase of the others.
+//   * The work is the list of 32x32 (key, query) squares in the order
+//     (b, KV head h), query chunk, key block, query head, query tile; each
+//     workgroup takes one equal, contiguous share of it, and the shares form
+//     whole rounds of resident workgroups, so the causal triangle costs no
+//     idle tail.  Shares are capped, so the workgroups in flight on one XCD
+//     cover one or two query chunks (about 2 MiB of Q), which stay in that
+//     XCD's L2 while every key block of the chunk streams them.  Within a
+//     key block, each wave
+//     keeps 32 keys resident as MFMA A fragments and streams the query tiles
+//     of all G heads of the group as B fragments:
+//     v_mfma_f32_32x32x16_bf16 yields S^T[key][query].  About 120 registers
+//     per wave keep four waves per SIMD resident, so the MFMA phase of one
+//     wave overlaps the exp2/accumulate phase of the others.
 //   * All waves of a workgroup share each query tile (32 queries).  Tiles
 //     reach LDS by direct global->LDS DMA into a ring of stages, requested
 //     two tiles ahead; each stage is its own LDS object so the compiler
@@ -24,17 +31,23 @@
 //     fragment reads bank-conflict free.  A bare s_barrier plus explicit
 //     vmcnt/lgkmcnt waits orders the ring.
 //   * Workgroups of 8 waves (256 keys) halve the L2 traffic per key-query
-//     pair against 4 waves (128 keys); launches with few keys use 4 waves to
-//     get more, shorter items.
+//     pair against 4 waves (128 keys); launches with few keys use 4 waves.
 //   * Each lane owns one query column and 16 key rows, so per-key sums stay
 //     in registers across every query tile and head; they are reduced
 //     across lanes once per item by a register transpose-reduce.
 //   * Tiles whose 32x32 (key, query) square lies fully inside the allowed
 //     region take a mask-free path (one FMA, one exp2, one add per pair);
 //     fully masked squares are skipped; only the diagonal squares mask.
-//   * Items write partial sums per (chunk, key); a second kernel sums the
-//     chunks of each key in a fixed order (deterministic), aggregates the
-//     group and applies count normalisation.
+//   * A workgroup writes one partial sum per key for every run (chunk and
+//     key block, or chunk, key block and query head) its share touches, into
+//     piece run + wg: runs and workgroups both advance monotonically along
+//     the list, so no two (run, workgroup) pairs share a piece.  The
+//     workgroup holding a run's first square records where the run starts.
+//     A second kernel sums each key's pieces over chunks and workgroups in a
+//     fixed order (deterministic for a given device), aggregates the group
+//     and applies count normalisation.
+#include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -43,23 +56,34 @@
 namespace kvpop {
 namespace {
 
-// Work split: query chunks shrink from the maximum (powers of two) until the
-// launch holds enough items to fill the chip, but not below the minimum.
-#ifndef KVPOP_TGT_MAX_CHUNK
-#define KVPOP_TGT_MAX_CHUNK 2048
+// Work split: the largest share (squares per workgroup), the smallest share
+// worth a workgroup, and the bytes of Q one query chunk should span.
+#ifndef KVPOP_TGT_SHARE_CAP
+#define KVPOP_TGT_SHARE_CAP 384
 #endif
-#ifndef KVPOP_TGT_MIN_CHUNK
-#define KVPOP_TGT_MIN_CHUNK 256
+// launches with at least this many rounds of non-empty runs give each
+// workgroup one whole run (all workgroups then stream a chunk's query tiles
+// in step, which keeps them in L2); smaller ones split the list evenly
+#ifndef KVPOP_TGT_ITEM_ROUNDS
+#define KVPOP_TGT_ITEM_ROUNDS 8
 #endif
-#ifndef KVPOP_TGT_MIN_ITEMS
-#define KVPOP_TGT_MIN_ITEMS 4096
+#ifndef KVPOP_TGT_MIN_SHARE
+#define KVPOP_TGT_MIN_SHARE 16
+#endif
+#ifndef KVPOP_TGT_CHUNK_BYTES
+#define KVPOP_TGT_CHUNK_BYTES (2 << 20)
 #endif
 #ifndef KVPOP_TGT_STAGES
 #define KVPOP_TGT_STAGES 3
 #endif
 // B * Hkv * S at or below which the 4-wave (128-key) workgroups are used
+// waves per SIMD the kernel is compiled for (sets its register budget:
+// 512 / n registers per lane)
+#ifndef KVPOP_TGT_WPE
+#define KVPOP_TGT_WPE 4
+#endif
 #ifndef KVPOP_TGT_SMALL_KEYS
-#define KVPOP_TGT_SMALL_KEYS 65536
+#define KVPOP_TGT_SMALL_KEYS 0
 #endif
 
 constexpr int kQT = 32;                    // queries per LDS tile
@@ -79,39 +103,29 @@ __device__ __forceinline__ void xreduce_step(float* v, int lane) {
   }
 }
 
-// Wait until at most n of this wave's DMA instructions are in flight
-// (n is wave-uniform: later tiles x this wave's instructions per tile).
-__device__ __forceinline__ void wait_inflight(int n) {
-  if (n <= 0) wait_vmcnt<0>();
-  else if (n == 1) wait_vmcnt<1>();
-  else if (n == 2) wait_vmcnt<2>();
-  else if (n == 3) wait_vmcnt<3>();
-  else if (n == 4) wait_vmcnt<4>();
-  else if (n == 5) wait_vmcnt<5>();
-  else wait_vmcnt<6>();
-}
-
 template <int D, bool PER_HEAD, int WAVES>
-__global__ __launch_bounds__(64 * WAVES, 16 / WAVES) void future_target_kernel(
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KVPOP_TGT_WPE, KVPOP_TGT_WPE))) void future_target_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const float* __restrict__ lse,
-    float* __restrict__ partial, int Hq, int Hkv, int S, int window, int lookahead, float c,
-    int chunk, int n_chunks, int n_kb, int n_items) {
-  constexpr int KB = 32 * WAVES;            // keys per work item
+    float* __restrict__ partial, long long* __restrict__ run_start, int Hq, int Hkv, int S,
+    int window, int lookahead, float c, TargetGeom geo) {
+  constexpr int KB = 32 * WAVES;            // keys per key block
   constexpr int NS = D / 16;                // MFMA k-slices
   constexpr int CPR = D / 8;                // 16-byte chunks per row
   constexpr int ROWB = D * 2;               // bytes per query row
   constexpr int TILE = kQT * ROWB;          // bytes per query tile
   constexpr int NQI = TILE / 1024;          // 1 KB DMA instructions per query tile
-  constexpr int QPW = NQI >= WAVES ? NQI / WAVES : 1;  // per loading wave
-  constexpr int Q_WAVES = NQI >= WAVES ? WAVES : NQI;  // waves that load query rows
+  static_assert(NQI % WAVES == 0, "every wave loads the same share of a tile");
+  constexpr int QPW = NQI / WAVES;          // query-row DMAs per wave per tile
+  constexpr int PT = QPW + 1;               // DMA instructions per wave per tile (+ normalizers)
   constexpr int ROWS_PER_LOAD = 1024 / ROWB;
-  static_assert(NQI % Q_WAVES == 0, "tile split over waves");
   // One LDS object per ring stage: every access below names its stage at
   // compile time, so a DMA into one stage is never mistaken for a write to
-  // the stage being read.
+  // the stage being read.  Each wave keeps its own copy of a tile's
+  // normalizers (64 floats: lanes 32-63 duplicate lanes 0-31).
   __shared__ __attribute__((aligned(1024))) uint8_t qs0[TILE], qs1[TILE], qs2[kStages > 2 ? TILE : 16],
       qs3[kStages > 3 ? TILE : 16];
-  __shared__ __attribute__((aligned(256))) float ls0[64], ls1[64], ls2[64], ls3[64];
+  __shared__ __attribute__((aligned(256))) float ls0[64 * WAVES], ls1[64 * WAVES],
+      ls2[kStages > 2 ? 64 * WAVES : 1], ls3[kStages > 3 ? 64 * WAVES : 1];
   auto qst = [&](auto J) -> uint8_t* {
     constexpr int j = decltype(J)::value;
     return j == 0 ? qs0 : j == 1 ? qs1 : j == 2 ? qs2 : qs3;
@@ -122,54 +136,95 @@ __global__ __launch_bounds__(64 * WAVES, 16 / WAVES) void future_target_kernel(
   };
 
   const int G = Hq / Hkv;
-  const int item = xcd_remap(blockIdx.x, n_items);
-  const int kb = item % n_kb;
-  const int rest = item / n_kb;
-  const int cidx = rest % n_chunks;
-  const int bh = rest / n_chunks;
-  const int b = bh / Hkv, h = bh % Hkv;
-  const int t0 = kb * KB;
-  if (t0 + window >= S) return;
-  const int c_first = (t0 + window) / chunk;
-  int c_last = n_chunks - 1;
-  if (lookahead >= 0) c_last = min(c_last, (t0 + KB - 1 + window + lookahead) / chunk);
-  if (cidx < c_first || cidx > c_last) return;
-  const int d_lo = max(cidx * chunk, t0 + window);
-  int d_hi = min((cidx + 1) * chunk, S);
-  if (lookahead >= 0) d_hi = min(d_hi, t0 + KB + window + lookahead);
-  const int dt0 = d_lo & ~(kQT - 1);
-  const int n_qt = (d_hi - dt0 + kQT - 1) / kQT;
-  const int n_iter = G * n_qt;
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);  // position of this share in the list
+  long long x, x_end;
+  int bh, ch, kb = 0, off;
+  if (geo.item_mode) {
+    // one whole run: wg is the dense run index (b, h), chunk, key block
+    kb = wg % geo.n_kb;
+    ch = (wg / geo.n_kb) % geo.n_chunks;
+    bh = wg / (geo.n_kb * geo.n_chunks);
+    const int n = n_qtiles(geo, ch, kb);
+    if (n == 0) return;
+    x = 0;
+    x_end = (long long)G * n;
+    off = 0;
+  } else {
+  x = (long long)wg * geo.share;
+  x_end = min(geo.total, x + geo.share);
+  if (x >= x_end) return;
+  // locate the share's first square: (b, h), chunk, key block, offset in the run
+  bh = (int)(x / geo.per_bh);
+  {
+    const long long rem = x - (long long)bh * geo.per_bh;
+    int lo = 0, hi = geo.n_chunks - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (geo.cpre[mid] <= rem) lo = mid;
+      else hi = mid - 1;
+    }
+    ch = lo;
+    long long r2 = rem - geo.cpre[ch];
+    for (;; ++kb) {
+      const long long n = (long long)G * n_qtiles(geo, ch, kb);
+      if (r2 < n) break;
+      r2 -= n;
+    }
+    off = (int)r2;
+  }
+  }
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int col = lane & 31, half = lane >> 5;
-  const int ts = t0 + 32 * wave;  // this wave's 32 keys
-  // this wave's share of each tile's DMA: query rows and/or the normalizers
-  const bool loads_q = wave < Q_WAVES;
-  const bool loads_l = wave == WAVES - 1;
-  const int per_tile = (loads_q ? QPW : 0) + (loads_l ? 1 : 0);
+  const int frow = col * ROWB;      // this lane's query row in a tile
+  const int sw = col & (CPR - 1);   // its swizzle
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
 
-  // DMA of query tile `it` (head-major, then position) into stage J.
-  auto issue = [&](auto J, int it) {
-    uint8_t* qd = qst(J);
-    float* ld = lst(J);
-    const int gl = it / n_qt;
-    const int d0 = dt0 + (it - gl * n_qt) * kQT;
-    const size_t head = (size_t)b * Hq + h * G + gl;
+  for (bool first = true;; first = false) {
+  const int nq = n_qtiles(geo, ch, kb);
+  const int n_iter = (int)min((long long)(G * nq - off), x_end - x);
+  const int b = bh / Hkv, h = bh - (bh / Hkv) * Hkv;
+  const int t0 = kb * KB;
+  const int dt0 = 32 * max(ch * geo.ct, kb * geo.kbt + geo.w_t);  // the run's first query tile
+  const int ts = t0 + 32 * wave;  // this wave's 32 keys
+  const long long run = ((long long)bh * geo.n_chunks + ch) * geo.n_kb + kb;
+  const long long run0 = run * (PER_HEAD ? G : 1);
+  const size_t head0 = (size_t)b * Hq + (size_t)h * G;  // first query head of the group
+  if (!geo.item_mode && off == 0 && tid == 0) run_start[run] = x;
+  if (!first) {
+    wait_lgkmcnt0();  // every wave is done reading the previous block's stages
+    bare_barrier();
+  }
+
+  // tile counters (query head of the group, tile in the run) of the next
+  // tile to fetch and of the tile being computed
+  int ig = off / nq;
+  int iq = off - ig * nq;
+  int cg = ig, cq = iq;
+
+  // DMA of tile (ig, iq) into stage J, then advance to the next tile.
+  auto issue = [&](auto J) {
+    const size_t head = head0 + ig;
+    const int d0 = dt0 + iq * kQT;
     const bf16_t* qb = q + head * S * D;
-    if (loads_q) {
+    // each lane fetches one 16-byte chunk of a query row; chunks are
+    // XOR-swizzled by row in LDS, so the lane holds logical chunk pc ^ row
 #pragma unroll
-      for (int j = 0; j < QPW; ++j) {
-        const int I = wave * QPW + j;
-        const int row = I * ROWS_PER_LOAD + lane / CPR;
-        const int pc = lane % CPR;              // physical chunk written by this lane
-        const int lc = pc ^ (row & (CPR - 1));  // logical chunk it holds
-        const int d = min(d0 + row, S - 1);
-        dma16(qb + (size_t)d * D + lc * 8, qd + I * 1024);
-      }
+    for (int j = 0; j < QPW; ++j) {
+      const int row = (wave * QPW + j) * ROWS_PER_LOAD + lane / CPR;
+      const int lc = (lane % CPR) ^ (row & (CPR - 1));
+      const int d = min(d0 + row, S - 1);
+      dma16(qb + (size_t)d * D + lc * 8, qst(J) + (wave * QPW + j) * 1024);
     }
-    if (loads_l && lane < kQT) dma4(lse + head * S + min(d0 + lane, S - 1), ld);
+    dma4(lse + head * S + min(d0 + col, S - 1), lst(J) + wave * 64);
+    if (++iq == nq) {
+      iq = 0;
+      ++ig;
+    }
   };
 
   bf16x8 ka[NS];
@@ -197,65 +252,88 @@ __global__ __launch_bounds__(64 * WAVES, 16 / WAVES) void future_target_kernel(
     const int r = col & 15;
     const int t = ts + 8 * (r >> 2) + 4 * half + (r & 3);
     if (col < 16 && t < S) {
-      const size_t base = PER_HEAD ? ((size_t)bh * G + gout) : (size_t)bh;
-      partial[(base * n_chunks + cidx) * S + t] = v[0];
+      const long long piece = run0 + (PER_HEAD ? gout : 0) + (geo.item_mode ? 0 : wg);
+      partial[piece * KB + (t - t0)] = v[0];
     }
   };
 
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  using I3 = std::integral_constant<int, 3>;
   // prologue: tiles 0 .. kStages-2 into stages 0 .. kStages-2
-  if (0 < n_iter) issue(I0{}, 0);
-  if (1 < n_iter && kStages > 2) issue(I1{}, 1);
-  if (2 < n_iter && kStages > 3) issue(I2{}, 2);
+  if (0 < n_iter) issue(I0{});
+  if (1 < n_iter && kStages > 2) issue(I1{});
+  if (2 < n_iter && kStages > 3) issue(I2{});
 
-  // One iteration on tile `it`, which lives in stage J; the stage of tile
+  // One step on local tile `it`, which lives in stage J; the stage of tile
   // it-1 (J-1 mod kStages) is refilled with tile it+kStages-1.
   auto step = [&](auto J, int it) {
     constexpr int j = decltype(J)::value;
     constexpr int jn = (j + kStages - 1) % kStages;
-    wait_inflight(per_tile * min(kStages - 2, n_iter - 1 - it));
+    // tiles issued after this one: min(kStages - 2, n_iter - 1 - it)
+    const int later = min(kStages - 2, n_iter - 1 - it);
+    if (later >= kStages - 2) wait_vmcnt<PT * (kStages - 2)>();
+    else if (kStages == 4 && later == 1) wait_vmcnt<PT>();
+    else wait_vmcnt<0>();
     wait_lgkmcnt0();  // this wave's reads of earlier stages have completed
     bare_barrier();   // tile `it` is in LDS for every wave; tile it-1's stage is free
-    if (it + kStages - 1 < n_iter) issue(std::integral_constant<int, jn>{}, it + kStages - 1);
-    const int gl = it / n_qt;
-    const int d0 = dt0 + (it - gl * n_qt) * kQT;
+    if (it + kStages - 1 < n_iter) issue(std::integral_constant<int, jn>{});
+    const int d0 = dt0 + cq * kQT;
     const bool skip = ts >= S || d0 + kQT - 1 < ts + window ||
                       (lookahead >= 0 && d0 > ts + 31 + window + lookahead);
     if (!skip) {
-      const float L2 = lst(J)[col] * kLog2e;
-      const uint8_t* tile = qst(J) + col * ROWB;
-      const int sw = col & (CPR - 1);
+      const uint8_t* tile = qst(J) + frow;
+      u32x4 bu[NS];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) bu[s] = *reinterpret_cast<const u32x4*>(tile + (((2 * s + half) ^ sw) << 4));
+      float lraw = lst(J)[wave * 64 + lane];
+      // all fragment reads are issued before one wait, not one wait per MFMA
+      if constexpr (NS == 8)
+        asm volatile("" ::"v"(bu[0]), "v"(bu[1]), "v"(bu[2]), "v"(bu[3]), "v"(bu[4]), "v"(bu[5]),
+                     "v"(bu[6]), "v"(bu[7]), "v"(lraw));
+      else
+        asm volatile("" ::"v"(bu[0]), "v"(bu[1]), "v"(bu[2]), "v"(bu[3]), "v"(lraw));
+      // queries past the sequence end get L = +inf, so their terms vanish
+      const float L2 = d0 + col < S ? lraw * kLog2e : __builtin_inff();
       f32x16 acc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-      for (int s = 0; s < NS; ++s)
-        acc = mfma32(ka[s], as_bf16x8(*reinterpret_cast<const uint4*>(tile + (((2 * s + half) ^ sw) << 4))), acc);
-      const bool full = d0 >= ts + 31 + window && d0 + kQT - 1 < S &&
+      for (int s = 0; s < NS; ++s) {
+        bf16x8 bq;
+        __builtin_memcpy(&bq, &bu[s], 16);
+        acc = mfma32(ka[s], bq, acc);
+      }
+      const bool full = d0 >= ts + 31 + window &&
                         (lookahead < 0 || d0 + kQT - 1 <= ts + window + lookahead);
       if (full) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) macc[r] += fast_exp2(fmaf(acc[r], c, -L2));
       } else {
-        // d - t - w for row r = base - (8*(r/4) + r%4)
-        const int d = d0 + col;
-        const int base = d - ts - 4 * half - window;
+        // key row of register r is ts + 4*half + 8*(r/4) + r%4: the pair is
+        // allowed when base - (8*(r/4) + r%4) lies in [0, lookahead]
+        const int base = d0 + col - ts - window - 4 * half;
+        if (lookahead < 0) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int diff = base - (8 * (r >> 2) + (r & 3));
-          const bool ok = diff >= 0 && d < S && (lookahead < 0 || diff <= lookahead);
-          const float p = fast_exp2(fmaf(acc[r], c, -L2));
-          macc[r] += ok ? p : 0.f;
+          for (int r = 0; r < 16; ++r) {
+            const float p = fast_exp2(fmaf(acc[r], c, -L2));
+            macc[r] += base >= 8 * (r >> 2) + (r & 3) ? p : 0.f;
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int diff = base - (8 * (r >> 2) + (r & 3));
+            const float p = fast_exp2(fmaf(acc[r], c, -L2));
+            macc[r] += (unsigned)diff <= (unsigned)lookahead ? p : 0.f;
+          }
         }
       }
     }
-    if (PER_HEAD && it - gl * n_qt == n_qt - 1) {
-      flush(gl);
+    if (PER_HEAD && (cq == nq - 1 || it == n_iter - 1)) {
+      flush(cg);
 #pragma unroll
       for (int r = 0; r < 16; ++r) macc[r] = 0.f;
+    }
+    if (++cq == nq) {
+      cq = 0;
+      ++cg;
     }
   };
 
@@ -266,45 +344,71 @@ __global__ __launch_bounds__(64 * WAVES, 16 / WAVES) void future_target_kernel(
     if (kStages > 3 && it + 3 < n_iter) step(I3{}, it + 3);
   }
   if (!PER_HEAD) flush(0);
+
+  x += n_iter;
+  if (x >= x_end) break;
+  off = 0;
+  do {  // next non-empty run
+    if (++kb == geo.n_kb) {
+      kb = 0;
+      if (++ch == geo.n_chunks) {
+        ch = 0;
+        ++bh;
+      }
+    }
+  } while (n_qtiles(geo, ch, kb) == 0);
+  }
 }
 
-// Sum each key's chunk partials in chunk order, aggregate the group and
-// apply count normalisation; writes every key (zeros where no query counts).
+// Sum each key's pieces over chunks and workgroups in a fixed order,
+// aggregate the group and apply count normalisation; writes every key
+// (zeros where no query counts).
 __global__ __launch_bounds__(256) void target_merge_kernel(
-    const float* __restrict__ partial, float* __restrict__ mass, float* __restrict__ mass_ph,
-    int B, int Hq, int Hkv, int S, int window, int lookahead, int key_block, int chunk,
-    int n_chunks, int agg, int count_normalize, int per_head) {
+    const float* __restrict__ partial, const long long* __restrict__ run_start,
+    float* __restrict__ mass, float* __restrict__ mass_ph, int B, int Hq, int Hkv, int S,
+    int window, int lookahead, TargetGeom geo, int agg, int count_normalize, int per_head) {
   const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (long)B * Hkv * S) return;
   const int t = (int)(idx % S);
   const int bh = (int)(idx / S);
   const int b = bh / Hkv, h = bh % Hkv;
   const int G = Hq / Hkv;
+  const int KB = geo.key_block;
   long nt = (long)S - t - window;
   if (nt < 0) nt = 0;
   if (lookahead >= 0 && nt > (long)lookahead + 1) nt = (long)lookahead + 1;
-  const int t0 = (t / key_block) * key_block;
-  const bool any = t0 + window < S;
-  int c_first = 0, c_last = -1;
-  if (any) {
-    c_first = (t0 + window) / chunk;
-    c_last = n_chunks - 1;
-    if (lookahead >= 0) c_last = min(c_last, (t0 + key_block - 1 + window + lookahead) / chunk);
-  }
+  const int kb = t / KB;
+  const int kk = t - kb * KB;
+  // sum of the pieces of run r, whose squares are [lo, lo + n) in the list
+  auto run_sum = [&](long long r, long long lo, long long n) {
+    if (geo.item_mode) return partial[r * KB + kk];  // one piece per run
+    float v = 0.f;
+    for (long long w = lo / geo.share; w <= (lo + n - 1) / geo.share; ++w)
+      v += partial[(r + w) * KB + kk];
+    return v;
+  };
   float sum = 0.f, mx = 0.f;
   if (per_head) {
     for (int gl = 0; gl < G; ++gl) {
       float v = 0.f;
-      const float* pp = partial + ((size_t)bh * G + gl) * n_chunks * (size_t)S + t;
-      for (int cc = c_first; cc <= c_last; ++cc) v += pp[(size_t)cc * S];
+      for (int ch = 0; ch < geo.n_chunks; ++ch) {
+        const int nq = n_qtiles(geo, ch, kb);
+        if (nq == 0) continue;
+        const long long run = ((long long)bh * geo.n_chunks + ch) * geo.n_kb + kb;
+        v += run_sum(run * G + gl, geo.item_mode ? 0 : run_start[run] + (long long)gl * nq, nq);
+      }
       if (mass_ph)
         mass_ph[((size_t)b * Hq + h * G + gl) * S + t] = count_normalize ? (nt > 0 ? v / (float)nt : 0.f) : v;
       sum += v;
       mx = gl == 0 ? v : fmaxf(mx, v);
     }
   } else {
-    const float* pp = partial + (size_t)bh * n_chunks * (size_t)S + t;
-    for (int cc = c_first; cc <= c_last; ++cc) sum += pp[(size_t)cc * S];
+    for (int ch = 0; ch < geo.n_chunks; ++ch) {
+      const int nq = n_qtiles(geo, ch, kb);
+      if (nq == 0) continue;
+      const long long run = ((long long)bh * geo.n_chunks + ch) * geo.n_kb + kb;
+      sum += run_sum(run, geo.item_mode ? 0 : run_start[run], (long long)G * nq);
+    }
   }
   float out = agg == 0 ? sum : agg == 1 ? sum / (float)G : mx;
   if (count_normalize) out = nt > 0 ? out / (float)nt : 0.f;
@@ -313,28 +417,118 @@ __global__ __launch_bounds__(256) void target_merge_kernel(
 
 }  // namespace
 
+int device_cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+static TargetGeom make_geometry(const AttnShape& s, const TargetPlan& p, int window, int lookahead,
+                                int slots) {
+  TargetGeom g;
+  g.G = s.Hq / s.Hkv;
+  g.S = s.S;
+  g.window = window;
+  g.key_block = p.key_block;
+  g.kbt = p.key_block / 32;
+  g.n_kb = p.n_kb;
+  g.n_chunks = p.n_chunks;
+  g.ct = p.chunk / 32;
+  g.w_t = (window & ~31) / 32;
+  g.s_t = (s.S + 31) / 32;
+  g.la_t = lookahead < 0 ? (1 << 30)
+                         : (int)(((long long)p.key_block + window + lookahead + 31) / 32);
+  g.cpre[0] = 0;
+  for (int ch = 0; ch < g.n_chunks; ++ch) {
+    long long n = 0;
+    for (int kb = 0; kb < g.n_kb; ++kb) n += n_qtiles(g, ch, kb);
+    g.cpre[ch + 1] = g.cpre[ch] + n * g.G;
+  }
+  for (int ch = g.n_chunks + 1; ch <= kTgtMaxChunks; ++ch) g.cpre[ch] = g.cpre[g.n_chunks];
+  g.per_bh = g.cpre[g.n_chunks];
+  g.total = g.per_bh * s.B * s.Hkv;
+  // whole rounds of `slots` workgroups, each share at most the cap
+  const long long cap = (long long)slots * KVPOP_TGT_SHARE_CAP;
+  const long long rounds = std::max(1LL, (g.total + cap - 1) / cap);
+  g.rounds = (int)rounds;
+  long long share = (g.total + (long long)slots * rounds - 1) / ((long long)slots * rounds);
+  if (share < KVPOP_TGT_MIN_SHARE) share = KVPOP_TGT_MIN_SHARE;
+  g.share = share;
+  g.n_wg = (int)((g.total + share - 1) / share);
+  // item mode: enough non-empty runs for many rounds of workgroups
+  long long runs_ne = 0;
+  for (int ch = 0; ch < g.n_chunks; ++ch)
+    for (int kb = 0; kb < g.n_kb; ++kb) runs_ne += n_qtiles(g, ch, kb) > 0;
+  runs_ne *= (long long)s.B * s.Hkv;
+  g.item_mode = runs_ne >= (long long)KVPOP_TGT_ITEM_ROUNDS * slots ? 1 : 0;
+  // (rounds stays the even split's: it bounds the workspace of any launch)
+  if (g.item_mode) g.n_wg = s.B * s.Hkv * g.n_chunks * g.n_kb;
+  return g;
+}
+
+// Resident workgroups of the transposed pass on the whole device (all its
+// variants for this head dim and wave count; the fewest, so a round of
+// shares never exceeds what runs at once).
+static int target_slots(int D, int waves) {
+  static std::atomic<int> cached[64][2][2];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  std::atomic<int>& slot = cached[dev][D == 128][waves == 8];
+  int n = slot.load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  int per_cu = 16 / waves;  // fallback: four waves per SIMD
+  auto occ = [&](const void* fn) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, 64 * waves, 0) == hipSuccess && nb > 0)
+      per_cu = std::min(per_cu == 16 / waves ? nb : per_cu, nb);
+  };
+  if (D == 128 && waves == 8) {
+    occ((const void*)future_target_kernel<128, false, 8>);
+    occ((const void*)future_target_kernel<128, true, 8>);
+  } else if (D == 128) {
+    occ((const void*)future_target_kernel<128, false, 4>);
+    occ((const void*)future_target_kernel<128, true, 4>);
+  } else {
+    occ((const void*)future_target_kernel<64, false, 4>);
+    occ((const void*)future_target_kernel<64, true, 4>);
+  }
+  n = device_cu_count() * per_cu;
+  slot.store(n, std::memory_order_relaxed);
+  return n;
+}
+
 TargetPlan plan_target(const AttnShape& s, int window) {
   TargetPlan p;
-  p.waves = (long)s.B * s.Hkv * s.S <= KVPOP_TGT_SMALL_KEYS ? 4 : 8;
+  // a 32-query tile of D = 64 is four 1 KB loads: one per wave of four
+  p.waves = s.D == 64 || (long)s.B * s.Hkv * s.S <= KVPOP_TGT_SMALL_KEYS ? 4 : 8;
   p.key_block = 32 * p.waves;
   p.n_kb = (s.S + p.key_block - 1) / p.key_block;
-  auto count_items = [&](int C) {
-    const int nc = (s.S + C - 1) / C;
-    long items = 0;
-    for (int kb = 0; kb < p.n_kb; ++kb) {
-      const long lo = (long)kb * p.key_block + window;
-      if (lo >= s.S) continue;
-      items += nc - lo / C;
-    }
-    return items * s.B * s.Hkv;
-  };
-  int C = KVPOP_TGT_MAX_CHUNK;
-  while (C > KVPOP_TGT_MIN_CHUNK && count_items(C) < KVPOP_TGT_MIN_ITEMS) C >>= 1;
-  p.chunk = C;
-  p.n_chunks = (s.S + C - 1) / C;
   const int G = s.Hq / s.Hkv;
-  p.partial_floats = (size_t)s.B * s.Hkv * G * p.n_chunks * (size_t)s.S;
+  long long C = (long long)KVPOP_TGT_CHUNK_BYTES / ((long long)G * s.D * 2);
+  C = std::max(256LL, C & ~31LL);
+  const long long min_c = (((long long)s.S + kTgtMaxChunks - 1) / kTgtMaxChunks + 31) & ~31LL;
+  C = std::max(C, min_c);
+  p.chunk = (int)C;
+  p.n_chunks = (int)((s.S + C - 1) / C);
+  // the most workgroups any lookahead needs: a launch has at most rounds x
+  // slots, and no lookahead gives the most squares and rounds
+  const int slots = target_slots(s.D, p.waves);
+  p.max_wg = make_geometry(s, p, window, -1, slots).rounds * slots;
+  p.runs = (size_t)s.B * s.Hkv * p.n_chunks * p.n_kb;
+  p.partial_floats = (p.runs * G + (size_t)p.max_wg) * p.key_block;
+  const size_t part_bytes = (p.partial_floats * sizeof(float) + 255) & ~(size_t)255;
+  p.workspace_bytes = part_bytes + p.runs * sizeof(long long);
   return p;
+}
+
+TargetGeom target_geometry(const AttnShape& s, const TargetPlan& p, int window, int lookahead) {
+  return make_geometry(s, p, window, lookahead, target_slots(s.D, p.waves));
 }
 
 hipError_t launch_future_target(const AttnShape& s, const void* q, const void* k,
@@ -342,32 +536,35 @@ hipError_t launch_future_target(const AttnShape& s, const void* q, const void* k
                                 int count_normalize, float* mass, float* mass_per_qhead,
                                 float* workspace, hipStream_t st) {
   const TargetPlan p = plan_target(s, window);
+  const TargetGeom geo = target_geometry(s, p, window, lookahead);
+  long long* run_start = reinterpret_cast<long long*>(
+      reinterpret_cast<char*>(workspace) + ((p.partial_floats * sizeof(float) + 255) & ~(size_t)255));
   const bool per_head = agg == 2 || mass_per_qhead != nullptr;
-  const int n_items = s.B * s.Hkv * p.n_chunks * p.n_kb;
   const float c = s.scale * kLog2e;
-  dim3 grid(n_items), block(64 * p.waves);
   auto* qq = (const bf16_t*)q;
   auto* kk = (const bf16_t*)k;
+  if (geo.n_wg > 0) {
+    dim3 grid(geo.n_wg), block(64 * p.waves);
 #define KVPOP_TARGET_LAUNCH(DD, PH, WW)                                                            \
   hipLaunchKernelGGL((future_target_kernel<DD, PH, WW>), grid, block, 0, st, qq, kk, lse,          \
-                     workspace, s.Hq, s.Hkv, s.S, window, lookahead, c, p.chunk, p.n_chunks,     \
-                     p.n_kb, n_items)
+                     workspace, run_start, s.Hq, s.Hkv, s.S, window, lookahead, c, geo)
 #define KVPOP_TARGET_WAVES(DD, PH)                  \
   if (p.waves == 4) KVPOP_TARGET_LAUNCH(DD, PH, 4); \
   else KVPOP_TARGET_LAUNCH(DD, PH, 8)
-  if (s.D == 128) {
-    if (per_head) { KVPOP_TARGET_WAVES(128, true); } else { KVPOP_TARGET_WAVES(128, false); }
-  } else {
-    if (per_head) { KVPOP_TARGET_WAVES(64, true); } else { KVPOP_TARGET_WAVES(64, false); }
-  }
+    if (s.D == 128) {
+      if (per_head) { KVPOP_TARGET_WAVES(128, true); } else { KVPOP_TARGET_WAVES(128, false); }
+    } else {
+      if (per_head) { KVPOP_TARGET_LAUNCH(64, true, 4); } else { KVPOP_TARGET_LAUNCH(64, false, 4); }
+    }
 #undef KVPOP_TARGET_WAVES
 #undef KVPOP_TARGET_LAUNCH
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const long n = (long)s.B * s.Hkv * s.S;
   hipLaunchKernelGGL(target_merge_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                     workspace, mass, mass_per_qhead, s.B, s.Hq, s.Hkv, s.S, window, lookahead,
-                     p.key_block, p.chunk, p.n_chunks, agg, count_normalize, per_head ? 1 : 0);
+                     workspace, run_start, mass, mass_per_qhead, s.B, s.Hq, s.Hkv, s.S, window,
+                     lookahead, geo, agg, count_normalize, per_head ? 1 : 0);
   return hipGetLastError();
 }
 

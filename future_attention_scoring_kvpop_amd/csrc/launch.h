@@ -27,15 +27,47 @@ hipError_t launch_fwd_lse(const AttnShape& s, const void* q, const void* k, floa
                           float* workspace, hipStream_t st);
 
 // ---- transposed future-attention pass ----
+constexpr int kTgtMaxChunks = 64;
+
 struct TargetPlan {
   int waves;      // waves per workgroup: 4 (128-key blocks) or 8 (256-key blocks)
-  int key_block;  // keys per work item (32 per wave)
-  int chunk;      // query positions per work item (multiple of 32)
-  int n_chunks;   // ceil(S / chunk)
-  int n_kb;       // key blocks
-  size_t partial_floats;  // workspace floats (per-query-head partials)
+  int key_block;  // keys per key block (32 per wave)
+  int n_kb;       // key blocks per (b, KV head)
+  int chunk;      // query positions per chunk (multiple of 32)
+  int n_chunks;   // ceil(S / chunk) <= kTgtMaxChunks
+  int max_wg;     // workgroups at most (any lookahead)
+  size_t runs;            // (b, KV head, chunk, key block) runs, empty ones included
+  size_t partial_floats;  // pieces x key_block
+  size_t workspace_bytes; // partials + run table
 };
+
+// The transposed pass's list of 32-query squares, in the order (b, KV head),
+// query chunk c, key block kb, query head of the group, query tile.  Run
+// (c, kb) holds G * n_qtiles(c, kb) squares: the query tiles of chunk c from
+// the first at or after kb's first allowed query up to the chunk end or the
+// lookahead bound.  cpre[c] = squares of the chunks before c of one (b, h).
+struct TargetGeom {
+  int G, S, window, key_block, kbt, n_kb, n_chunks, ct, w_t, s_t, la_t, n_wg, rounds;
+  int item_mode;     // 1: one workgroup per run (n_wg = all runs, empty ones exit)
+  long long per_bh;  // squares per (b, KV head)
+  long long total;   // squares in the launch
+  long long share;   // squares per workgroup
+  long long cpre[kTgtMaxChunks + 1];
+};
+
+__host__ __device__ inline int n_qtiles(const TargetGeom& g, int c, int kb) {
+  if (kb * g.key_block + g.window >= g.S) return 0;  // no key of the block has a query
+  const int u = kb * g.kbt;
+  const int lo = c * g.ct;
+  const int hi = (c + 1) * g.ct < g.s_t ? (c + 1) * g.ct : g.s_t;
+  const int right = hi < u + g.la_t ? hi : u + g.la_t;
+  const int left = lo > u + g.w_t ? lo : u + g.w_t;
+  return right > left ? right - left : 0;
+}
+
 TargetPlan plan_target(const AttnShape& s, int window);
+TargetGeom target_geometry(const AttnShape& s, const TargetPlan& p, int window, int lookahead);
+int device_cu_count();
 hipError_t launch_future_target(const AttnShape& s, const void* q, const void* k,
                                 const float* lse, int window, int lookahead, int agg,
                                 int count_normalize, float* mass, float* mass_per_qhead,

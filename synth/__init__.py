@@ -154,6 +154,16 @@ def scores(shape, seed, device="cpu", kind="normal"):
     raise ValueError(kind)
 
 
+def normalizers(B, Hq, S, seed, device="cpu"):
+    """A seeded stand-in for per-query log-normalizers [B,Hq,S] (fp32):
+    ln(d + 1) + 1.5 + N(0, 0.25^2), the size a causal row of small logits has.
+    Lets the transposed pass be checked at full size on an input both sides
+    are handed, without the dense pass."""
+    d = torch.arange(S, dtype=torch.float32, device=device)
+    base = torch.log1p(d) + 1.5
+    return (base + normal((B, Hq, S), seed, device, std=0.25)).contiguous()
+
+
 def mlp_weights(Hkv, D, hidden, seed, device="cpu"):
     """Random-init headwise scorer: W1 ~ N(0, 1/D), w2 ~ N(0, 1/hidden), zero biases."""
     w1 = normal((Hkv, hidden, D), seed * 5 + 1, device, D ** -0.5)

@@ -91,8 +91,8 @@ def test_ragged_and_degenerate_shapes(kv, B, Hq, Hkv, S, D, window):
 
 @pytest.mark.parametrize("agg,lookahead,count_normalize", [("sum", -1, False), ("max", 300, True)])
 def test_many_keys_launch_full_parity(kv, agg, lookahead, count_normalize):
-    """B*Hkv*S = 67584 keys: above the size where the transposed pass switches
-    from 128-key to 256-key work items; every key compared with the oracle."""
+    """B*Hkv*S = 67584 keys over 33 (b, KV head) pairs and three query
+    chunks; every key compared with the oracle."""
     B, Hq, Hkv, S, D, window = 11, 6, 3, 2048, 64, 100
     q = synth.bf16(synth.normal((B, Hq, S, D), 21)).cuda()
     k = synth.bf16(synth.normal((B, Hkv, S, D), 22)).cuda()
@@ -158,6 +158,32 @@ def test_qwen8b_prefill_layer(kv):
     assert_close(f32(m[0, 3, t_lo:t_hi]), om, MASS_ATOL, MASS_RTOL, "mass tail")
     _sampled_lse_rows(q, k, lse, n=24, seed=3)
     _zero_window_invariant(kv, q, k)
+
+
+@pytest.mark.parametrize("wl,per_qhead", [("skewed", False), ("qwen8b", False), ("qwen8b", True)])
+def test_full_size_transposed_pass_sampled_keys(kv, wl, per_qhead):
+    """The transposed pass alone at full size, on one seeded normalizer array
+    handed to both sides: keys at the start (summed over every query chunk),
+    across a key-block boundary, mid-sequence and at the tail, for the first
+    and the last (b, KV head)."""
+    w = synth.SKEWED if wl == "skewed" else synth.QWEN8B
+    q, k, _ = synth.attention_inputs(w, seed=31, device="cuda")
+    lse = synth.normalizers(w.B, w.Hq, w.S, seed=32).cuda()
+    out = kv.future_attn_target(q, k, lse, w.window, per_qhead=per_qhead)
+    m, ph = out if per_qhead else (out, None)
+    torch.cuda.synchronize()
+    G = w.Hq // w.Hkv
+    keys = np.concatenate([np.arange(0, 24), np.arange(1010, 1040), np.arange(w.S // 2 - 12, w.S // 2 + 12),
+                           np.arange(w.S - w.window - 24, w.S)]).astype(np.int64)
+    lse_h = lse.cpu().numpy()
+    for b, h in ((0, 0), (w.B - 1, w.Hkv - 1)):
+        qs, ks = group_problem(q, k, b, h)
+        om, oph = oracle.future_mass(qs, ks, lse_h[b:b + 1, h * G:(h + 1) * G], w.window, cols=keys,
+                                     per_head=True)
+        assert_close(f32(m[b, h])[keys], om, MASS_ATOL, MASS_RTOL, f"mass ({b},{h})")
+        if per_qhead:
+            assert_close(f32(ph[b, h * G:(h + 1) * G])[:, keys].T, oph, MASS_ATOL, MASS_RTOL,
+                         f"per-head ({b},{h})")
 
 
 def _sampled_lse_rows(q, k, lse, n, seed):
