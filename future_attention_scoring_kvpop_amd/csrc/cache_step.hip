@@ -94,6 +94,11 @@ __global__ __launch_bounds__(kThreads) void score_mlp_kernel(
   }
 }
 
+// Pool slots each thread scans per pass (loaded together, then reduced).
+constexpr int kScanPer = 16;
+// W1 elements per thread held in registers while staging (hidden * D <= 64 * 128).
+constexpr int kW1Per = 64 * 128 / kThreads;
+
 __global__ __launch_bounds__(kThreads) void cache_step_kernel(
     int D, int n_sink, int window, int budget, int delay, int pos_q,
     const bf16_t* __restrict__ k_new, const bf16_t* __restrict__ v_new,
@@ -103,7 +108,9 @@ __global__ __launch_bounds__(kThreads) void cache_step_kernel(
     float* __restrict__ slot_score, int Hkv) {
   extern __shared__ float smem[];
   __shared__ int red_empty[kThreads / 64];
-  __shared__ int red_worst[kThreads / 64];
+  __shared__ int red_slot[kThreads / 64];
+  __shared__ uint32_t red_key[kThreads / 64];
+  __shared__ int red_pos[kThreads / 64];
   __shared__ int sh_dst;
 
   const long row = blockIdx.x;  // b * Hkv + h
@@ -116,32 +123,82 @@ __global__ __launch_bounds__(kThreads) void cache_step_kernel(
   bf16_t* vr = vc + row * (size_t)budget * D;
   const int cpr = D / 8;
   const int q = pos_q;
+  const int u = q - window;               // the token leaving the window
+  const bool exiting = u >= n_sink;
+  const int ring_u = n_sink + kk + ((u % window) + window) % window;
+  const int slot = q < n_sink ? q : n_sink + kk + (q % window);  // where q is written
+  const int r = q - delay;                // the token scored at this step
+  const bool scoring = r >= n_sink;
+  const int rslot = n_sink + kk + ((r % window) + window) % window;
+  const bool use_mlp = scoring && w1 != nullptr;
 
-  // ---- (a) the token leaving the window ----
-  const int u = q - window;
-  if (u >= n_sink) {
-    const int ring_u = n_sink + kk + (u % window);
-    int first_empty = 0x7fffffff, worst = -1;
-    uint32_t wkey = 0;
-    int wpos = 0;
-    for (int j = n_sink + tid; j < n_sink + kk; j += kThreads) {
-      const int p = sp[j];
-      if (p < 0) {
-        first_empty = min(first_empty, j);
-      } else {
-        const uint32_t key = rank_key(ss[j]);
-        if (worst < 0 || key < wkey || (key == wkey && p > wpos)) {
-          worst = j;
-          wkey = key;
-          wpos = p;
+  // ---- every global read first: one memory latency for the whole step ----
+  // rows: thread i < cpr owns 16-byte chunk i of K, cpr <= i < 2 cpr of V;
+  // the exiting row is read before the same thread overwrites its slot
+  const bool row_thread = tid < 2 * cpr;
+  const bool is_k = tid < cpr;
+  const int chunk = is_k ? tid : tid - cpr;
+  uint4 old_row = make_uint4(0, 0, 0, 0), new_row = make_uint4(0, 0, 0, 0);
+  if (row_thread) {
+    if (exiting) old_row = ldg16((is_k ? kr : vr) + (size_t)ring_u * D + chunk * 8);
+    new_row = ldg16((is_k ? k_new : v_new) + row * D + chunk * 8);
+  }
+  int pos_u = 0;
+  float score_u = 0.f, given = 0.f;
+  if (tid == 0) {
+    if (exiting) {
+      pos_u = sp[ring_u];
+      score_u = ss[ring_u];
+    }
+    if (scoring && !use_mlp) given = scores_r[row];
+  }
+  float w1v[kW1Per];
+  float keyv = 0.f;
+  if (use_mlp) {
+    const float* w1h = w1 + (size_t)h * hidden * D;
+#pragma unroll
+    for (int i = 0; i < kW1Per; ++i) {
+      const int e = tid + i * kThreads;
+      w1v[i] = e < hidden * D ? w1h[e] : 0.f;
+    }
+    const bf16_t* ksrc = r == q ? k_new + row * D : kr + (size_t)rslot * D;
+    if (tid < D) keyv = __uint_as_float((uint32_t)ksrc[tid] << 16);
+  }
+
+  // ---- (a) scan of the long-range slots: first empty slot, worst kept token
+  int first_empty = 0x7fffffff, worst = -1, wpos = 0;
+  uint32_t wkey = 0;
+  if (exiting) {
+    for (int base = 0; base < kk; base += kThreads * kScanPer) {
+      int pv[kScanPer];
+      float sv[kScanPer];
+#pragma unroll
+      for (int i = 0; i < kScanPer; ++i) {
+        const int j = base + tid + i * kThreads;
+        pv[i] = j < kk ? sp[n_sink + j] : -2;
+        sv[i] = j < kk ? ss[n_sink + j] : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < kScanPer; ++i) {
+        const int j = n_sink + base + tid + i * kThreads;
+        if (pv[i] == -2) continue;
+        if (pv[i] < 0) {
+          first_empty = min(first_empty, j);
+        } else {
+          const uint32_t key = rank_key(sv[i]);
+          if (worst < 0 || key < wkey || (key == wkey && pv[i] > wpos)) {
+            worst = j;
+            wkey = key;
+            wpos = pv[i];
+          }
         }
       }
     }
-    // wave reduction, then across waves
+    // worst = lowest rank key, ties to the later position (positions of kept
+    // tokens are distinct, so the order is total)
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
-      const int fe = __shfl_xor(first_empty, off);
-      first_empty = min(first_empty, fe);
+      first_empty = min(first_empty, __shfl_xor(first_empty, off));
       const int ow = __shfl_xor(worst, off);
       const uint32_t ok = (uint32_t)__shfl_xor((int)wkey, off);
       const int op = __shfl_xor(wpos, off);
@@ -153,76 +210,68 @@ __global__ __launch_bounds__(kThreads) void cache_step_kernel(
     }
     if (lane == 0) {
       red_empty[wave] = first_empty;
-      red_worst[wave] = worst;
+      red_slot[wave] = worst;
+      red_key[wave] = wkey;
+      red_pos[wave] = wpos;
     }
-    __syncthreads();
-    if (tid == 0) {
-      int fe = 0x7fffffff, wv = -1;
+  }
+  float* w1s = smem;                         // hidden x (D+1)
+  float* key = smem + (size_t)hidden * (D + 1);
+  if (use_mlp) {
+#pragma unroll
+    for (int i = 0; i < kW1Per; ++i) {
+      const int e = tid + i * kThreads;
+      if (e < hidden * D) w1s[(e / D) * (D + 1) + e % D] = w1v[i];
+    }
+    if (tid < D) key[tid] = keyv;
+  }
+  __syncthreads();
+
+  // ---- decision (one thread): empty slot first, else strict evict-min ----
+  if (tid == 0) {
+    int dst = -1;
+    if (exiting) {
+      int fe = 0x7fffffff, wv = -1, wp = 0;
       uint32_t wk = 0;
-      int wp = 0;
       for (int w = 0; w < kThreads / 64; ++w) {
         fe = min(fe, red_empty[w]);
-        const int cand = red_worst[w];
-        if (cand >= 0) {
-          const uint32_t ck = rank_key(ss[cand]);
-          const int cp = sp[cand];
-          if (wv < 0 || ck < wk || (ck == wk && cp > wp)) {
-            wv = cand;
-            wk = ck;
-            wp = cp;
-          }
+        const int cand = red_slot[w];
+        if (cand >= 0 && (wv < 0 || red_key[w] < wk || (red_key[w] == wk && red_pos[w] > wp))) {
+          wv = cand;
+          wk = red_key[w];
+          wp = red_pos[w];
         }
       }
-      int dst = -1;
       if (fe != 0x7fffffff) {
         dst = fe;
       } else if (wv >= 0) {
-        const uint32_t uk = rank_key(ss[ring_u]);
+        const uint32_t uk = rank_key(score_u);
         if (uk > wk || (uk == wk && u < wp)) dst = wv;
       }
       if (dst >= 0) {
-        sp[dst] = sp[ring_u];
-        ss[dst] = ss[ring_u];
+        sp[dst] = pos_u;
+        ss[dst] = score_u;
       }
-      sh_dst = dst;
     }
-    __syncthreads();
-    const int dst = sh_dst;
-    if (dst >= 0) {
-      if (tid < cpr) stg16(kr + (size_t)dst * D + tid * 8, ldg16(kr + (size_t)ring_u * D + tid * 8));
-      else if (tid < 2 * cpr)
-        stg16(vr + (size_t)dst * D + (tid - cpr) * 8, ldg16(vr + (size_t)ring_u * D + (tid - cpr) * 8));
-    }
-  }
-
-  // ---- (b) append the new token ----
-  const int slot = q < n_sink ? q : n_sink + kk + (q % window);
-  if (tid < cpr) stg16(kr + (size_t)slot * D + tid * 8, ldg16(k_new + row * D + tid * 8));
-  else if (tid < 2 * cpr)
-    stg16(vr + (size_t)slot * D + (tid - cpr) * 8, ldg16(v_new + row * D + (tid - cpr) * 8));
-  if (tid == 0) {
+    sh_dst = dst;
+    // (b) the new token takes its ring slot, unscored for now
     sp[slot] = q;
     ss[slot] = __uint_as_float(0x7fc00000u);
   }
+  __syncthreads();
+  const int dst = sh_dst;
+  if (row_thread) {
+    bf16_t* base = is_k ? kr : vr;
+    if (dst >= 0) stg16(base + (size_t)dst * D + chunk * 8, old_row);
+    stg16(base + (size_t)slot * D + chunk * 8, new_row);
+  }
 
   // ---- (c) delayed scoring of token r = q - delay ----
-  const int r = q - delay;
-  if (r >= n_sink) {
-    const int rslot = n_sink + kk + (r % window);
-    float sc;
-    if (w1 == nullptr) {
-      sc = scores_r[row];
-    } else {
-      float* w1s = smem;
-      float* key = smem + hidden * (D + 1);
-      stage_w1(w1s, w1 + (size_t)h * hidden * D, D, hidden);
-      const bf16_t* ksrc = r == q ? k_new + row * D : kr + (size_t)rslot * D;
-      for (int cc = tid; cc < D; cc += kThreads) key[cc] = __uint_as_float((uint32_t)ksrc[cc] << 16);
-      __syncthreads();
-      sc = 0.f;
-      if (wave == 0) sc = mlp_wave(key, w1s, D, hidden, b1 + (size_t)h * hidden, w2 + (size_t)h * hidden, b2[h], lane);
-    }
-    if (tid == 0) ss[rslot] = sc;
+  if (scoring && wave == 0) {
+    float sc = given;
+    if (use_mlp)
+      sc = mlp_wave(key, w1s, D, hidden, b1 + (size_t)h * hidden, w2 + (size_t)h * hidden, b2[h], lane);
+    if (lane == 0) ss[rslot] = sc;  // after the NaN marker when r == q (same thread)
   }
 }
 

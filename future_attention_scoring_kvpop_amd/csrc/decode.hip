@@ -15,6 +15,8 @@
 //     an online (max, sum, o) state per head over blocks of 4 slots, and the
 //     16 states of a workgroup are merged once through LDS.  Splits are
 //     merged by a second small kernel with the same log-sum-exp rule.
+#include <atomic>
+
 #include "common.h"
 #include "launch.h"
 
@@ -22,6 +24,10 @@ namespace kvpop {
 namespace {
 
 constexpr int kThreads = 256;
+// 1: the next iteration's K/V rows are loaded before this one is computed
+#ifndef KVPOP_DEC_PREFETCH
+#define KVPOP_DEC_PREFETCH 1
+#endif
 constexpr int kNB = 4;                    // slots per quarter-wave per iteration
 constexpr int kSlotsPerIter = 16 * kNB;   // per workgroup
 
@@ -94,18 +100,32 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
       for (int f = 0; f < FPL; ++f) o[g][f] = 0.f;
     }
 
-    for (int jb = j_begin; jb < j_end; jb += kSlotsPerIter) {
-      uint4 kr[kNB], vr[kNB];
-      bool ok[kNB];
+    // rows of iteration jb (prefetched one iteration ahead when enabled)
+    uint4 kn[kNB], vn[kNB];
+    int pn[kNB];
+    auto fetch = [&](int jb) {
 #pragma unroll
       for (int i = 0; i < kNB; ++i) {
         const int j = jb + qw * kNB + i;
         const bool in = j < j_end;
         const size_t off = (row0 + (in ? j : j_begin)) * D + ql * FPL;
-        kr[i] = load_row_part<FPL>(kc + off);
-        vr[i] = load_row_part<FPL>(vc + off);
-        ok[i] = in && slot_pos[row0 + (in ? j : j_begin)] >= 0;
+        kn[i] = load_row_part<FPL>(kc + off);
+        vn[i] = load_row_part<FPL>(vc + off);
+        pn[i] = in ? slot_pos[row0 + j] : -1;
       }
+    };
+    if (KVPOP_DEC_PREFETCH) fetch(j_begin);
+    for (int jb = j_begin; jb < j_end; jb += kSlotsPerIter) {
+      uint4 kr[kNB], vr[kNB];
+      bool ok[kNB];
+      if (!KVPOP_DEC_PREFETCH) fetch(jb);
+#pragma unroll
+      for (int i = 0; i < kNB; ++i) {
+        kr[i] = kn[i];
+        vr[i] = vn[i];
+        ok[i] = pn[i] >= 0;
+      }
+      if (KVPOP_DEC_PREFETCH && jb + kSlotsPerIter < j_end) fetch(jb + kSlotsPerIter);
       float kf[kNB][8], vf[kNB][8];
 #pragma unroll
       for (int i = 0; i < kNB; ++i) {
@@ -224,10 +244,42 @@ __global__ void decode_merge_kernel(const float* __restrict__ ws, void* __restri
 
 }  // namespace
 
+// rounds of resident workgroups a decode launch is split into
+#ifndef KVPOP_DEC_ROUNDS
+#define KVPOP_DEC_ROUNDS 1
+#endif
+
+// Resident decode workgroups on the current device for the group size used.
+static int decode_slots(int D, int G) {
+  static std::atomic<int> cached[64][2][4];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  const int gi = G >= 8 ? 3 : G >= 4 ? 2 : G >= 2 ? 1 : 0;
+  std::atomic<int>& slot = cached[dev][D == 128][gi];
+  int n = slot.load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  const void* fn;
+  if (D == 128) {
+    const void* t[4] = {(const void*)decode_kernel<128, 1>, (const void*)decode_kernel<128, 2>,
+                        (const void*)decode_kernel<128, 4>, (const void*)decode_kernel<128, 8>};
+    fn = t[gi];
+  } else {
+    const void* t[4] = {(const void*)decode_kernel<64, 1>, (const void*)decode_kernel<64, 2>,
+                        (const void*)decode_kernel<64, 4>, (const void*)decode_kernel<64, 8>};
+    fn = t[gi];
+  }
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kThreads, 0) != hipSuccess || nb <= 0) nb = 2;
+  n = device_cu_count() * nb;
+  slot.store(n, std::memory_order_relaxed);
+  return n;
+}
+
 DecodePlan plan_decode(const AttnShape& s) {
   DecodePlan p;
   const int units = s.B * s.Hkv;
-  int want = (2048 + units - 1) / units;
+  const int wgs = KVPOP_DEC_ROUNDS * decode_slots(s.D, s.Hq / s.Hkv);
+  int want = (wgs + units - 1) / units;
   const int max_split = (s.S + 255) / 256;
   p.n_split = want < 1 ? 1 : (want > max_split ? max_split : want);
   if (p.n_split < 1) p.n_split = 1;

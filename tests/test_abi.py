@@ -96,7 +96,9 @@ def test_select_validation(lib):
 
 
 def test_decode_validation(lib):
-    d = kv.dims(64, 32, 8, 4096, 128)
+    # 64 x 8 (b, KV head) rows fill the device alone: no split, no workspace
+    assert kv.workspace_bytes(kv.OP_DECODE, kv.dims(64, 32, 8, 4096, 128)) == 0
+    d = kv.dims(1, 32, 8, 4096, 128)  # 8 rows: slots are split, partials need room
     need = kv.workspace_bytes(kv.OP_DECODE, d)
     assert need > 0
 
