@@ -38,8 +38,8 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 # a torch copy of known size (`bench.py --calibrate-copy`).  Valid only for
 # the kernel sources it was taken on: bench reports null once they change.
 TRAFFIC_SOURCES = ("future_target.hip", "common.h", "launch.h")
-TRAFFIC = {"sha256": "57d627d713c32b4f51b3518b47bebc3f765aa4e21b076bfc6e91433553874db3",
-           "fetch_bytes": 2 * (20165.4 + 543.0) * 1024, "write_bytes": (1024.0 + 128.0) * 1024}
+TRAFFIC = {"sha256": "4b9ee089dc5c257278482dd14b74c7de9ab11391ef69a93fe59dbe62a9b30aee",
+           "fetch_bytes": 2 * (24179.7 + 345.0) * 1024, "write_bytes": (578.5 + 128.0) * 1024}
 METRIC = "future-attn target keys/s + MFMA util; bounded-cache decode steps/s + HBM util"
 
 
@@ -69,6 +69,8 @@ class TargetStep:
         d = kv.dims(w.B, w.Hq, w.Hkv, w.S, w.D)
         self.ws = torch.empty(kv.workspace_bytes(kv.OP_FUTURE_TARGET, d, w.window), dtype=torch.uint8,
                               device=dev)
+        self.fws = torch.empty(max(kv.workspace_bytes(kv.OP_FWD_LSE, d), 16), dtype=torch.uint8,
+                               device=dev)
         self.sp = torch.empty((w.B, w.Hkv, w.budget), dtype=torch.int32, device=dev)
         self.ss = torch.empty((w.B, w.Hkv, w.budget), dtype=torch.float32, device=dev)
         self.kc = torch.empty((w.B, w.Hkv, w.budget, w.D), dtype=torch.bfloat16, device=dev)
@@ -86,7 +88,7 @@ class TargetStep:
         kv, w = self.kv, self.w
         if ev:
             ev[0].record()
-        kv.fwd_lse(self.q, self.k, out=self.lse)
+        kv.fwd_lse(self.q, self.k, out=self.lse, workspace=self.fws)
         if ev:
             ev[1].record()
         kv.future_attn_target(self.q, self.k, self.lse, w.window, agg="sum", out=self.mass,
