@@ -108,6 +108,7 @@ class TargetStep:
 def bench_target(kv, steps, warmup):
     w = synth.QWEN4B
     st = TargetStep(kv, w)
+    bench_target.step = st
     for _ in range(warmup):
         st.run()
     torch.cuda.synchronize()
@@ -126,6 +127,46 @@ def bench_target(kv, steps, warmup):
     t_rest = sum(e[2].elapsed_time(e[3]) for e in evs) / steps
     f_fwd, f_tr = target_flops(w)
     return w, ms, t_fwd, t_tr, t_rest, f_fwd, f_tr
+
+
+def target_flops_lookahead(w, lookahead):
+    """Algorithmic flops of the transposed pass with a finite lookahead L:
+    key t counts queries t+w .. min(S-1, t+w+L), so 2*D*sum_j min(L+1, j)
+    over j = 1..S-w, per query head."""
+    n = max(w.S - w.window, 0)
+    m = lookahead + 1
+    pairs = n * (n + 1) // 2 if m >= n else m * (m + 1) // 2 + (n - m) * m
+    return 2.0 * w.D * pairs * w.Hq * w.B
+
+
+def bench_target_variants(kv, st, reps=20):
+    """The pages' other target forms on the same layer inputs: MAX over the
+    group (App. B.1, per-query-head sums kept), and a finite lookahead with
+    count normalisation (App. B.2)."""
+    w = st.w
+    variants = {
+        "max_per_qhead": (dict(agg="max", per_qhead=True), target_flops(w)[1]),
+        "sum_lookahead512_count_normalized": (dict(agg="sum", lookahead=512, count_normalize=True),
+                                              target_flops_lookahead(w, 512)),
+    }
+    out = {}
+    for name, (kw, flops) in variants.items():
+        def call():
+            kv.future_attn_target(st.q, st.k, st.lse, w.window, out=st.mass, workspace=st.ws, **kw)
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            call()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        tf = flops / (ms / 1e3) / 1e12
+        out[name] = {"ms": ms, "flops": flops, "tflops": tf, "frac": tf / MFMA_BF16_PEAK_TFLOPS}
+    return out
 
 
 def decode_bytes_per_step(w, layers):
@@ -390,6 +431,7 @@ def main():
                                            "frac": achieved_tr / MFMA_BF16_PEAK_TFLOPS},
                     "select_gather_decode": {"ms": t_rest}},
     }
+    out["target_variants"] = bench_target_variants(kv, bench_target.step)
     if not a.no_decode:
         log(f"decode: {a.decode_steps} steps x {a.decode_layers} layers")
         out["decode"] = bench_decode(kv, a.decode_steps, a.decode_layers)

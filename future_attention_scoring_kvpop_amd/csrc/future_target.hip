@@ -77,6 +77,11 @@ namespace {
 #define KVPOP_TGT_STAGES 3
 #endif
 // B * Hkv * S at or below which the 4-wave (128-key) workgroups are used
+// 32-query tiles per LDS ring stage: each barrier, DMA issue and wait then
+// covers this many tiles
+#ifndef KVPOP_TGT_TPS
+#define KVPOP_TGT_TPS 2
+#endif
 // waves per SIMD the kernel is compiled for (sets its register budget:
 // 512 / n registers per lane)
 #ifndef KVPOP_TGT_WPE
@@ -113,17 +118,21 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KVPO
   constexpr int CPR = D / 8;                // 16-byte chunks per row
   constexpr int ROWB = D * 2;               // bytes per query row
   constexpr int TILE = kQT * ROWB;          // bytes per query tile
+  constexpr int TPS = KVPOP_TGT_TPS;        // tiles per stage
+  static_assert(TPS == 1 || TPS == 2, "tiles per stage");
   constexpr int NQI = TILE / 1024;          // 1 KB DMA instructions per query tile
-  static_assert(NQI % WAVES == 0, "every wave loads the same share of a tile");
-  constexpr int QPW = NQI / WAVES;          // query-row DMAs per wave per tile
-  constexpr int PT = QPW + 1;               // DMA instructions per wave per tile (+ normalizers)
+  static_assert((TPS * NQI) % WAVES == 0, "every wave loads the same share of a stage");
+  constexpr int QPW = TPS * NQI / WAVES;    // query-row DMAs per wave per stage
+  constexpr int PT = QPW + 1;               // DMA instructions per wave per stage (+ normalizers)
   constexpr int ROWS_PER_LOAD = 1024 / ROWB;
   // One LDS object per ring stage: every access below names its stage at
   // compile time, so a DMA into one stage is never mistaken for a write to
-  // the stage being read.  Each wave keeps its own copy of a tile's
-  // normalizers (64 floats: lanes 32-63 duplicate lanes 0-31).
-  __shared__ __attribute__((aligned(1024))) uint8_t qs0[TILE], qs1[TILE], qs2[kStages > 2 ? TILE : 16],
-      qs3[kStages > 3 ? TILE : 16];
+  // the stage being read.  Each wave keeps its own copy of a stage's
+  // normalizers (64 floats: tile tt in lanes 32 tt .. 32 tt + 31; with one
+  // tile per stage lanes 32-63 duplicate lanes 0-31).
+  constexpr int STAGE = TPS * TILE;
+  __shared__ __attribute__((aligned(1024))) uint8_t qs0[STAGE], qs1[STAGE],
+      qs2[kStages > 2 ? STAGE : 16], qs3[kStages > 3 ? STAGE : 16];
   __shared__ __attribute__((aligned(256))) float ls0[64 * WAVES], ls1[64 * WAVES],
       ls2[kStages > 2 ? 64 * WAVES : 1], ls3[kStages > 3 ? 64 * WAVES : 1];
   auto qst = [&](auto J) -> uint8_t* {
@@ -206,25 +215,41 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KVPO
   int iq = off - ig * nq;
   int cg = ig, cq = iq;
 
-  // DMA of tile (ig, iq) into stage J, then advance to the next tile.
+  // DMA of the stage's tiles (ig, iq) and the next one into stage J, then
+  // advance past them.  Query-row DMA I fetches tile I / NQI; past the last
+  // tile of the segment the final tile is fetched again (never computed).
   auto issue = [&](auto J) {
-    const size_t head = head0 + ig;
-    const int d0 = dt0 + iq * kQT;
-    const bf16_t* qb = q + head * S * D;
+    int tg[2], tq[2];
+    tg[0] = ig;
+    tq[0] = iq;
+    tg[1] = iq + 1 == nq ? ig + 1 : ig;
+    tq[1] = iq + 1 == nq ? 0 : iq + 1;
+    if (TPS == 2 && tg[1] >= G) {
+      tg[1] = tg[0];
+      tq[1] = tq[0];
+    }
     // each lane fetches one 16-byte chunk of a query row; chunks are
     // XOR-swizzled by row in LDS, so the lane holds logical chunk pc ^ row
 #pragma unroll
     for (int j = 0; j < QPW; ++j) {
-      const int row = (wave * QPW + j) * ROWS_PER_LOAD + lane / CPR;
+      const int I = wave * QPW + j;
+      const int tt = I / NQI;
+      const int row = (I % NQI) * ROWS_PER_LOAD + lane / CPR;
       const int lc = (lane % CPR) ^ (row & (CPR - 1));
-      const int d = min(d0 + row, S - 1);
-      dma16(qb + (size_t)d * D + lc * 8, qst(J) + (wave * QPW + j) * 1024);
+      const int d = min(dt0 + tq[tt] * kQT + row, S - 1);
+      const bf16_t* qb = q + (head0 + tg[tt]) * S * D;
+      dma16(qb + (size_t)d * D + lc * 8, qst(J) + I * 1024);
     }
-    dma4(lse + head * S + min(d0 + col, S - 1), lst(J) + wave * 64);
-    if (++iq == nq) {
-      iq = 0;
-      ++ig;
+    {
+      const int tt = TPS == 2 ? half : 0;
+      dma4(lse + (head0 + tg[tt]) * S + min(dt0 + tq[tt] * kQT + col, S - 1), lst(J) + wave * 64);
     }
+#pragma unroll
+    for (int t = 0; t < TPS; ++t)
+      if (++iq == nq) {
+        iq = 0;
+        ++ig;
+      }
   };
 
   bf16x8 ka[NS];
@@ -257,91 +282,97 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KVPO
     }
   };
 
-  // prologue: tiles 0 .. kStages-2 into stages 0 .. kStages-2
-  if (0 < n_iter) issue(I0{});
-  if (1 < n_iter && kStages > 2) issue(I1{});
-  if (2 < n_iter && kStages > 3) issue(I2{});
+  // prologue: stages 0 .. kStages-2
+  const int n_st = (n_iter + TPS - 1) / TPS;  // stages of this segment
+  if (0 < n_st) issue(I0{});
+  if (1 < n_st && kStages > 2) issue(I1{});
+  if (2 < n_st && kStages > 3) issue(I2{});
 
-  // One step on local tile `it`, which lives in stage J; the stage of tile
-  // it-1 (J-1 mod kStages) is refilled with tile it+kStages-1.
-  auto step = [&](auto J, int it) {
+  // One step on local stage `si`, which lives in ring slot J; the slot of
+  // stage si-1 (J-1 mod kStages) is refilled with stage si+kStages-1.
+  auto step = [&](auto J, int si) {
     constexpr int j = decltype(J)::value;
     constexpr int jn = (j + kStages - 1) % kStages;
-    // tiles issued after this one: min(kStages - 2, n_iter - 1 - it)
-    const int later = min(kStages - 2, n_iter - 1 - it);
+    // stages issued after this one: min(kStages - 2, n_st - 1 - si)
+    const int later = min(kStages - 2, n_st - 1 - si);
     if (later >= kStages - 2) wait_vmcnt<PT * (kStages - 2)>();
     else if (kStages == 4 && later == 1) wait_vmcnt<PT>();
     else wait_vmcnt<0>();
     wait_lgkmcnt0();  // this wave's reads of earlier stages have completed
-    bare_barrier();   // tile `it` is in LDS for every wave; tile it-1's stage is free
-    if (it + kStages - 1 < n_iter) issue(std::integral_constant<int, jn>{});
-    const int d0 = dt0 + cq * kQT;
-    const bool skip = ts >= S || d0 + kQT - 1 < ts + window ||
-                      (lookahead >= 0 && d0 > ts + 31 + window + lookahead);
-    if (!skip) {
-      const uint8_t* tile = qst(J) + frow;
-      u32x4 bu[NS];
+    bare_barrier();   // stage si is in LDS for every wave; stage si-1's slot is free
+    if (si + kStages - 1 < n_st) issue(std::integral_constant<int, jn>{});
 #pragma unroll
-      for (int s = 0; s < NS; ++s) bu[s] = *reinterpret_cast<const u32x4*>(tile + (((2 * s + half) ^ sw) << 4));
-      float lraw = lst(J)[wave * 64 + lane];
-      // all fragment reads are issued before one wait, not one wait per MFMA
-      if constexpr (NS == 8)
-        asm volatile("" ::"v"(bu[0]), "v"(bu[1]), "v"(bu[2]), "v"(bu[3]), "v"(bu[4]), "v"(bu[5]),
-                     "v"(bu[6]), "v"(bu[7]), "v"(lraw));
-      else
-        asm volatile("" ::"v"(bu[0]), "v"(bu[1]), "v"(bu[2]), "v"(bu[3]), "v"(lraw));
-      // queries past the sequence end get L = +inf, so their terms vanish
-      const float L2 = d0 + col < S ? lraw * kLog2e : __builtin_inff();
-      f32x16 acc;
+    for (int tt = 0; tt < TPS; ++tt) {
+      const int it = si * TPS + tt;
+      if (it >= n_iter) break;
+      const int d0 = dt0 + cq * kQT;
+      const bool skip = ts >= S || d0 + kQT - 1 < ts + window ||
+                        (lookahead >= 0 && d0 > ts + 31 + window + lookahead);
+      if (!skip) {
+        const uint8_t* tile = qst(J) + tt * TILE + frow;
+        u32x4 bu[NS];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+        for (int s = 0; s < NS; ++s) bu[s] = *reinterpret_cast<const u32x4*>(tile + (((2 * s + half) ^ sw) << 4));
+        float lraw = lst(J)[wave * 64 + (TPS == 2 ? tt * 32 + col : lane)];
+        // all fragment reads are issued before one wait, not one wait per MFMA
+        if constexpr (NS == 8)
+          asm volatile("" ::"v"(bu[0]), "v"(bu[1]), "v"(bu[2]), "v"(bu[3]), "v"(bu[4]), "v"(bu[5]),
+                       "v"(bu[6]), "v"(bu[7]), "v"(lraw));
+        else
+          asm volatile("" ::"v"(bu[0]), "v"(bu[1]), "v"(bu[2]), "v"(bu[3]), "v"(lraw));
+        // queries past the sequence end get L = +inf, so their terms vanish
+        const float L2 = d0 + col < S ? lraw * kLog2e : __builtin_inff();
+        f32x16 acc;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        bf16x8 bq;
-        __builtin_memcpy(&bq, &bu[s], 16);
-        acc = mfma32(ka[s], bq, acc);
-      }
-      const bool full = d0 >= ts + 31 + window &&
-                        (lookahead < 0 || d0 + kQT - 1 <= ts + window + lookahead);
-      if (full) {
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) macc[r] += fast_exp2(fmaf(acc[r], c, -L2));
-      } else {
-        // key row of register r is ts + 4*half + 8*(r/4) + r%4: the pair is
-        // allowed when base - (8*(r/4) + r%4) lies in [0, lookahead]
-        const int base = d0 + col - ts - window - 4 * half;
-        if (lookahead < 0) {
+        for (int s = 0; s < NS; ++s) {
+          bf16x8 bq;
+          __builtin_memcpy(&bq, &bu[s], 16);
+          acc = mfma32(ka[s], bq, acc);
+        }
+        const bool full = d0 >= ts + 31 + window &&
+                          (lookahead < 0 || d0 + kQT - 1 <= ts + window + lookahead);
+        if (full) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = fast_exp2(fmaf(acc[r], c, -L2));
-            macc[r] += base >= 8 * (r >> 2) + (r & 3) ? p : 0.f;
-          }
+          for (int r = 0; r < 16; ++r) macc[r] += fast_exp2(fmaf(acc[r], c, -L2));
         } else {
+          // key row of register r is ts + 4*half + 8*(r/4) + r%4: the pair is
+          // allowed when base - (8*(r/4) + r%4) lies in [0, lookahead]
+          const int base = d0 + col - ts - window - 4 * half;
+          if (lookahead < 0) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int diff = base - (8 * (r >> 2) + (r & 3));
-            const float p = fast_exp2(fmaf(acc[r], c, -L2));
-            macc[r] += (unsigned)diff <= (unsigned)lookahead ? p : 0.f;
+            for (int r = 0; r < 16; ++r) {
+              const float p = fast_exp2(fmaf(acc[r], c, -L2));
+              macc[r] += base >= 8 * (r >> 2) + (r & 3) ? p : 0.f;
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int diff = base - (8 * (r >> 2) + (r & 3));
+              const float p = fast_exp2(fmaf(acc[r], c, -L2));
+              macc[r] += (unsigned)diff <= (unsigned)lookahead ? p : 0.f;
+            }
           }
         }
       }
-    }
-    if (PER_HEAD && (cq == nq - 1 || it == n_iter - 1)) {
-      flush(cg);
+      if (PER_HEAD && (cq == nq - 1 || it == n_iter - 1)) {
+        flush(cg);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) macc[r] = 0.f;
-    }
-    if (++cq == nq) {
-      cq = 0;
-      ++cg;
+        for (int r = 0; r < 16; ++r) macc[r] = 0.f;
+      }
+      if (++cq == nq) {
+        cq = 0;
+        ++cg;
+      }
     }
   };
 
-  for (int it = 0; it < n_iter; it += kStages) {
-    step(I0{}, it);
-    if (it + 1 < n_iter) step(I1{}, it + 1);
-    if (kStages > 2 && it + 2 < n_iter) step(I2{}, it + 2);
-    if (kStages > 3 && it + 3 < n_iter) step(I3{}, it + 3);
+  for (int si = 0; si < n_st; si += kStages) {
+    step(I0{}, si);
+    if (si + 1 < n_st) step(I1{}, si + 1);
+    if (kStages > 2 && si + 2 < n_st) step(I2{}, si + 2);
+    if (kStages > 3 && si + 3 < n_st) step(I3{}, si + 3);
   }
   if (!PER_HEAD) flush(0);
 
