@@ -108,7 +108,9 @@ kvpop_status kvpop_fwd_lse(const kvpop_dims* dims, const void* q, const void* k,
  *   workspace:      at least kvpop_workspace_bytes(KVPOP_OP_FUTURE_TARGET,
  *                   dims, window) bytes, 256-byte aligned; contents are
  *                   scratch and need no initialisation.
- * The result is deterministic (fixed-order reduction of partial sums).
+ * The result is deterministic on a given device: partial sums are reduced
+ * in a fixed order, and how the work is cut depends only on the shape and
+ * the device's count of resident workgroups.
  */
 kvpop_status kvpop_future_attn_target(const kvpop_dims* dims, const void* q, const void* k,
                                       const float* lse, int window, int lookahead, kvpop_agg agg,
@@ -150,7 +152,9 @@ kvpop_status kvpop_evict_select(int batch, int n_kv_heads, int seq_len, int head
  *   slot_pos: int32 [B][Hkv][n_slots]; slots with slot_pos < 0 are skipped
  *   o:        [B][Hq][D], fp32 or bf16 (round to nearest even) per o_dtype
  *   lse:      nullable fp32 [B][Hq], natural log of the softmax denominator
- *   workspace: kvpop_workspace_bytes(KVPOP_OP_DECODE, dims, 0) bytes.
+ *   workspace: kvpop_workspace_bytes(KVPOP_OP_DECODE, dims, 0) bytes,
+ *   16-byte aligned (zero when B * Hkv rows fill the device without
+ *   splitting the slots; then it may be NULL).
  * A head with no valid slot gets o = 0 and lse = -inf.
  */
 kvpop_status kvpop_decode_attend(const kvpop_dims* dims, const void* q, const void* k_cache,
@@ -200,7 +204,10 @@ kvpop_status kvpop_cache_step(int batch, int n_kv_heads, int head_dim, int n_sin
                               const float* scores_r, void* k_cache, void* v_cache,
                               int32_t* slot_pos, float* slot_score, hipStream_t stream);
 
-/* Bytes of workspace needed by `op` for these dims (0 if none). */
+/* Bytes of workspace needed by `op` for these dims (0 if none).  The
+ * target and decode sizes depend on the current HIP device (its compute
+ * units and the kernels' occupancy): query with the device the call will
+ * run on current. */
 size_t kvpop_workspace_bytes(int op, const kvpop_dims* dims, int window);
 
 #ifdef __cplusplus
