@@ -38,8 +38,8 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 # a torch copy of known size (`bench.py --calibrate-copy`).  Valid only for
 # the kernel sources it was taken on: bench reports null once they change.
 TRAFFIC_SOURCES = ("future_target.hip", "common.h", "launch.h")
-TRAFFIC = {"sha256": "4b9ee089dc5c257278482dd14b74c7de9ab11391ef69a93fe59dbe62a9b30aee",
-           "fetch_bytes": 2 * (24179.7 + 345.0) * 1024, "write_bytes": (578.5 + 128.0) * 1024}
+TRAFFIC = {"sha256": "7ed9ae5c63dd71744b15b74437f4638ca0609074dd0c402ff7661216ff4341f9",
+           "fetch_bytes": 2 * (28614.6 + 345.0) * 1024, "write_bytes": (8770.5 + 128.0) * 1024}
 METRIC = "future-attn target keys/s + MFMA util; bounded-cache decode steps/s + HBM util"
 
 
