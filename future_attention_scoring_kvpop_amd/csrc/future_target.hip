@@ -82,6 +82,10 @@ namespace {
 #ifndef KVPOP_TGT_TPS
 #define KVPOP_TGT_TPS 2
 #endif
+// B fragments read from LDS per wait (8: all at once; 4: two groups)
+#ifndef KVPOP_TGT_FRAG_GROUP
+#define KVPOP_TGT_FRAG_GROUP 4
+#endif
 // waves per SIMD the kernel is compiled for (sets its register budget:
 // 512 / n registers per lane)
 #ifndef KVPOP_TGT_WPE
@@ -111,7 +115,7 @@ __device__ __forceinline__ void xreduce_step(float* v, int lane) {
 template <int D, bool PER_HEAD, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KVPOP_TGT_WPE, KVPOP_TGT_WPE))) void future_target_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const float* __restrict__ lse,
-    float* __restrict__ partial, long long* __restrict__ run_start, int Hq, int Hkv, int S,
+    float* __restrict__ partial, int* __restrict__ run_start, int Hq, int Hkv, int S,
     int window, int lookahead, float c, TargetGeom geo) {
   constexpr int KB = 32 * WAVES;            // keys per key block
   constexpr int NS = D / 16;                // MFMA k-slices
@@ -146,7 +150,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KVPO
 
   const int G = Hq / Hkv;
   const int wg = xcd_remap(blockIdx.x, gridDim.x);  // position of this share in the list
-  long long x, x_end;
+  int x, x_end;
   int bh, ch, kb = 0, off;
   if (geo.item_mode) {
     // one whole run: wg is the dense run index (b, h), chunk, key block
@@ -156,16 +160,16 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KVPO
     const int n = n_qtiles(geo, ch, kb);
     if (n == 0) return;
     x = 0;
-    x_end = (long long)G * n;
+    x_end = G * n;
     off = 0;
   } else {
-  x = (long long)wg * geo.share;
+  x = wg * geo.share;
   x_end = min(geo.total, x + geo.share);
   if (x >= x_end) return;
   // locate the share's first square: (b, h), chunk, key block, offset in the run
-  bh = (int)(x / geo.per_bh);
+  bh = x / geo.per_bh;
   {
-    const long long rem = x - (long long)bh * geo.per_bh;
+    const int rem = x - bh * geo.per_bh;
     int lo = 0, hi = geo.n_chunks - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -173,13 +177,13 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KVPO
       else hi = mid - 1;
     }
     ch = lo;
-    long long r2 = rem - geo.cpre[ch];
+    int r2 = rem - geo.cpre[ch];
     for (;; ++kb) {
-      const long long n = (long long)G * n_qtiles(geo, ch, kb);
+      const int n = G * n_qtiles(geo, ch, kb);
       if (r2 < n) break;
       r2 -= n;
     }
-    off = (int)r2;
+    off = r2;
   }
   }
 
@@ -195,13 +199,13 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KVPO
 
   for (bool first = true;; first = false) {
   const int nq = n_qtiles(geo, ch, kb);
-  const int n_iter = (int)min((long long)(G * nq - off), x_end - x);
+  const int n_iter = min(G * nq - off, x_end - x);
   const int b = bh / Hkv, h = bh - (bh / Hkv) * Hkv;
   const int t0 = kb * KB;
   const int dt0 = 32 * max(ch * geo.ct, kb * geo.kbt + geo.w_t);  // the run's first query tile
   const int ts = t0 + 32 * wave;  // this wave's 32 keys
-  const long long run = ((long long)bh * geo.n_chunks + ch) * geo.n_kb + kb;
-  const long long run0 = run * (PER_HEAD ? G : 1);
+  const int run = (bh * geo.n_chunks + ch) * geo.n_kb + kb;
+  const int run0 = run * (PER_HEAD ? G : 1);
   const size_t head0 = (size_t)b * Hq + (size_t)h * G;  // first query head of the group
   if (!geo.item_mode && off == 0 && tid == 0) run_start[run] = x;
   if (!first) {
@@ -277,8 +281,8 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KVPO
     const int r = col & 15;
     const int t = ts + 8 * (r >> 2) + 4 * half + (r & 3);
     if (col < 16 && t < S) {
-      const long long piece = run0 + (PER_HEAD ? gout : 0) + (geo.item_mode ? 0 : wg);
-      partial[piece * KB + (t - t0)] = v[0];
+      const int piece = run0 + (PER_HEAD ? gout : 0) + (geo.item_mode ? 0 : wg);
+      partial[(size_t)piece * KB + (t - t0)] = v[0];
     }
   };
 
@@ -310,27 +314,33 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KVPO
                         (lookahead >= 0 && d0 > ts + 31 + window + lookahead);
       if (!skip) {
         const uint8_t* tile = qst(J) + tt * TILE + frow;
-        u32x4 bu[NS];
-#pragma unroll
-        for (int s = 0; s < NS; ++s) bu[s] = *reinterpret_cast<const u32x4*>(tile + (((2 * s + half) ^ sw) << 4));
         float lraw = lst(J)[wave * 64 + (TPS == 2 ? tt * 32 + col : lane)];
-        // all fragment reads are issued before one wait, not one wait per MFMA
-        if constexpr (NS == 8)
-          asm volatile("" ::"v"(bu[0]), "v"(bu[1]), "v"(bu[2]), "v"(bu[3]), "v"(bu[4]), "v"(bu[5]),
-                       "v"(bu[6]), "v"(bu[7]), "v"(lraw));
-        else
-          asm volatile("" ::"v"(bu[0]), "v"(bu[1]), "v"(bu[2]), "v"(bu[3]), "v"(lraw));
-        // queries past the sequence end get L = +inf, so their terms vanish
-        const float L2 = d0 + col < S ? lraw * kLog2e : __builtin_inff();
         f32x16 acc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+        // fragment reads in groups of FG, each group issued before one wait
+        // (the next group's reads overlap this group's MFMAs)
+        constexpr int FG = KVPOP_TGT_FRAG_GROUP;
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          bf16x8 bq;
-          __builtin_memcpy(&bq, &bu[s], 16);
-          acc = mfma32(ka[s], bq, acc);
+        for (int s0 = 0; s0 < NS; s0 += FG) {
+          u32x4 bu[FG];
+#pragma unroll
+          for (int s = 0; s < FG; ++s)
+            bu[s] = *reinterpret_cast<const u32x4*>(tile + (((2 * (s0 + s) + half) ^ sw) << 4));
+          if constexpr (FG == 8)
+            asm volatile("" ::"v"(bu[0]), "v"(bu[1]), "v"(bu[2]), "v"(bu[3]), "v"(bu[4]), "v"(bu[5]),
+                         "v"(bu[6]), "v"(bu[7]), "v"(lraw));
+          else
+            asm volatile("" ::"v"(bu[0]), "v"(bu[1]), "v"(bu[2]), "v"(bu[3]), "v"(lraw));
+#pragma unroll
+          for (int s = 0; s < FG; ++s) {
+            bf16x8 bq;
+            __builtin_memcpy(&bq, &bu[s], 16);
+            acc = mfma32(ka[s0 + s], bq, acc);
+          }
         }
+        // queries past the sequence end get L = +inf, so their terms vanish
+        const float L2 = d0 + col < S ? lraw * kLog2e : __builtin_inff();
         const bool full = d0 >= ts + 31 + window &&
                           (lookahead < 0 || d0 + kQT - 1 <= ts + window + lookahead);
         if (full) {
@@ -395,7 +405,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KVPO
 // aggregate the group and apply count normalisation; writes every key
 // (zeros where no query counts).
 __global__ __launch_bounds__(256) void target_merge_kernel(
-    const float* __restrict__ partial, const long long* __restrict__ run_start,
+    const float* __restrict__ partial, const int* __restrict__ run_start,
     float* __restrict__ mass, float* __restrict__ mass_ph, int B, int Hq, int Hkv, int S,
     int window, int lookahead, TargetGeom geo, int agg, int count_normalize, int per_head) {
   const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -411,11 +421,11 @@ __global__ __launch_bounds__(256) void target_merge_kernel(
   const int kb = t / KB;
   const int kk = t - kb * KB;
   // sum of the pieces of run r, whose squares are [lo, lo + n) in the list
-  auto run_sum = [&](long long r, long long lo, long long n) {
-    if (geo.item_mode) return partial[r * KB + kk];  // one piece per run
+  auto run_sum = [&](int r, int lo, int n) {
+    if (geo.item_mode) return partial[(size_t)r * KB + kk];  // one piece per run
     float v = 0.f;
-    for (long long w = lo / geo.share; w <= (lo + n - 1) / geo.share; ++w)
-      v += partial[(r + w) * KB + kk];
+    for (int w = lo / geo.share; w <= (lo + n - 1) / geo.share; ++w)
+      v += partial[(size_t)(r + w) * KB + kk];
     return v;
   };
   float sum = 0.f, mx = 0.f;
@@ -425,8 +435,8 @@ __global__ __launch_bounds__(256) void target_merge_kernel(
       for (int ch = 0; ch < geo.n_chunks; ++ch) {
         const int nq = n_qtiles(geo, ch, kb);
         if (nq == 0) continue;
-        const long long run = ((long long)bh * geo.n_chunks + ch) * geo.n_kb + kb;
-        v += run_sum(run * G + gl, geo.item_mode ? 0 : run_start[run] + (long long)gl * nq, nq);
+        const int run = (bh * geo.n_chunks + ch) * geo.n_kb + kb;
+        v += run_sum(run * G + gl, geo.item_mode ? 0 : run_start[run] + gl * nq, nq);
       }
       if (mass_ph)
         mass_ph[((size_t)b * Hq + h * G + gl) * S + t] = count_normalize ? (nt > 0 ? v / (float)nt : 0.f) : v;
@@ -437,8 +447,8 @@ __global__ __launch_bounds__(256) void target_merge_kernel(
     for (int ch = 0; ch < geo.n_chunks; ++ch) {
       const int nq = n_qtiles(geo, ch, kb);
       if (nq == 0) continue;
-      const long long run = ((long long)bh * geo.n_chunks + ch) * geo.n_kb + kb;
-      sum += run_sum(run, geo.item_mode ? 0 : run_start[run], (long long)G * nq);
+      const int run = (bh * geo.n_chunks + ch) * geo.n_kb + kb;
+      sum += run_sum(run, geo.item_mode ? 0 : run_start[run], G * nq);
     }
   }
   float out = agg == 0 ? sum : agg == 1 ? sum / (float)G : mx;
@@ -475,31 +485,40 @@ static TargetGeom make_geometry(const AttnShape& s, const TargetPlan& p, int win
   g.s_t = (s.S + 31) / 32;
   g.la_t = lookahead < 0 ? (1 << 30)
                          : (int)(((long long)p.key_block + window + lookahead + 31) / 32);
-  g.cpre[0] = 0;
+  // squares per chunk of one (b, h), and of the launch, in 64 bits
+  long long cpre[kTgtMaxChunks + 1];
+  cpre[0] = 0;
   for (int ch = 0; ch < g.n_chunks; ++ch) {
     long long n = 0;
     for (int kb = 0; kb < g.n_kb; ++kb) n += n_qtiles(g, ch, kb);
-    g.cpre[ch + 1] = g.cpre[ch] + n * g.G;
+    cpre[ch + 1] = cpre[ch] + n * g.G;
   }
-  for (int ch = g.n_chunks + 1; ch <= kTgtMaxChunks; ++ch) g.cpre[ch] = g.cpre[g.n_chunks];
-  g.per_bh = g.cpre[g.n_chunks];
-  g.total = g.per_bh * s.B * s.Hkv;
+  const long long per_bh = cpre[g.n_chunks];
+  const long long total = per_bh * s.B * s.Hkv;
   // whole rounds of `slots` workgroups, each share at most the cap
   const long long cap = (long long)slots * KVPOP_TGT_SHARE_CAP;
-  const long long rounds = std::max(1LL, (g.total + cap - 1) / cap);
-  g.rounds = (int)rounds;
-  long long share = (g.total + (long long)slots * rounds - 1) / ((long long)slots * rounds);
+  const long long rounds = std::max(1LL, (total + cap - 1) / cap);
+  g.rounds = (int)rounds;  // the even split's: it bounds the workspace of any launch
+  long long share = (total + (long long)slots * rounds - 1) / ((long long)slots * rounds);
   if (share < KVPOP_TGT_MIN_SHARE) share = KVPOP_TGT_MIN_SHARE;
-  g.share = share;
-  g.n_wg = (int)((g.total + share - 1) / share);
-  // item mode: enough non-empty runs for many rounds of workgroups
+  // one run per workgroup when there are many rounds of runs, or when the
+  // list does not fit the 32-bit offsets the even split uses
   long long runs_ne = 0;
   for (int ch = 0; ch < g.n_chunks; ++ch)
     for (int kb = 0; kb < g.n_kb; ++kb) runs_ne += n_qtiles(g, ch, kb) > 0;
   runs_ne *= (long long)s.B * s.Hkv;
-  g.item_mode = runs_ne >= (long long)KVPOP_TGT_ITEM_ROUNDS * slots ? 1 : 0;
-  // (rounds stays the even split's: it bounds the workspace of any launch)
-  if (g.item_mode) g.n_wg = s.B * s.Hkv * g.n_chunks * g.n_kb;
+  g.item_mode = runs_ne >= (long long)KVPOP_TGT_ITEM_ROUNDS * slots || total >= (1LL << 30) ? 1 : 0;
+  if (g.item_mode) {
+    g.per_bh = g.total = g.share = 0;
+    for (int ch = 0; ch <= kTgtMaxChunks; ++ch) g.cpre[ch] = 0;
+    g.n_wg = s.B * s.Hkv * g.n_chunks * g.n_kb;
+  } else {
+    for (int ch = 0; ch <= kTgtMaxChunks; ++ch) g.cpre[ch] = (int)cpre[std::min(ch, g.n_chunks)];
+    g.per_bh = (int)per_bh;
+    g.total = (int)total;
+    g.share = (int)share;
+    g.n_wg = (int)((total + share - 1) / share);
+  }
   return g;
 }
 
@@ -554,7 +573,7 @@ TargetPlan plan_target(const AttnShape& s, int window) {
   p.runs = (size_t)s.B * s.Hkv * p.n_chunks * p.n_kb;
   p.partial_floats = (p.runs * G + (size_t)p.max_wg) * p.key_block;
   const size_t part_bytes = (p.partial_floats * sizeof(float) + 255) & ~(size_t)255;
-  p.workspace_bytes = part_bytes + p.runs * sizeof(long long);
+  p.workspace_bytes = part_bytes + p.runs * sizeof(int);
   return p;
 }
 
@@ -568,7 +587,7 @@ hipError_t launch_future_target(const AttnShape& s, const void* q, const void* k
                                 float* workspace, hipStream_t st) {
   const TargetPlan p = plan_target(s, window);
   const TargetGeom geo = target_geometry(s, p, window, lookahead);
-  long long* run_start = reinterpret_cast<long long*>(
+  int* run_start = reinterpret_cast<int*>(
       reinterpret_cast<char*>(workspace) + ((p.partial_floats * sizeof(float) + 255) & ~(size_t)255));
   const bool per_head = agg == 2 || mass_per_qhead != nullptr;
   const float c = s.scale * kLog2e;

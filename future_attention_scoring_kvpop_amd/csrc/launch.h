@@ -49,10 +49,12 @@ struct TargetPlan {
 struct TargetGeom {
   int G, S, window, key_block, kbt, n_kb, n_chunks, ct, w_t, s_t, la_t, n_wg, rounds;
   int item_mode;     // 1: one workgroup per run (n_wg = all runs, empty ones exit)
-  long long per_bh;  // squares per (b, KV head)
-  long long total;   // squares in the launch
-  long long share;   // squares per workgroup
-  long long cpre[kTgtMaxChunks + 1];
+  // (32-bit: an even split is only used while the whole list fits; larger
+  // launches take one run per workgroup and use none of these)
+  int per_bh;  // squares per (b, KV head)
+  int total;   // squares in the launch
+  int share;   // squares per workgroup
+  int cpre[kTgtMaxChunks + 1];
 };
 
 __host__ __device__ inline int n_qtiles(const TargetGeom& g, int c, int kb) {
