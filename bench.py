@@ -9,7 +9,8 @@ value = KV-head keys scored per second = B*Hkv*S / step time.
 
 Also reported: the bounded-cache decode workload (64 sequences, 36 layers,
 budget 4096 per KV head, 512 steps: per layer and step one cache step with
-the delayed MLP scorer and one GQA decode attention) in steps/s with its
+the delayed MLP scorer and one GQA decode attention; the same steps through
+the single-call kvpop_decode_step are reported beside it) in steps/s with its
 HBM roofline, the roofline of the dominant kernel, and the CPU oracle timed
 on a bounded sample.
 
@@ -210,14 +211,20 @@ def bench_decode(kv, steps, layers, seed=5):
     dd = kv.dims(B, Hq, Hkv, bud, D)
     dws = torch.empty(kv.workspace_bytes(kv.OP_DECODE, dd), dtype=torch.uint8, device=dev)
 
-    def one_step(i):
-        pos = S + i
+    def one_step(i, pos):
         for layer in range(layers):
             kc, vc, sp, ss = caches[layer]
             kv.cache_step(kc, vc, sp, ss, ks[i, layer], vs[i, layer], pos, w.n_sink, w.window, delay,
                           mlp=mlps[layer])
             kv.decode_attend(qs[i, layer], kc, vc, sp, out_dtype=torch.bfloat16, want_lse=False,
                              out=o, workspace=dws)
+
+    def one_fused_step(i, pos):
+        for layer in range(layers):
+            kc, vc, sp, ss = caches[layer]
+            kv.decode_step(qs[i, layer], kc, vc, sp, ss, ks[i, layer], vs[i, layer], pos, w.n_sink,
+                           w.window, delay, mlp=mlps[layer], out_dtype=torch.bfloat16,
+                           want_lse=False, out=o, workspace=dws)
 
     # attention-only timing of one layer (events on the launch stream)
     ea = torch.cuda.Event(enable_timing=True)
@@ -235,19 +242,24 @@ def bench_decode(kv, steps, layers, seed=5):
     torch.cuda.synchronize()
     t_att_ms = ea.elapsed_time(eb) / n_att
 
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(steps):
-        one_step(i)
-        if (i + 1) % 128 == 0:
-            log(f"decode: {i + 1}/{steps} steps issued")
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1)
+    def timed(fn, pos0, label):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            fn(i, pos0 + i)
+            if (i + 1) % 128 == 0:
+                log(f"decode ({label}): {i + 1}/{steps} steps issued")
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1), time.perf_counter() - t0
+
+    # the decode steps continue one sequence: the fused calls take the
+    # positions after the two-call run
+    ms, wall = timed(one_step, S, "cache step + attention")
+    ms_fused, _ = timed(one_fused_step, S + steps, "fused decode step")
     sps = steps / (ms / 1e3)
     by = decode_bytes_per_step(w, layers)
     att_bytes = B * Hkv * 2 * bud * D * 2 + B * Hq * D * 2 * 2
@@ -257,6 +269,9 @@ def bench_decode(kv, steps, layers, seed=5):
         "wall_s": wall, "bytes_per_step": by,
         "hbm": {"achieved": by * sps / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": by * sps / 1e9 / HBM_PEAK_GBS},
+        "fused_decode_step": {"value": steps / (ms_fused / 1e3), "unit": "steps/s",
+                              "ms_per_step": ms_fused / steps,
+                              "hbm_frac": by * steps / (ms_fused / 1e3) / 1e9 / HBM_PEAK_GBS},
         "attend_kernel": {"ms": t_att_ms, "bytes": att_bytes,
                           "achieved": att_bytes / (t_att_ms / 1e3) / 1e9, "unit": "GB/s",
                           "frac": att_bytes / (t_att_ms / 1e3) / 1e9 / HBM_PEAK_GBS},

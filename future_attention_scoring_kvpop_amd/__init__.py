@@ -28,7 +28,7 @@ OP_FWD_LSE = 2
 
 EXPORTS = ("kvpop_abi_version", "kvpop_status_string", "kvpop_workspace_bytes", "kvpop_fwd_lse",
            "kvpop_future_attn_target", "kvpop_evict_select", "kvpop_decode_attend",
-           "kvpop_score_mlp", "kvpop_cache_step")
+           "kvpop_score_mlp", "kvpop_cache_step", "kvpop_decode_step")
 
 
 class KvpopError(RuntimeError):
@@ -65,6 +65,8 @@ def lib():
             "kvpop_decode_attend": (I, [DP, P, P, P, P, P, I, P, P, Z, P]),
             "kvpop_score_mlp": (I, [I, I, I, I, I, P, P, P, P, P, P, P]),
             "kvpop_cache_step": (I, [I, I, I, I, I, I, I, I, P, P, P, P, P, P, I, P, P, P, P, P, P]),
+            "kvpop_decode_step": (I, [DP, I, I, I, I, P, P, P, P, P, P, I, P, P, P, P, P, P, P, I, P,
+                                      P, Z, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -238,3 +240,41 @@ def cache_step(k_cache, v_cache, slot_pos, slot_score, k_new, v_new, pos_q, n_si
                                 _p(scores_r), _p(k_cache), _p(v_cache), _p(slot_pos),
                                 _p(slot_score), _stream())
     _check("kvpop_cache_step", st)
+
+
+def decode_step(q, k_cache, v_cache, slot_pos, slot_score, k_new, v_new, pos_q, n_sink, window,
+                delay, mlp=None, scores_r=None, out_dtype=torch.float32, want_lse=True, scale=0.0,
+                out=None, out_lse=None, workspace=None):
+    """One bounded-cache decode step in place, then decode attention over the
+    updated cache (Sec. 3, App. C.1, App. E.4): o [B,Hq,D], lse [B,Hq].
+    Same effect as cache_step(...) followed by decode_attend(...)."""
+    _need(q, torch.bfloat16, "q", 3)
+    _need(k_cache, torch.bfloat16, "k_cache", 4)
+    _need(v_cache, torch.bfloat16, "v_cache", 4)
+    _need(slot_pos, torch.int32, "slot_pos", 3)
+    _need(slot_score, torch.float32, "slot_score", 3)
+    _need(k_new, torch.bfloat16, "k_new", 3)
+    _need(v_new, torch.bfloat16, "v_new", 3)
+    B, Hq, D = q.shape
+    Hkv, budget = k_cache.shape[1], k_cache.shape[2]
+    w1 = b1 = w2 = b2 = None
+    hidden = 0
+    if mlp is not None:
+        w1, b1, w2, b2 = mlp
+        hidden = w1.shape[1]
+    if scores_r is not None:
+        _need(scores_r, torch.float32, "scores_r")
+    d = dims(B, Hq, Hkv, budget, D, scale)
+    o = out if out is not None else torch.empty((B, Hq, D), dtype=out_dtype, device=q.device)
+    lse = out_lse if out_lse is not None else (
+        torch.empty((B, Hq), dtype=torch.float32, device=q.device) if want_lse else None)
+    nbytes = workspace_bytes(OP_DECODE, d)
+    ws = workspace if workspace is not None else (
+        torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None)
+    st = lib().kvpop_decode_step(ctypes.byref(d), int(n_sink), int(window), int(delay), int(pos_q),
+                                 _p(k_new), _p(v_new), _p(w1), _p(b1), _p(w2), _p(b2), hidden,
+                                 _p(scores_r), _p(k_cache), _p(v_cache), _p(slot_pos),
+                                 _p(slot_score), _p(q), _p(o), 1 if o.dtype == torch.bfloat16 else 0,
+                                 _p(lse), _p(ws), 0 if ws is None else ws.numel(), _stream())
+    _check("kvpop_decode_step", st)
+    return o, lse

@@ -200,4 +200,39 @@ kvpop_status kvpop_cache_step(int batch, int n_kv_heads, int head_dim, int n_sin
                                            slot_pos, slot_score, stream));
 }
 
+kvpop_status kvpop_decode_step(const kvpop_dims* dims, int n_sink, int window, int delay,
+                               int pos_q, const void* k_new, const void* v_new, const float* w1,
+                               const float* b1, const float* w2, const float* b2, int hidden,
+                               const float* scores_r, void* k_cache, void* v_cache,
+                               int32_t* slot_pos, float* slot_score, const void* q, void* o,
+                               kvpop_out_dtype o_dtype, float* lse, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  AttnShape s;
+  kvpop_status st = check_dims(dims, &s);
+  if (st != KVPOP_OK) return st;
+  const int budget = s.S;
+  if (n_sink < 0 || window < 1 || budget < n_sink + window) return KVPOP_ERR_INVALID_ARGUMENT;
+  if (delay < 0 || delay >= window || pos_q < 0) return KVPOP_ERR_INVALID_ARGUMENT;
+  if (!k_new || !v_new || !k_cache || !v_cache || !slot_pos || !slot_score || !q || !o)
+    return KVPOP_ERR_INVALID_ARGUMENT;
+  if (o_dtype != KVPOP_OUT_F32 && o_dtype != KVPOP_OUT_BF16) return KVPOP_ERR_INVALID_ARGUMENT;
+  const bool mlp = w1 != nullptr;
+  if (mlp == (scores_r != nullptr)) return KVPOP_ERR_INVALID_ARGUMENT;
+  if (mlp && (!b1 || !w2 || !b2)) return KVPOP_ERR_INVALID_ARGUMENT;
+  if (mlp && (hidden < 1 || hidden > 64)) return KVPOP_ERR_UNSUPPORTED;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(slot_pos, 4) || !aligned(slot_score, 4) ||
+      !aligned(q, 16) || !aligned(o, 4) || (lse && !aligned(lse, 4)))
+    return KVPOP_ERR_INVALID_ARGUMENT;
+  const kvpop::DecodePlan p = kvpop::plan_decode(s);
+  if (p.workspace_floats) {
+    if (!workspace || !aligned(workspace, 16)) return KVPOP_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < p.workspace_floats * sizeof(float)) return KVPOP_ERR_WORKSPACE_TOO_SMALL;
+  }
+  return from_hip(kvpop::launch_decode_step(
+      s, n_sink, window, delay, pos_q, k_new, v_new, w1, b1, w2, b2, mlp ? hidden : 0, scores_r,
+      k_cache, v_cache, slot_pos, slot_score, q, o, o_dtype == KVPOP_OUT_BF16 ? 1 : 0, lse,
+      (float*)workspace, stream));
+}
+
 }  // extern "C"

@@ -102,4 +102,13 @@ hipError_t launch_cache_step(int B, int Hkv, int D, int n_sink, int window, int 
                              const float* b2, int hidden, const float* scores_r, void* kc,
                              void* vc, int32_t* slot_pos, float* slot_score, hipStream_t st);
 
+// cache step, then decode attention over the updated cache (one launch
+// when the decode plan needs no slot split)
+hipError_t launch_decode_step(const AttnShape& s, int n_sink, int window, int delay, int pos_q,
+                              const void* k_new, const void* v_new, const float* w1,
+                              const float* b1, const float* w2, const float* b2, int hidden,
+                              const float* scores_r, void* kc, void* vc, int32_t* slot_pos,
+                              float* slot_score, const void* q, void* o, int o_bf16, float* lse,
+                              float* workspace, hipStream_t st);
+
 }  // namespace kvpop

@@ -204,6 +204,25 @@ kvpop_status kvpop_cache_step(int batch, int n_kv_heads, int head_dim, int n_sin
                               const float* scores_r, void* k_cache, void* v_cache,
                               int32_t* slot_pos, float* slot_score, hipStream_t stream);
 
+/*
+ * kvpop_decode_step -- one bounded-cache decode step, then decode attention
+ * over the updated cache.  Sec. 3, App. C.1 and App. E.4: the token leaving
+ * the window is kept or dropped, the new token enters its ring slot, the
+ * delayed score is taken, and the query attends over the retained entries.
+ * Same effect, bit for bit, as kvpop_cache_step(...) followed by
+ * kvpop_decode_attend(...) with the same arguments (dims->seq_len is the
+ * budget); when B * Hkv rows fill the device the two run in one launch.
+ *   workspace: kvpop_workspace_bytes(KVPOP_OP_DECODE, dims, 0) bytes.
+ * Errors: the union of the two calls' checks.
+ */
+kvpop_status kvpop_decode_step(const kvpop_dims* dims, int n_sink, int window, int delay,
+                               int pos_q, const void* k_new, const void* v_new, const float* w1,
+                               const float* b1, const float* w2, const float* b2, int hidden,
+                               const float* scores_r, void* k_cache, void* v_cache,
+                               int32_t* slot_pos, float* slot_score, const void* q, void* o,
+                               kvpop_out_dtype o_dtype, float* lse, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
 /* Bytes of workspace needed by `op` for these dims (0 if none).  The
  * target and decode sizes depend on the current HIP device (its compute
  * units and the kernels' occupancy): query with the device the call will

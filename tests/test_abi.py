@@ -131,6 +131,26 @@ def test_mlp_and_cache_step_validation(lib):
     assert step(w1=GOOD, sr=None, hidden=65) == 2
 
 
+def test_decode_step_validation(lib):
+    d = kv.dims(64, 32, 8, 4096, 128)
+
+    def call(d=d, window=256, delay=16, w1=None, sr=GOOD, hidden=64, o_dtype=0, pos=40000, q=GOOD):
+        return lib.kvpop_decode_step(ctypes.byref(d), 4, window, delay, pos, GOOD, GOOD, w1, GOOD,
+                                     GOOD, GOOD, hidden, sr, GOOD, GOOD, GOOD, GOOD, q, GOOD,
+                                     o_dtype, None, None, 0, None)
+
+    assert call(window=0) == 1
+    assert call(delay=256) == 1
+    assert call(pos=-1) == 1
+    assert call(q=None) == 1
+    assert call(o_dtype=2) == 1
+    assert call(w1=GOOD) == 1                 # both an MLP and given scores
+    assert call(w1=None, sr=None) == 1        # neither
+    assert call(w1=GOOD, sr=None, hidden=65) == 2
+    assert call(d=kv.dims(64, 32, 8, 200, 128)) == 1  # budget < s + w
+    assert call(d=kv.dims(64, 32, 8, 4096, 96)) == 2  # head dim
+
+
 def test_python_binding_rejects_host_tensors():
     import torch
     with pytest.raises(ValueError):

@@ -145,3 +145,53 @@ def test_cache_step_mlp_matches_score_kernel(kv):
             assert torch.equal(got.view(torch.int32), ref.view(torch.int32)), i
             o = oracle.mlp_score(f32(kr), *(t.cpu().numpy() for t in (w1, b1, w2, b2)))[:, :, 0]
             assert_close(f32(got), o, MLP_ATOL, MLP_RTOL, "mlp in step")
+
+
+def _decode_state(B, Hkv, D, s, w, budget, seed):
+    """A full bounded cache as the prefix selection leaves it."""
+    S0 = 4 * budget
+    k = synth.bf16(synth.normal((B, Hkv, S0, D), seed, std=0.5)).cuda()
+    v = synth.bf16(synth.normal((B, Hkv, S0, D), seed + 1)).cuda()
+    sc = synth.scores((B, Hkv, S0), seed + 2, kind="normal").cuda()
+    sp, ss, kc, vc = kv_lib().evict_select(sc, s, w, budget, k, v)
+    return S0, {"kc": kc, "vc": vc, "sp": sp, "ss": ss}
+
+
+def kv_lib():
+    return ensure_built()
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,D,k_sel,use_mlp", [
+    (64, 32, 8, 128, 60, True), (64, 32, 8, 128, 60, False), (2, 8, 2, 64, 60, True),
+    (3, 4, 4, 128, 60, False),
+    (1, 8, 2, 128, 1000, True)])  # few rows, long budget: slots split, two launches
+def test_decode_step_matches_two_calls(kv, B, Hq, Hkv, D, k_sel, use_mlp):
+    """kvpop_decode_step (one launch when every (b, KV head) row has its own
+    workgroup, else the two kernels) leaves the same cache state, bit for
+    bit, and gives the same o and lse as kvpop_cache_step followed by
+    kvpop_decode_attend."""
+    s, w, delay, hidden = 4, 32, 5, 64
+    budget = s + w + k_sel
+    S0, a = _decode_state(B, Hkv, D, s, w, budget, seed=B + D)
+    b = {n: t.clone() for n, t in a.items()}
+    mlp = [t.cuda() for t in synth.mlp_weights(Hkv, D, hidden, seed=8)] if use_mlp else None
+    g = torch.Generator().manual_seed(11)
+    for i in range(40):
+        q = S0 + i
+        kn = synth.bf16(synth.normal((B, Hkv, D), 300 + i, std=0.5)).cuda()
+        vn = synth.bf16(synth.normal((B, Hkv, D), 600 + i)).cuda()
+        qv = synth.bf16(synth.normal((B, Hq, D), 900 + i, std=0.5)).cuda()
+        sr = None if use_mlp else (torch.randint(0, 6, (B, Hkv), generator=g).float() * 0.5).cuda()
+        kv.cache_step(a["kc"], a["vc"], a["sp"], a["ss"], kn, vn, q, s, w, delay, mlp=mlp, scores_r=sr)
+        oa, la = kv.decode_attend(qv, a["kc"], a["vc"], a["sp"])
+        ob, lb = kv.decode_step(qv, b["kc"], b["vc"], b["sp"], b["ss"], kn, vn, q, s, w, delay,
+                                mlp=mlp, scores_r=sr)
+        torch.cuda.synchronize()
+        for n in ("sp", "ss", "kc", "vc"):
+            x, y = a[n], b[n]
+            if x.dtype != torch.int32:
+                x, y = x.view(torch.int16 if x.dtype == torch.bfloat16 else torch.int32), \
+                    y.view(torch.int16 if y.dtype == torch.bfloat16 else torch.int32)
+            assert torch.equal(x, y), (i, n)
+        assert torch.equal(oa.view(torch.int32), ob.view(torch.int32)), i
+        assert torch.equal(la.view(torch.int32), lb.view(torch.int32)), i
