@@ -61,7 +61,7 @@ template <int D>
 __global__ __launch_bounds__(kThreads, KVPOP_FWD_MIN_BLOCKS) void fwd_lse_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, float* __restrict__ lse,
     float2* __restrict__ part, int B, int Hq, int Hkv, int S, float c, float scale, int n_pb,
-    int kmax, int n_pieces, int n_items) {
+    int kmax, int n_pieces, int n_items, int snake_cus) {
   constexpr int NS = D / 16;           // MFMA k-slices
   constexpr int CPR = D / 8;           // 16-byte chunks per row
   constexpr int ROWB = D * 2;          // bytes per K row
@@ -78,7 +78,24 @@ __global__ __launch_bounds__(kThreads, KVPOP_FWD_MIN_BLOCKS) void fwd_lse_kernel
 
   const int G = Hq / Hkv;
   const int P = 128 / G;
-  const int item = xcd_remap(blockIdx.x, n_items);
+  // Blocks go round robin over the 8 XCDs and, within an XCD, over its CUs.
+  // Each XCD takes a contiguous range of items (longest first).  When the
+  // whole launch is resident at once (snake_cus = CUs per XCD, else 0), the
+  // range is dealt to the CUs in alternating direction per round, so every
+  // CU gets a long and a short block in turn and the same total work.
+  int item;
+  {
+    const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int q8 = n_items >> 3, r8 = n_items & 7;
+    const int xstart = x * q8 + (x < r8 ? x : r8), xcount = q8 + (x < r8 ? 1 : 0);
+    int jj = j;
+    if (snake_cus > 0) {
+      const int rnd = j / snake_cus, cu = j - rnd * snake_cus;
+      if (rnd & 1) jj = rnd * snake_cus + (snake_cus - 1 - cu);
+      if (jj >= xcount) jj = j;  // a partial last round keeps its order
+    }
+    item = xstart + jj;
+  }
   const int bh = item / (n_pb * n_pieces);
   const int rest = item - bh * (n_pb * n_pieces);
   const int pb = n_pb - 1 - rest / n_pieces;  // longest rows first
@@ -247,16 +264,19 @@ hipError_t launch_fwd_lse(const AttnShape& s, const void* q, const void* k, floa
   const FwdPlan p = plan_fwd(s);
   const int n_items = s.B * s.Hkv * p.n_pb * p.n_pieces;
   const float c = s.scale * kLog2e;
+  // one resident round (four workgroups per CU): deal each XCD's blocks in a snake
+  const int cus = device_cu_count();
+  const int snake_cus = n_items <= cus * KVPOP_FWD_MIN_BLOCKS && cus % 8 == 0 ? cus / 8 : 0;
   dim3 grid(n_items), block(kThreads);
   float2* part = reinterpret_cast<float2*>(workspace);
   if (s.D == 128)
     hipLaunchKernelGGL(fwd_lse_kernel<128>, grid, block, 0, st, (const bf16_t*)q, (const bf16_t*)k,
                        lse, part, s.B, s.Hq, s.Hkv, s.S, c, s.scale, p.n_pb, p.kmax, p.n_pieces,
-                       n_items);
+                       n_items, snake_cus);
   else
     hipLaunchKernelGGL(fwd_lse_kernel<64>, grid, block, 0, st, (const bf16_t*)q, (const bf16_t*)k,
                        lse, part, s.B, s.Hq, s.Hkv, s.S, c, s.scale, p.n_pb, p.kmax, p.n_pieces,
-                       n_items);
+                       n_items, snake_cus);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_pieces == 1) return e;
   const long rows = (long)s.B * s.Hq * s.S;
