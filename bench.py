@@ -39,8 +39,8 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 # a torch copy of known size (`bench.py --calibrate-copy`).  Valid only for
 # the kernel sources it was taken on: bench reports null once they change.
 TRAFFIC_SOURCES = ("future_target.hip", "common.h", "launch.h")
-TRAFFIC = {"sha256": "7ed9ae5c63dd71744b15b74437f4638ca0609074dd0c402ff7661216ff4341f9",
-           "fetch_bytes": 2 * (28614.6 + 345.0) * 1024, "write_bytes": (8770.5 + 128.0) * 1024}
+TRAFFIC = {"sha256": "8dd68ca283e7794bf02037c29805f97bd1fb601e7b0b9368c018a6e6c301a198",
+           "fetch_bytes": 2 * (22895.9 + 325.0) * 1024, "write_bytes": (577.6 + 128.0) * 1024}
 METRIC = "future-attn target keys/s + MFMA util; bounded-cache decode steps/s + HBM util"
 
 
