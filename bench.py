@@ -37,9 +37,10 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 # the Qwen3-4B layer workload, from two rocprofv3 --pmc runs (FETCH_SIZE, then
 # WRITE_SIZE, KiB per dispatch) each scaled by what the same counter reads for
 # a torch copy of known size (`bench.py --calibrate-copy`).  Valid only for
-# the kernel sources it was taken on: bench reports null once they change.
+# the kernel code it was taken on (sources_digest): bench reports null once
+# that changes.
 TRAFFIC_SOURCES = ("future_target.hip", "common.h", "launch.h")
-TRAFFIC = {"sha256": "8dd68ca283e7794bf02037c29805f97bd1fb601e7b0b9368c018a6e6c301a198",
+TRAFFIC = {"sha256": "1dd8f41b1a35accbc85396a0ba0d721461214a86f6a11ed7c7bafc5cf3dd7d73",
            "fetch_bytes": 2 * (22895.9 + 325.0) * 1024, "write_bytes": (577.6 + 128.0) * 1024}
 METRIC = "future-attn target keys/s + MFMA util; bounded-cache decode steps/s + HBM util"
 
@@ -109,7 +110,6 @@ class TargetStep:
 def bench_target(kv, steps, warmup):
     w = synth.QWEN4B
     st = TargetStep(kv, w)
-    bench_target.step = st
     for _ in range(warmup):
         st.run()
     torch.cuda.synchronize()
@@ -127,7 +127,7 @@ def bench_target(kv, steps, warmup):
     t_tr = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
     t_rest = sum(e[2].elapsed_time(e[3]) for e in evs) / steps
     f_fwd, f_tr = target_flops(w)
-    return w, ms, t_fwd, t_tr, t_rest, f_fwd, f_tr
+    return st, ms, t_fwd, t_tr, t_rest, f_fwd, f_tr
 
 
 def target_flops_lookahead(w, lookahead):
@@ -362,18 +362,27 @@ def cpu_decode_baseline(threads, units=4, steps=16):
                       f"by 64 x 36 units per step"}
 
 
-def traffic_bytes():
-    """The recorded HBM traffic of the target call, or None when the kernel
-    sources differ from those it was measured on."""
+def sources_digest():
+    """SHA-256 of the target kernel's sources with comments and blank lines
+    removed, so that only a change of code invalidates recorded counters."""
     import hashlib
+    import re
 
-    if TRAFFIC is None:
-        return None
     h = hashlib.sha256()
     for name in TRAFFIC_SOURCES:
-        with open(os.path.join(ROOT, "future_attention_scoring_kvpop_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
-    if h.hexdigest() != TRAFFIC["sha256"]:
+        with open(os.path.join(ROOT, "future_attention_scoring_kvpop_amd", "csrc", name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        lines = [ln.rstrip() for ln in text.splitlines() if ln.strip()]
+        h.update("\n".join(lines).encode())
+    return h.hexdigest()
+
+
+def traffic_bytes():
+    """The recorded HBM traffic of the target call, or None when the kernel
+    code differs from the code it was measured on."""
+    if TRAFFIC is None or sources_digest() != TRAFFIC["sha256"]:
         return None
     return TRAFFIC["fetch_bytes"] + TRAFFIC["write_bytes"]
 
@@ -420,7 +429,8 @@ def main():
     torch.cuda.set_device(0)
 
     log(f"target step: {a.warmup} warmup + {a.steps} timed")
-    w, ms, t_fwd, t_tr, t_rest, f_fwd, f_tr = bench_target(kv, a.steps, a.warmup)
+    st, ms, t_fwd, t_tr, t_rest, f_fwd, f_tr = bench_target(kv, a.steps, a.warmup)
+    w = st.w
     keys = w.B * w.Hkv * w.S
     value = keys / (ms / 1e3)
     log(f"target step {ms:.4f} ms (fwd_lse {t_fwd:.4f}, future target {t_tr:.4f}, "
@@ -446,7 +456,7 @@ def main():
                                            "frac": achieved_tr / MFMA_BF16_PEAK_TFLOPS},
                     "select_gather_decode": {"ms": t_rest}},
     }
-    out["target_variants"] = bench_target_variants(kv, bench_target.step)
+    out["target_variants"] = bench_target_variants(kv, st)
     if not a.no_decode:
         log(f"decode: {a.decode_steps} steps x {a.decode_layers} layers")
         out["decode"] = bench_decode(kv, a.decode_steps, a.decode_layers)

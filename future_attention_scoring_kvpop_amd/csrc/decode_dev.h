@@ -16,8 +16,8 @@
 //     an online (max, sum, o) state per head over blocks of 4 slots, and the
 //     16 states of a workgroup are merged once through LDS.  Splits are
 //     merged by a second small kernel with the same log-sum-exp rule.
-#include <atomic>
-
+//   * Each quarter-wave loads the next iteration's K/V rows before it
+//     computes the current one, so a wave always has a row block in flight.
 #pragma once
 
 #include "common.h"

@@ -10,38 +10,37 @@
 //   m_t^(g) = sum_{d=t+w}^{end_t} exp2(s_dt * scale*log2e - LSE_d * log2e)
 //
 // gfx950 mapping
-//   * The work is the list of 32x32 (key, query) squares in the order
-//     (b, KV head h), query chunk, key block, query head, query tile; each
-//     workgroup takes one equal, contiguous share of it, and the shares form
-//     whole rounds of resident workgroups, so the causal triangle costs no
-//     idle tail.  Shares are capped, so the workgroups in flight on one XCD
-//     cover one or two query chunks (about 2 MiB of Q), which stay in that
-//     XCD's L2 while every key block of the chunk streams them.  Within a
-//     key block, each wave
-//     keeps 32 keys resident as MFMA A fragments and streams the query tiles
-//     of all G heads of the group as B fragments:
-//     v_mfma_f32_32x32x16_bf16 yields S^T[key][query].  About 120 registers
-//     per wave keep four waves per SIMD resident, so the MFMA phase of one
-//     wave overlaps the exp2/accumulate phase of the others.
-//   * All waves of a workgroup share each query tile (32 queries).  Tiles
-//     reach LDS by direct global->LDS DMA into a ring of stages, requested
-//     two tiles ahead; each stage is its own LDS object so the compiler
-//     never drains in-flight prefetches before a read.  Rows are stored
-//     unpadded with their 16-byte chunks XOR-swizzled by row, which keeps the
+//   * The work is a list of 32x32 (key, query) squares in the order
+//     (b, KV head h), query chunk (about 2 MiB of Q), key block, query head,
+//     query tile; a run is the squares of one (chunk, key block).  Launches
+//     with few runs give every resident workgroup an equal contiguous share
+//     of the list, so the causal triangle leaves no idle tail; launches with
+//     many rounds of runs give each workgroup one run, so the workgroups of
+//     an XCD stream a chunk's query tiles in step and keep them in L2.
+//   * Within a run each wave keeps its 32 keys resident as MFMA A fragments
+//     and streams the query tiles of all G heads of the group as B
+//     fragments: v_mfma_f32_32x32x16_bf16 yields S^T[key][query].  About 120
+//     registers per wave keep four waves per SIMD resident, so the MFMA
+//     phase of one wave overlaps the exp2/accumulate phase of the others.
+//   * All waves of a workgroup (8 for D = 128) share each stage of two
+//     query tiles.  Stages reach LDS by direct global->LDS DMA into a ring,
+//     each wave issuing a fixed share (and its own copy of the tiles'
+//     normalizers); each stage is its own LDS object so the compiler never
+//     drains in-flight prefetches before a read.  Rows are stored unpadded
+//     with their 16-byte chunks XOR-swizzled by row, which keeps the
 //     fragment reads bank-conflict free.  A bare s_barrier plus explicit
-//     vmcnt/lgkmcnt waits orders the ring.
-//   * Workgroups of 8 waves (256 keys) halve the L2 traffic per key-query
-//     pair against 4 waves (128 keys); launches with few keys use 4 waves.
+//     vmcnt/lgkmcnt waits orders the ring; B fragments are read in groups of
+//     four before one wait.
 //   * Each lane owns one query column and 16 key rows, so per-key sums stay
-//     in registers across every query tile and head; they are reduced
-//     across lanes once per item by a register transpose-reduce.
-//   * Tiles whose 32x32 (key, query) square lies fully inside the allowed
-//     region take a mask-free path (one FMA, one exp2, one add per pair);
-//     fully masked squares are skipped; only the diagonal squares mask.
-//   * A workgroup writes one partial sum per key for every run (chunk and
-//     key block, or chunk, key block and query head) its share touches, into
-//     piece run + wg: runs and workgroups both advance monotonically along
-//     the list, so no two (run, workgroup) pairs share a piece.  The
+//     in registers across every query tile and head of a run; they are
+//     reduced across lanes once per run by a register transpose-reduce.
+//   * Squares fully inside the allowed region take a mask-free path (one
+//     FMA, one exp2, one add per pair); fully masked squares are skipped;
+//     diagonal squares compare each register's key row with a per-lane
+//     threshold; queries past S are masked by L = +inf.
+//   * Each run writes one partial sum per key and workgroup, into piece
+//     run + wg (even split; runs and workgroups both advance along the list,
+//     so no two pairs share a piece) or run (one run per workgroup); the
 //     workgroup holding a run's first square records where the run starts.
 //     A second kernel sums each key's pieces over chunks and workgroups in a
 //     fixed order (deterministic for a given device), aggregates the group
