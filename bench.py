@@ -170,6 +170,44 @@ def bench_target_variants(kv, st, reps=20):
     return out
 
 
+def bench_retention(kv, st, reps=50):
+    """Selection alone and selection + compaction on the layer's fp32 mass,
+    with their algorithmic HBM bytes: select reads the scores of every row
+    and writes slot positions and scores (4 S + 8 budget bytes per row);
+    the gather reads and writes every kept K and V row (4 budget D bytes per
+    row each way)."""
+    w = st.w
+    rows = w.B * w.Hkv
+    sel_bytes = rows * (4 * w.S + 8 * w.budget)
+    gat_bytes = rows * 2 * (2 * w.budget * w.D * 2)
+
+    def t_ms(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    t_sel = t_ms(lambda: kv.evict_select(st.mass, w.n_sink, w.window, w.budget, out_pos=st.sp,
+                                         out_score=st.ss))
+    t_both = t_ms(lambda: kv.evict_select(st.mass, w.n_sink, w.window, w.budget, st.k, st.v,
+                                          out_pos=st.sp, out_score=st.ss, out_k=st.kc, out_v=st.vc))
+    gbs = lambda by, ms: by / (ms / 1e3) / 1e9
+    return {"rows": rows,
+            "select": {"ms": t_sel, "bytes": sel_bytes, "achieved": gbs(sel_bytes, t_sel),
+                       "unit": "GB/s", "frac": gbs(sel_bytes, t_sel) / HBM_PEAK_GBS},
+            "select_gather": {"ms": t_both, "bytes": sel_bytes + gat_bytes,
+                              "achieved": gbs(sel_bytes + gat_bytes, t_both), "unit": "GB/s",
+                              "frac": gbs(sel_bytes + gat_bytes, t_both) / HBM_PEAK_GBS},
+            "note": "8 rows of 4096 scores: launch- and latency-bound, not bandwidth-bound"}
+
+
 def decode_bytes_per_step(w, layers):
     """Algorithmic HBM bytes of one decode step over all layers: the whole
     bounded K/V cache read once, the appended K/V rows written, the exiting
@@ -180,6 +218,42 @@ def decode_bytes_per_step(w, layers):
     exit_copy = units * 2 * 2 * w.D * 2
     qo = w.B * layers * w.Hq * w.D * 2 * 2
     return cache + append + exit_copy + qo
+
+
+def time_prefix_retention(kv, w, sc, kp, vp, reps=3):
+    """Selection and selection + compaction of one layer's prefix (64 x 8
+    rows of 32768 MLP scores down to the budget): select reads every score
+    and writes positions and scores, the gather reads and writes every kept
+    K and V row."""
+    rows = w.B * w.Hkv
+    sel_bytes = rows * (4 * w.S + 8 * w.budget)
+    gat_bytes = rows * 2 * (2 * w.budget * w.D * 2)
+    outs = kv.evict_select(sc, w.n_sink, w.window, w.budget, kp, vp)
+
+    def t_ms(fn):
+        fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    t_sel = t_ms(lambda: kv.evict_select(sc, w.n_sink, w.window, w.budget, out_pos=outs[0],
+                                         out_score=outs[1]))
+    t_both = t_ms(lambda: kv.evict_select(sc, w.n_sink, w.window, w.budget, kp, vp, out_pos=outs[0],
+                                          out_score=outs[1], out_k=outs[2], out_v=outs[3]))
+    del outs
+    gbs = lambda by, ms: by / (ms / 1e3) / 1e9
+    return {"rows": rows, "seq_len": w.S, "budget": w.budget,
+            "select": {"ms": t_sel, "bytes": sel_bytes, "achieved": gbs(sel_bytes, t_sel),
+                       "unit": "GB/s", "frac": gbs(sel_bytes, t_sel) / HBM_PEAK_GBS},
+            "select_gather": {"ms": t_both, "bytes": sel_bytes + gat_bytes,
+                              "achieved": gbs(sel_bytes + gat_bytes, t_both), "unit": "GB/s",
+                              "frac": gbs(sel_bytes + gat_bytes, t_both) / HBM_PEAK_GBS}}
 
 
 def bench_decode(kv, steps, layers, seed=5):
@@ -196,6 +270,8 @@ def bench_decode(kv, steps, layers, seed=5):
         vp = synth.bf16(synth.normal((B, Hkv, S, D), ls * 3 + 2, dev, w.std))
         mlp = [t.to(dev) for t in synth.mlp_weights(Hkv, D, hidden, seed=ls)]
         sc = kv.score_mlp(kp, *mlp)
+        if layer == 0:
+            prefix_retention = time_prefix_retention(kv, w, sc, kp, vp)
         sp, ss, kc, vc = kv.evict_select(sc, w.n_sink, w.window, bud, kp, vp)
         del kp, vp, sc
         caches.append([kc, vc, sp, ss])
@@ -269,6 +345,7 @@ def bench_decode(kv, steps, layers, seed=5):
         "wall_s": wall, "bytes_per_step": by,
         "hbm": {"achieved": by * sps / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": by * sps / 1e9 / HBM_PEAK_GBS},
+        "prefix_retention": prefix_retention,
         "fused_decode_step": {"value": steps / (ms_fused / 1e3), "unit": "steps/s",
                               "ms_per_step": ms_fused / steps,
                               "hbm_frac": by * steps / (ms_fused / 1e3) / 1e9 / HBM_PEAK_GBS},
@@ -457,6 +534,7 @@ def main():
                     "select_gather_decode": {"ms": t_rest}},
     }
     out["target_variants"] = bench_target_variants(kv, st)
+    out["retention"] = bench_retention(kv, st)
     if not a.no_decode:
         log(f"decode: {a.decode_steps} steps x {a.decode_layers} layers")
         out["decode"] = bench_decode(kv, a.decode_steps, a.decode_layers)
