@@ -11,6 +11,8 @@
 //     order-preserving uint32 keys (NaN lowest, -0 == +0) and the k-th
 //     largest key is found by a 4-pass MSD radix select (8-bit digits,
 //     per-wave LDS histograms, one wave-parallel suffix scan per pass).
+//     Rows of 8K..32K eligible tokens hold their keys in registers (32 per
+//     thread) across the four passes; shorter and longer rows re-read them.
 //   * Ties at the threshold key go to the lowest positions: a block-wide
 //     scan over the row in position order counts equal keys, and a second
 //     scan gives every kept token its output slot, so the long-range slots
@@ -25,6 +27,8 @@ namespace {
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kVPT = 8;  // contiguous positions per thread per compaction chunk
+constexpr int kRegKeys = 32;       // eligible keys per thread held in registers (32768 per row)
+constexpr int kRegMin = 8 * 1024;  // rows longer than this keep their keys in registers
 
 // exclusive scan over the workgroup; returns the prefix, total in *total
 __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
@@ -102,14 +106,33 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   }
 
   // ---- radix select of the kk-th largest key ----
+  // Long rows (more than kRegMin eligible tokens, up to kRegKeys per
+  // thread) read their keys once into registers for all four passes;
+  // shorter rows, whose passes are latency-bound, re-read the scores.
+  const bool in_regs = n_e > kRegMin && n_e <= kRegKeys * kSelThreads;
+  uint32_t rk[kRegKeys];
+  if (in_regs) {
+#pragma unroll
+    for (int i = 0; i < kRegKeys; ++i) {
+      const int p = e_lo + tid + i * kSelThreads;
+      rk[i] = p < e_hi ? rank_key(sc[p]) : 0u;
+    }
+  }
   uint32_t prefix = 0, pmask = 0, rem = (uint32_t)kk;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
     for (int i = tid; i < kSelWaves * 256; i += kSelThreads) (&hist[0][0])[i] = 0u;
     __syncthreads();
-    for (int p = e_lo + tid; p < e_hi; p += kSelThreads) {
-      const uint32_t key = rank_key(sc[p]);
-      if ((key & pmask) == prefix) atomicAdd(&hist[wave][(key >> shift) & 255u], 1u);
+    if (in_regs) {
+#pragma unroll
+      for (int i = 0; i < kRegKeys; ++i)
+        if (tid + i * kSelThreads < n_e && (rk[i] & pmask) == prefix)
+          atomicAdd(&hist[wave][(rk[i] >> shift) & 255u], 1u);
+    } else {
+      for (int p = e_lo + tid; p < e_hi; p += kSelThreads) {
+        const uint32_t key = rank_key(sc[p]);
+        if ((key & pmask) == prefix) atomicAdd(&hist[wave][(key >> shift) & 255u], 1u);
+      }
     }
     __syncthreads();
     if (wave == 0) {
