@@ -32,6 +32,7 @@ import synth  # noqa: E402
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+FP32_VECTOR_PEAK_TFS = 157.3     # MI355X fp32 vector (counts packed FMA; one FMA per lane per cycle is half)
 
 # HBM bytes of one kvpop_future_attn_target call (transposed pass + merge) on
 # the Qwen3-4B layer workload, from two rocprofv3 --pmc runs (FETCH_SIZE, then
@@ -220,14 +221,18 @@ def decode_bytes_per_step(w, layers):
     return cache + append + exit_copy + qo
 
 
-def time_prefix_retention(kv, w, sc, kp, vp, reps=3):
-    """Selection and selection + compaction of one layer's prefix (64 x 8
-    rows of 32768 MLP scores down to the budget): select reads every score
-    and writes positions and scores, the gather reads and writes every kept
-    K and V row."""
+def time_prefix_retention(kv, w, kp, vp, mlp, reps=3):
+    """One-shot retention of one layer's prefix (64 x 8 rows of 32768 tokens
+    down to the budget): the MLP scorer over every prefix key (one FMA per
+    weight and key, fp32 on the vector ALU), selection (reads every score,
+    writes positions and scores) and selection + compaction (the gather also
+    reads and writes every kept K and V row)."""
     rows = w.B * w.Hkv
+    hidden = mlp[0].shape[1]
+    score_flops = 2 * rows * w.S * hidden * w.D
     sel_bytes = rows * (4 * w.S + 8 * w.budget)
     gat_bytes = rows * 2 * (2 * w.budget * w.D * 2)
+    sc = kv.score_mlp(kp, *mlp)
     outs = kv.evict_select(sc, w.n_sink, w.window, w.budget, kp, vp)
 
     def t_ms(fn):
@@ -242,13 +247,19 @@ def time_prefix_retention(kv, w, sc, kp, vp, reps=3):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps
 
+    t_score = t_ms(lambda: kv.score_mlp(kp, *mlp, out=sc))
     t_sel = t_ms(lambda: kv.evict_select(sc, w.n_sink, w.window, w.budget, out_pos=outs[0],
                                          out_score=outs[1]))
     t_both = t_ms(lambda: kv.evict_select(sc, w.n_sink, w.window, w.budget, kp, vp, out_pos=outs[0],
                                           out_score=outs[1], out_k=outs[2], out_v=outs[3]))
     del outs
     gbs = lambda by, ms: by / (ms / 1e3) / 1e9
+    tfl = score_flops / (t_score / 1e3) / 1e12
     return {"rows": rows, "seq_len": w.S, "budget": w.budget,
+            "score": {"ms": t_score, "flops": score_flops, "achieved": tfl, "unit": "TFLOP/s",
+                      "bound": "alu", "peak": FP32_VECTOR_PEAK_TFS,
+                      "frac": tfl / FP32_VECTOR_PEAK_TFS},
+            "score_select_gather_ms": t_score + t_both,
             "select": {"ms": t_sel, "bytes": sel_bytes, "achieved": gbs(sel_bytes, t_sel),
                        "unit": "GB/s", "frac": gbs(sel_bytes, t_sel) / HBM_PEAK_GBS},
             "select_gather": {"ms": t_both, "bytes": sel_bytes + gat_bytes,
@@ -269,9 +280,9 @@ def bench_decode(kv, steps, layers, seed=5):
         kp = synth.bf16(synth.normal((B, Hkv, S, D), ls * 3 + 1, dev, w.std))
         vp = synth.bf16(synth.normal((B, Hkv, S, D), ls * 3 + 2, dev, w.std))
         mlp = [t.to(dev) for t in synth.mlp_weights(Hkv, D, hidden, seed=ls)]
-        sc = kv.score_mlp(kp, *mlp)
         if layer == 0:
-            prefix_retention = time_prefix_retention(kv, w, sc, kp, vp)
+            prefix_retention = time_prefix_retention(kv, w, kp, vp, mlp)
+        sc = kv.score_mlp(kp, *mlp)
         sp, ss, kc, vc = kv.evict_select(sc, w.n_sink, w.window, bud, kp, vp)
         del kp, vp, sc
         caches.append([kc, vc, sp, ss])
@@ -332,10 +343,10 @@ def bench_decode(kv, steps, layers, seed=5):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1), time.perf_counter() - t0
 
-    # the decode steps continue one sequence: the fused calls take the
-    # positions after the two-call run
-    ms, wall = timed(one_step, S, "cache step + attention")
-    ms_fused, _ = timed(one_fused_step, S + steps, "fused decode step")
+    # the decode steps continue one sequence: the two-call run takes the
+    # positions after the fused run (kvpop_decode_step, the primary figure)
+    ms, wall = timed(one_fused_step, S, "fused decode step")
+    ms_two, _ = timed(one_step, S + steps, "cache step + attention")
     sps = steps / (ms / 1e3)
     by = decode_bytes_per_step(w, layers)
     att_bytes = B * Hkv * 2 * bud * D * 2 + B * Hq * D * 2 * 2
@@ -346,9 +357,11 @@ def bench_decode(kv, steps, layers, seed=5):
         "hbm": {"achieved": by * sps / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": by * sps / 1e9 / HBM_PEAK_GBS},
         "prefix_retention": prefix_retention,
-        "fused_decode_step": {"value": steps / (ms_fused / 1e3), "unit": "steps/s",
-                              "ms_per_step": ms_fused / steps,
-                              "hbm_frac": by * steps / (ms_fused / 1e3) / 1e9 / HBM_PEAK_GBS},
+        "entry_point": "kvpop_decode_step",
+        "two_calls": {"entry_points": "kvpop_cache_step + kvpop_decode_attend",
+                      "value": steps / (ms_two / 1e3), "unit": "steps/s",
+                      "ms_per_step": ms_two / steps,
+                      "hbm_frac": by * steps / (ms_two / 1e3) / 1e9 / HBM_PEAK_GBS},
         "attend_kernel": {"ms": t_att_ms, "bytes": att_bytes,
                           "achieved": att_bytes / (t_att_ms / 1e3) / 1e9, "unit": "GB/s",
                           "frac": att_bytes / (t_att_ms / 1e3) / 1e9 / HBM_PEAK_GBS},

@@ -13,10 +13,12 @@
 //   * App. C.1: the cache holds B = s + w + k entries per head.
 //
 // gfx950 mapping
-//   * The MLP of one token runs on one wave: lane j owns hidden units j,
-//     j+64, ...; W1 is staged through LDS with a padded row so the lane-
-//     varying reads are conflict free; the output layer is a fixed xor
-//     butterfly, so every kernel that scores a token produces the same bits.
+//   * The MLP runs on one wave: lane j owns hidden unit j with its W1 row
+//     in registers; the key's dwords are spread one per lane and handed to
+//     the wave by v_readlane, so each weight costs one FMA and no LDS
+//     access; the output layer is a fixed xor butterfly.  The prefix scorer
+//     and the decode step share this code, so a key scores the same bits in
+//     both.
 //   * The decode step of a (b, h) row is one 256-thread workgroup: every
 //     global read is issued first, one reduction finds the first empty slot
 //     and the worst kept token, one thread takes the decision, and the same
@@ -35,48 +37,60 @@ __device__ __forceinline__ float gelu_erf(float x) {
   return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
 }
 
-// Score of one key by one wave.  key: D floats in LDS; w1s: LDS copy of the
-// head's W1 with row stride D+1.  Returns the same value in every lane.
-__device__ __forceinline__ float mlp_wave(const float* key, const float* w1s, int D, int hidden,
-                                          const float* __restrict__ b1,
-                                          const float* __restrict__ w2, float b2, int lane) {
-  float part = 0.f;
-  for (int j = lane; j < hidden; j += 64) {
-    const float* wr = w1s + j * (D + 1);
-    float a = b1[j];
-    for (int cc = 0; cc < D; ++cc) a = fmaf(wr[cc], key[cc], a);
-    part = fmaf(w2[j], gelu_erf(a), part);
-  }
+// The headwise scorer as one wave holds it: lane j owns hidden unit j
+// (its W1 row, b1 and w2 entries); lanes j >= hidden own nothing.
+template <int D>
+struct ScorerLane {
+  float w[D];
+  float b, w2;
+  bool unit;
+};
+
+template <int D>
+__device__ __forceinline__ void load_scorer(ScorerLane<D>& sl, const float* __restrict__ w1,
+                                            const float* __restrict__ b1,
+                                            const float* __restrict__ w2, int h, int hidden,
+                                            int lane) {
+  sl.unit = lane < hidden;
+  const size_t j = (size_t)h * hidden + (sl.unit ? lane : 0);
+  const float* wr = w1 + j * D;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) part = part + __shfl_xor(part, off);
-  return part + b2;
+  for (int cc = 0; cc < D; ++cc) sl.w[cc] = wr[cc];
+  sl.b = b1[j];
+  sl.w2 = w2[j];
 }
 
-// LDS written by lanes of one wave becomes visible to the other lanes of the
-// same wave (no workgroup barrier: waves of a block walk different tokens).
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-__device__ __forceinline__ void stage_w1(float* w1s, const float* __restrict__ w1, int D,
-                                         int hidden) {
-  for (int e = threadIdx.x; e < hidden * D; e += blockDim.x) {
-    const int j = e / D, cc = e % D;
-    w1s[j * (D + 1) + cc] = w1[e];
+// This lane's term of one token's score: a_j = b1_j + sum_c W1[j][c] k_c as
+// one FMA chain in c order, then w2_j * GELU(a_j).  kdw: lane i holds dword
+// i of the bf16 key (elements 2i, 2i+1); v_readlane hands each dword to the
+// whole wave.  Every scorer in this library goes through this function and
+// wave_sum, so a key gets the same bits wherever it is scored.
+template <int D>
+__device__ __forceinline__ float scorer_term(const ScorerLane<D>& sl, uint32_t kdw) {
+  float a = sl.b;
+#pragma unroll
+  for (int c2 = 0; c2 < D / 2; ++c2) {
+    const uint32_t u = __builtin_amdgcn_readlane(kdw, c2);
+    a = fmaf(sl.w[2 * c2], __uint_as_float(u << 16), a);
+    a = fmaf(sl.w[2 * c2 + 1], __uint_as_float(u & 0xffff0000u), a);
   }
+  return sl.unit ? fmaf(sl.w2, gelu_erf(a), 0.f) : 0.f;
+}
+
+// Sum over the wave by a fixed xor butterfly (every lane gets the same bits).
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = x + __shfl_xor(x, off);
+  return x;
 }
 
 // Pool slots each thread scans per pass (loaded together, then reduced).
 constexpr int kScanPer = 16;
-// W1 elements per thread held in registers while staging (hidden * D <= 64 * 128).
-constexpr int kW1Per = 64 * 128 / kThreads;
-
 // The bounded-cache decode step of one (b, h) row by one 256-thread
-// workgroup.  smem: hidden * (D+1) + D floats of LDS when w1 is given.
+// workgroup; wave 0 holds the scorer when w1 is given.
+template <int D>
 __device__ __forceinline__ void cache_step_row(
-    long row, float* smem, int D, int n_sink, int window, int budget, int delay, int pos_q,
+    long row, int n_sink, int window, int budget, int delay, int pos_q,
     const bf16_t* __restrict__ k_new, const bf16_t* __restrict__ v_new,
     const float* __restrict__ w1, const float* __restrict__ b1, const float* __restrict__ w2,
     const float* __restrict__ b2, int hidden, const float* __restrict__ scores_r,
@@ -95,7 +109,7 @@ __device__ __forceinline__ void cache_step_row(
   float* ss = slot_score + row * budget;
   bf16_t* kr = kc + row * (size_t)budget * D;
   bf16_t* vr = vc + row * (size_t)budget * D;
-  const int cpr = D / 8;
+  constexpr int cpr = D / 8;
   const int q = pos_q;
   const int u = q - window;               // the token leaving the window
   const bool exiting = u >= n_sink;
@@ -107,36 +121,43 @@ __device__ __forceinline__ void cache_step_row(
   const bool use_mlp = scoring && w1 != nullptr;
 
   // ---- every global read first: one memory latency for the whole step ----
-  // rows: thread i < cpr owns 16-byte chunk i of K, cpr <= i < 2 cpr of V;
-  // the exiting row is read before the same thread overwrites its slot
+  // The loads are unconditional or under wave-uniform conditions (indices
+  // clamped into the row), so they all go out before the first wait.
+  // Rows: thread i < cpr owns 16-byte chunk i of K, cpr <= i < 2 cpr of V
+  // (the other threads load a duplicate and store nothing); the exiting
+  // row is read before the same thread overwrites its slot.  ring_u is a
+  // ring slot even when no token exits.
   const bool row_thread = tid < 2 * cpr;
-  const bool is_k = tid < cpr;
-  const int chunk = is_k ? tid : tid - cpr;
-  uint4 old_row = make_uint4(0, 0, 0, 0), new_row = make_uint4(0, 0, 0, 0);
-  if (row_thread) {
-    if (exiting) old_row = ldg16((is_k ? kr : vr) + (size_t)ring_u * D + chunk * 8);
-    new_row = ldg16((is_k ? k_new : v_new) + row * D + chunk * 8);
-  }
-  int pos_u = 0;
-  float score_u = 0.f, given = 0.f;
-  if (tid == 0) {
-    if (exiting) {
-      pos_u = sp[ring_u];
-      score_u = ss[ring_u];
-    }
-    if (scoring && !use_mlp) given = scores_r[row];
-  }
-  float w1v[kW1Per];
-  float keyv = 0.f;
-  if (use_mlp) {
-    const float* w1h = w1 + (size_t)h * hidden * D;
+  const int rt = tid % (2 * cpr);
+  const bool is_k = rt < cpr;
+  const int chunk = is_k ? rt : rt - cpr;
+  const uint4 old_row = ldg16((is_k ? kr : vr) + (size_t)ring_u * D + chunk * 8);
+  const uint4 new_row = ldg16((is_k ? k_new : v_new) + row * D + chunk * 8);
+  const int pos_u = sp[ring_u];
+  const float score_u = ss[ring_u];
+  const float given = scoring && !use_mlp ? scores_r[row] : 0.f;
+
+  // first pass of the long-range scan (up to kThreads * kScanPer slots)
+  const bool scan = exiting && kk > 0;
+  int pv[kScanPer];
+  float sv[kScanPer];
+  if (scan) {
 #pragma unroll
-    for (int i = 0; i < kW1Per; ++i) {
-      const int e = tid + i * kThreads;
-      w1v[i] = e < hidden * D ? w1h[e] : 0.f;
+    for (int i = 0; i < kScanPer; ++i) {
+      const int j = min(tid + i * kThreads, kk - 1);
+      pv[i] = sp[n_sink + j];
+      sv[i] = ss[n_sink + j];
     }
+  }
+
+  // wave 0 holds the scorer (its loads go out last: they are needed last)
+  const bool wave0 = __builtin_amdgcn_readfirstlane(wave) == 0;
+  ScorerLane<D> sl;
+  uint32_t kdw = 0;
+  if (use_mlp && wave0) {
+    load_scorer<D>(sl, w1, b1, w2, h, hidden, lane);
     const bf16_t* ksrc = r == q ? k_new + row * D : kr + (size_t)rslot * D;
-    if (tid < D) keyv = __uint_as_float((uint32_t)ksrc[tid] << 16);
+    kdw = reinterpret_cast<const uint32_t*>(ksrc)[lane % (D / 2)];
   }
 
   // ---- (a) scan of the long-range slots: first empty slot, worst kept token
@@ -144,24 +165,24 @@ __device__ __forceinline__ void cache_step_row(
   uint32_t wkey = 0;
   if (exiting) {
     for (int base = 0; base < kk; base += kThreads * kScanPer) {
-      int pv[kScanPer];
-      float sv[kScanPer];
+      if (base > 0) {  // rows longer than one pass
 #pragma unroll
-      for (int i = 0; i < kScanPer; ++i) {
-        const int j = base + tid + i * kThreads;
-        pv[i] = j < kk ? sp[n_sink + j] : -2;
-        sv[i] = j < kk ? ss[n_sink + j] : 0.f;
+        for (int i = 0; i < kScanPer; ++i) {
+          const int j = min(base + tid + i * kThreads, kk - 1);
+          pv[i] = sp[n_sink + j];
+          sv[i] = ss[n_sink + j];
+        }
       }
 #pragma unroll
       for (int i = 0; i < kScanPer; ++i) {
-        const int j = n_sink + base + tid + i * kThreads;
-        if (pv[i] == -2) continue;
+        const int j = base + tid + i * kThreads;
+        if (j >= kk) continue;
         if (pv[i] < 0) {
-          first_empty = min(first_empty, j);
+          first_empty = min(first_empty, n_sink + j);
         } else {
           const uint32_t key = rank_key(sv[i]);
           if (worst < 0 || key < wkey || (key == wkey && pv[i] > wpos)) {
-            worst = j;
+            worst = n_sink + j;
             wkey = key;
             wpos = pv[i];
           }
@@ -188,16 +209,6 @@ __device__ __forceinline__ void cache_step_row(
       red_key[wave] = wkey;
       red_pos[wave] = wpos;
     }
-  }
-  float* w1s = smem;                         // hidden x (D+1)
-  float* key = smem + (size_t)hidden * (D + 1);
-  if (use_mlp) {
-#pragma unroll
-    for (int i = 0; i < kW1Per; ++i) {
-      const int e = tid + i * kThreads;
-      if (e < hidden * D) w1s[(e / D) * (D + 1) + e % D] = w1v[i];
-    }
-    if (tid < D) key[tid] = keyv;
   }
   __syncthreads();
 
@@ -243,8 +254,7 @@ __device__ __forceinline__ void cache_step_row(
   // ---- (c) delayed scoring of token r = q - delay ----
   if (scoring && wave == 0) {
     float sc = given;
-    if (use_mlp)
-      sc = mlp_wave(key, w1s, D, hidden, b1 + (size_t)h * hidden, w2 + (size_t)h * hidden, b2[h], lane);
+    if (use_mlp) sc = wave_sum(scorer_term<D>(sl, kdw)) + b2[h];
     if (lane == 0) ss[rslot] = sc;  // after the NaN marker when r == q (same thread)
   }
 }

@@ -27,10 +27,9 @@ __global__ __launch_bounds__(decdev::kThreads) void decode_step_kernel(
     void* __restrict__ o_out, int o_bf16, float* __restrict__ lse_out, int Hq, int Hkv, int sps,
     float c) {
   static_assert(csdev::kThreads == decdev::kThreads, "one workgroup shape for both phases");
-  extern __shared__ float smem[];
   const int row = blockIdx.x;  // b * Hkv + h
-  csdev::cache_step_row(row, smem, D, n_sink, window, budget, delay, pos_q, k_new, v_new, w1, b1,
-                        w2, b2, hidden, scores_r, kc, vc, slot_pos, slot_score, Hkv);
+  csdev::cache_step_row<D>(row, n_sink, window, budget, delay, pos_q, k_new, v_new, w1, b1, w2,
+                           b2, hidden, scores_r, kc, vc, slot_pos, slot_score, Hkv);
   // The step's writes (moved row, new row, positions, scores) are
   // performed before the barrier (workgroup-scope release), and every wave
   // of the workgroup reads them through the one L1 of its CU, so the
@@ -59,7 +58,6 @@ hipError_t launch_decode_step(const AttnShape& s, int n_sink, int window, int de
   }
   const int G = s.Hq / s.Hkv;
   const float c = s.scale * kLog2e;
-  const size_t smem = w1 ? sizeof(float) * ((size_t)hidden * (s.D + 1) + s.D) : 0;
   dim3 grid(s.B * s.Hkv), block(decdev::kThreads);
   auto* kn = (const bf16_t*)k_new;
   auto* vn = (const bf16_t*)v_new;
@@ -67,7 +65,7 @@ hipError_t launch_decode_step(const AttnShape& s, int n_sink, int window, int de
   auto* vv = (bf16_t*)vc;
   auto* qq = (const bf16_t*)q;
 #define KVPOP_STEP(DD, GG)                                                                          \
-  hipLaunchKernelGGL((decode_step_kernel<DD, GG>), grid, block, smem, st, n_sink, window, s.S, delay, \
+  hipLaunchKernelGGL((decode_step_kernel<DD, GG>), grid, block, 0, st, n_sink, window, s.S, delay, \
                      pos_q, kn, vn, w1, b1, w2, b2, hidden, scores_r, kk, vv, slot_pos, slot_score,  \
                      qq, o, o_bf16, lse, s.Hq, s.Hkv, p.slots_per_split, c)
   const int gc = G >= 8 ? 8 : G;
