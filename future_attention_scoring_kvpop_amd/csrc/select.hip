@@ -10,14 +10,21 @@
 //   * One 1024-thread workgroup per (b, h) row.  Scores are mapped to
 //     order-preserving uint32 keys (NaN lowest, -0 == +0) and the k-th
 //     largest key is found by a 4-pass MSD radix select (8-bit digits,
-//     per-wave LDS histograms, one wave-parallel suffix scan per pass).
-//     Rows of 8K..32K eligible tokens hold their keys in registers (32 per
-//     thread) across the four passes; shorter and longer rows re-read them.
-//   * Ties at the threshold key go to the lowest positions: a block-wide
-//     scan over the row in position order counts equal keys, and a second
-//     scan gives every kept token its output slot, so the long-range slots
-//     come out in ascending position with no sort.
+//     per-wave LDS histograms -- eight per wave in the first pass of rows
+//     of 16K+ tokens, where clustered keys would serialise the atomics --
+//     and one wave-parallel suffix scan per pass).
+//   * Rows of up to 32K eligible tokens are read once, coalesced: each
+//     wave keeps the keys of a contiguous run of 64 x (4..32) positions in
+//     registers (slots past the row hold key 0, which is never kept).
+//     Ties at the threshold key go to the lowest positions; since the kept
+//     equal keys fill up in position order, one scan of the waves' packed
+//     (equal, above) counts plus ballots within each wave give every kept
+//     token its output slot, so the long-range slots come out in ascending
+//     position with no sort.  Longer rows are streamed from memory, with two
+//     block scans per 8K-position chunk.
 //   * The gather is a separate, fully coalesced 16-byte-per-lane copy.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -27,8 +34,6 @@ namespace {
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kVPT = 8;  // contiguous positions per thread per compaction chunk
-constexpr int kRegKeys = 32;       // eligible keys per thread held in registers (32768 per row)
-constexpr int kRegMin = 8 * 1024;  // rows longer than this keep their keys in registers
 
 // exclusive scan over the workgroup; returns the prefix, total in *total
 __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
@@ -57,10 +62,70 @@ __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t* t
   return before + x - v;
 }
 
+// The first radix pass counts into kSelCopies histograms per wave (lane l
+// into copy l % kSelCopies): its digit is a float key's sign and exponent,
+// where scores cluster, and lanes of one atomic that hit one LDS address
+// serialise.  Later passes see only the keys under the chosen prefix and
+// use one histogram per wave.
+constexpr int kSelCopies = 8;
+constexpr int kSelHists = kSelWaves * kSelCopies;
+
+// Every thread: sums the kSelHists copies of each bin into the first
+// kSelThreads / 256 rows of part (4 partial sums per bin), then folds them
+// into row 0..kSelWaves-1 form for radix_pick: row g < 4 holds partial g,
+// rows 4..kSelWaves-1 are zeroed.
+__device__ __forceinline__ void fold_copies(uint32_t (*hist)[256]) {
+  const int tid = threadIdx.x, bin = tid & 255, grp = tid >> 8;
+  uint32_t c = 0;
+  for (int k = grp; k < kSelHists; k += kSelThreads / 256) c += hist[k][bin];
+  __syncthreads();
+  hist[grp][bin] = c;
+  for (int k = kSelThreads / 256 + grp; k < kSelWaves; k += kSelThreads / 256) hist[k][bin] = 0u;
+}
+
+// Wave 0 turns the per-wave digit histograms of one radix pass into the
+// digit of the rem-th largest key (higher digits first) and the rank of
+// that key among the keys with this digit.
+__device__ __forceinline__ void radix_pick(const uint32_t (*hist)[256], uint32_t rem,
+                                           uint32_t* sh_digit, uint32_t* sh_rem) {
+  const int lane = threadIdx.x & 63;
+  uint32_t cnt[4], tot = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t c = 0;
+    for (int w = 0; w < kSelWaves; ++w) c += hist[w][4 * lane + i];
+    cnt[i] = c;
+    tot += c;
+  }
+  // inclusive suffix sum over lanes
+  uint32_t x = tot;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_down(x, off);
+    if (lane + off < 64) x += y;
+  }
+  const uint32_t above = x - tot;
+  if (above < rem && rem <= x) {
+    uint32_t cum = above;
+    for (int i = 3; i >= 0; --i) {
+      if (cum + cnt[i] >= rem) {
+        *sh_digit = 4 * lane + i;
+        *sh_rem = rem - cum;
+        break;
+      }
+      cum += cnt[i];
+    }
+  }
+}
+
+// VPT > 0: rows of at most VPT * kSelThreads eligible tokens, held in
+// registers (VPT keys per lane) for the radix passes and the compaction.
+// VPT == 0: longer rows, streamed from memory in chunks.
+template <int VPT>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const float* __restrict__ scores, int32_t* __restrict__ slot_pos,
     float* __restrict__ slot_score, int S, int n_sink, int window, int budget) {
-  __shared__ uint32_t hist[kSelWaves][256];
+  __shared__ uint32_t hist[kSelHists][256];
   __shared__ uint32_t wsum[2 * kSelWaves];
   __shared__ uint32_t sh_digit, sh_rem;
 
@@ -68,7 +133,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   const float* sc = scores + row * S;
   int32_t* sp = slot_pos + row * budget;
   float* ss = slot_score ? slot_score + row * budget : nullptr;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, wave = tid >> 6;
   const int kk = budget - n_sink - window;
   const int e_lo = n_sink;
   const int e_hi = max(S - window, n_sink);
@@ -105,112 +170,145 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     return;
   }
 
-  // ---- radix select of the kk-th largest key ----
-  // Long rows (more than kRegMin eligible tokens, up to kRegKeys per
-  // thread) read their keys once into registers for all four passes;
-  // shorter rows, whose passes are latency-bound, re-read the scores.
-  const bool in_regs = n_e > kRegMin && n_e <= kRegKeys * kSelThreads;
-  uint32_t rk[kRegKeys];
-  if (in_regs) {
+  if constexpr (VPT > 0) {
+    // wave w owns the 64*VPT positions from e_lo + 64*VPT*w; its lane l
+    // holds position e_lo + 64*(VPT*w + i) + l in slot i (coalesced loads)
+    const int lane = tid & 63;
+    const int p0 = e_lo + 64 * VPT * wave + lane;
+    // Slots past the row get key 0 (the key of NaN): they rank with the
+    // lowest tokens and come after every real position, so with kk < n_e
+    // none of them is ever kept and the counts stay consistent.
+    uint32_t kv[VPT];
 #pragma unroll
-    for (int i = 0; i < kRegKeys; ++i) {
-      const int p = e_lo + tid + i * kSelThreads;
-      rk[i] = p < e_hi ? rank_key(sc[p]) : 0u;
+    for (int i = 0; i < VPT; ++i) {
+      const int p = p0 + 64 * i;
+      const uint32_t key = rank_key(sc[min(p, e_hi - 1)]);
+      kv[i] = p < e_hi ? key : 0u;
     }
-  }
-  uint32_t prefix = 0, pmask = 0, rem = (uint32_t)kk;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = tid; i < kSelWaves * 256; i += kSelThreads) (&hist[0][0])[i] = 0u;
-    __syncthreads();
-    if (in_regs) {
+    // first-pass histogram copies pay off once a lane holds many keys
+    constexpr int NC = VPT >= 16 ? kSelCopies : 1;
+    for (int i = tid; i < kSelWaves * NC * 64; i += kSelThreads)
+      reinterpret_cast<uint4*>(&hist[0][0])[i] = make_uint4(0, 0, 0, 0);
+
+    // ---- radix select of the kk-th largest key ----
+    uint32_t prefix = 0, pmask = 0, rem = (uint32_t)kk;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      if (pass > 0)
+        for (int i = tid; i < kSelWaves * 256; i += kSelThreads) (&hist[0][0])[i] = 0u;
+      __syncthreads();
+      uint32_t* h = hist[pass == 0 ? wave * NC + lane % NC : wave];
 #pragma unroll
-      for (int i = 0; i < kRegKeys; ++i)
-        if (tid + i * kSelThreads < n_e && (rk[i] & pmask) == prefix)
-          atomicAdd(&hist[wave][(rk[i] >> shift) & 255u], 1u);
-    } else {
+      for (int i = 0; i < VPT; ++i)
+        if ((kv[i] & pmask) == prefix) atomicAdd(&h[(kv[i] >> shift) & 255u], 1u);
+      __syncthreads();
+      if (NC > 1 && pass == 0) {
+        fold_copies(hist);
+        __syncthreads();
+      }
+      if (wave == 0) radix_pick(hist, rem, &sh_digit, &sh_rem);
+      __syncthreads();
+      prefix |= sh_digit << shift;
+      pmask |= 255u << shift;
+      rem = sh_rem;
+      __syncthreads();
+    }
+    const uint32_t T = prefix;     // key of the kk-th best token
+    const uint32_t need_eq = rem;  // tokens with key == T to keep (lowest positions)
+
+    // ---- compaction in position order: tokens above T, and the first
+    // need_eq tokens equal to T.  Counts before a wave come from one scan of
+    // the waves' packed (equal, above) totals; within a wave, ballots order
+    // the lanes; before any position, min(equal so far, need_eq) of the
+    // equal tokens were kept. ----
+    const unsigned long long below = (1ull << lane) - 1ull;
+    uint32_t w_gt = 0, w_eq = 0;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      w_gt += __popcll(__ballot(kv[i] > T));
+      w_eq += __popcll(__ballot(kv[i] == T));
+    }
+    if (lane == 0) wsum[wave] = (w_eq << 16) | w_gt;
+    __syncthreads();
+    uint32_t pre = 0;
+    for (int w = 0; w < wave; ++w) pre += wsum[w];
+    uint32_t eq_run = pre >> 16;
+    uint32_t out = n_sink + (pre & 0xffffu) + min(eq_run, need_eq);
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int p = p0 + 64 * i;
+      const bool eq = kv[i] == T;
+      const unsigned long long em = __ballot(eq);
+      const bool keep = kv[i] > T || (eq && eq_run + __popcll(em & below) < need_eq);
+      const unsigned long long km = __ballot(keep);
+      const uint32_t o = out + __popcll(km & below);
+      if (keep && o < (uint32_t)(n_sink + kk)) {
+        sp[o] = p;
+        if (ss) ss[o] = sc[p];  // the score's own bits (keys merge -0/+0 and NaNs)
+      }
+      out += __popcll(km);
+      eq_run += __popcll(em);
+    }
+  } else {
+    // ---- radix select of the kk-th largest key, re-reading the scores ----
+    uint32_t prefix = 0, pmask = 0, rem = (uint32_t)kk;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      for (int i = tid; i < kSelWaves * 256; i += kSelThreads) (&hist[0][0])[i] = 0u;
+      __syncthreads();
       for (int p = e_lo + tid; p < e_hi; p += kSelThreads) {
         const uint32_t key = rank_key(sc[p]);
         if ((key & pmask) == prefix) atomicAdd(&hist[wave][(key >> shift) & 255u], 1u);
       }
+      __syncthreads();
+      if (wave == 0) radix_pick(hist, rem, &sh_digit, &sh_rem);
+      __syncthreads();
+      prefix |= sh_digit << shift;
+      pmask |= 255u << shift;
+      rem = sh_rem;
+      __syncthreads();
     }
-    __syncthreads();
-    if (wave == 0) {
-      uint32_t cnt[4], tot = 0;
+    const uint32_t T = prefix;
+    const uint32_t need_eq = rem;
+
+    // ---- compaction in position order, chunk by chunk ----
+    uint32_t eq_run = 0, kept_run = 0, total;
+    for (int base = e_lo; base < e_hi; base += kSelThreads * kVPT) {
+      const int p0 = base + tid * kVPT;
+      uint32_t keys[kVPT];
+      uint32_t n_gt = 0, n_eq = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t c = 0;
-        for (int w = 0; w < kSelWaves; ++w) c += hist[w][4 * lane + i];
-        cnt[i] = c;
-        tot += c;
+      for (int i = 0; i < kVPT; ++i) {
+        const int p = p0 + i;
+        keys[i] = p < e_hi ? rank_key(sc[p]) : 0u;
+        const bool in = p < e_hi;
+        n_gt += (in && keys[i] > T) ? 1u : 0u;
+        n_eq += (in && keys[i] == T) ? 1u : 0u;
       }
-      // inclusive suffix sum over lanes (higher digits first)
-      uint32_t x = tot;
+      const uint32_t eq_pre = eq_run + block_exclusive_scan(n_eq, wsum, &total);
+      const uint32_t eq_tot = total;
+      const uint32_t take = eq_pre >= need_eq ? 0u : min(n_eq, need_eq - eq_pre);
+      const uint32_t kept_pre = kept_run + block_exclusive_scan(n_gt + take, wsum, &total);
+      uint32_t out = n_sink + kept_pre, e = eq_pre;
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_down(x, off);
-        if (lane + off < 64) x += y;
-      }
-      const uint32_t above = x - tot;
-      if (above < rem && rem <= x) {
-        uint32_t cum = above;
-        for (int i = 3; i >= 0; --i) {
-          if (cum + cnt[i] >= rem) {
-            sh_digit = 4 * lane + i;
-            sh_rem = rem - cum;
-            break;
-          }
-          cum += cnt[i];
+      for (int i = 0; i < kVPT; ++i) {
+        const int p = p0 + i;
+        if (p >= e_hi) break;
+        bool keep = keys[i] > T;
+        if (keys[i] == T) {
+          keep = e < need_eq;
+          ++e;
+        }
+        if (keep && out < (uint32_t)(n_sink + kk)) {
+          sp[out] = p;
+          if (ss) ss[out] = sc[p];
+          ++out;
         }
       }
+      eq_run += eq_tot;
+      kept_run += total;
     }
-    __syncthreads();
-    prefix |= sh_digit << shift;
-    pmask |= 255u << shift;
-    rem = sh_rem;
-    __syncthreads();
   }
-  const uint32_t T = prefix;        // key of the kk-th best token
-  const uint32_t need_eq = rem;     // tokens with key == T to keep (lowest positions)
-
-  // ---- compaction in position order ----
-  uint32_t eq_run = 0, kept_run = 0, total;
-  for (int base = e_lo; base < e_hi; base += kSelThreads * kVPT) {
-    const int p0 = base + tid * kVPT;
-    uint32_t keys[kVPT];
-    uint32_t n_gt = 0, n_eq = 0;
-#pragma unroll
-    for (int i = 0; i < kVPT; ++i) {
-      const int p = p0 + i;
-      keys[i] = p < e_hi ? rank_key(sc[p]) : 0u;
-      const bool in = p < e_hi;
-      n_gt += (in && keys[i] > T) ? 1u : 0u;
-      n_eq += (in && keys[i] == T) ? 1u : 0u;
-    }
-    const uint32_t eq_pre = eq_run + block_exclusive_scan(n_eq, wsum, &total);
-    const uint32_t eq_tot = total;
-    const uint32_t take = eq_pre >= need_eq ? 0u : min(n_eq, need_eq - eq_pre);
-    const uint32_t kept_pre = kept_run + block_exclusive_scan(n_gt + take, wsum, &total);
-    uint32_t out = n_sink + kept_pre, e = eq_pre;
-#pragma unroll
-    for (int i = 0; i < kVPT; ++i) {
-      const int p = p0 + i;
-      if (p >= e_hi) break;
-      bool keep = keys[i] > T;
-      if (keys[i] == T) {
-        keep = e < need_eq;
-        ++e;
-      }
-      if (keep && out < (uint32_t)(n_sink + kk)) {
-        sp[out] = p;
-        if (ss) ss[out] = sc[p];
-        ++out;
-      }
-    }
-    eq_run += eq_tot;
-    kept_run += total;
-  }
-  (void)lane;
 }
 
 // One thread per 16-byte chunk of one cache row, for K and V.
@@ -242,8 +340,21 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
 hipError_t launch_select(int B, int Hkv, int S, int n_sink, int window, int budget,
                          const float* scores, int32_t* slot_pos, float* slot_score,
                          hipStream_t st) {
-  hipLaunchKernelGGL(select_kernel, dim3(B * Hkv), dim3(kSelThreads), 0, st, scores, slot_pos,
-                     slot_score, S, n_sink, window, budget);
+  const int n_e = std::max(S - window, n_sink) - n_sink;
+#define KVPOP_SEL(V)                                                                            \
+  hipLaunchKernelGGL(select_kernel<V>, dim3(B * Hkv), dim3(kSelThreads), 0, st, scores, slot_pos, \
+                     slot_score, S, n_sink, window, budget)
+  if (n_e <= 4 * kSelThreads)
+    KVPOP_SEL(4);
+  else if (n_e <= 8 * kSelThreads)
+    KVPOP_SEL(8);
+  else if (n_e <= 16 * kSelThreads)
+    KVPOP_SEL(16);
+  else if (n_e <= 32 * kSelThreads)
+    KVPOP_SEL(32);
+  else
+    KVPOP_SEL(0);
+#undef KVPOP_SEL
   return hipGetLastError();
 }
 

@@ -60,16 +60,36 @@ def test_decode_workload_shape_and_empty_rows(kv):
     assert not f32(o)[3, 8:12].any() and np.all(f32(lse)[3, 8:12] == -np.inf)
 
 
-def test_score_mlp_parity(kv):
-    B, Hkv, n, D, hidden = 2, 8, 700, 128, 64
-    keys = synth.bf16(synth.normal((B, Hkv, n, D), 3, std=0.5))
-    w1, b1, w2, b2 = synth.mlp_weights(Hkv, D, hidden, seed=4)
+@pytest.mark.parametrize("B,Hkv,n,D,hidden", [(2, 8, 700, 128, 64), (3, 2, 1001, 64, 40),
+                                              (1, 3, 5, 128, 1), (2, 4, 4099, 128, 17),
+                                              (1, 1, 1, 64, 64)])
+def test_score_mlp_parity(kv, B, Hkv, n, D, hidden):
+    """Every token against the oracle: ragged runs per wave, hidden < 64
+    (lanes without a unit), D = 64 and a single token."""
+    keys = synth.bf16(synth.normal((B, Hkv, n, D), 3 + n, std=0.5))
+    w1, b1, w2, b2 = synth.mlp_weights(Hkv, D, hidden, seed=4 + hidden)
     b1 = b1 + 0.1
     b2 = b2 - 0.3
     sc = kv.score_mlp(keys.cuda(), w1.cuda(), b1.cuda(), w2.cuda(), b2.cuda())
     torch.cuda.synchronize()
     ref = oracle.mlp_score(f32(keys), w1.numpy(), b1.numpy(), w2.numpy(), b2.numpy())
     assert_close(f32(sc), ref, MLP_ATOL, MLP_RTOL, "mlp")
+
+
+def test_score_mlp_decode_prefix_sampled(kv):
+    """The decode workload's prefix at full size (64 x 8 x 32768 keys, runs
+    of 512 tokens per wave): sampled tokens of every row against the oracle,
+    including the first and last token of each row and of a run."""
+    w = synth.DECODE
+    keys = synth.bf16(synth.normal((w.B, w.Hkv, w.S, w.D), 12, device="cuda", std=w.std))
+    mlp = [t.cuda() for t in synth.mlp_weights(w.Hkv, w.D, w.extra["hidden"], seed=13)]
+    sc = kv.score_mlp(keys, *mlp)
+    torch.cuda.synchronize()
+    r = np.random.default_rng(14)
+    toks = np.unique(np.concatenate([[0, 511, 512, w.S - 1], r.integers(0, w.S, 28)]))
+    got = f32(sc[:, :, toks])
+    ref = oracle.mlp_score(f32(keys[:, :, toks]), *(t.cpu().numpy() for t in mlp))
+    assert_close(got, ref, MLP_ATOL, MLP_RTOL, "mlp prefix")
 
 
 def _prefix_state(kv, B, Hkv, S0, D, s, w, budget, seed):

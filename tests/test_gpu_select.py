@@ -61,9 +61,12 @@ def test_decode_prefix_shape(kv, kind):
     (1, 4, 16, 64), (3, 2, 4, 8), (20, 4, 16, 64), (100, 0, 0, 10), (100, 5, 0, 5),
     (100, 0, 7, 7), (5000, 4, 128, 132), (9000, 4, 1, 8200), (8193, 1, 1, 8192),
     (70000, 4, 256, 10000), (33028, 4, 256, 4096), (33029, 4, 256, 4096),
-    (8452, 4, 256, 1000), (8453, 4, 256, 1000)])
+    (8452, 4, 256, 1000), (8453, 4, 256, 1000), (4228, 4, 128, 1000), (4229, 4, 128, 1000),
+    (16644, 4, 256, 2000), (16645, 4, 256, 2000)])
 def test_edges(kv, S, s, w, budget):
-    for kind in ("normal", "ties", "special"):
+    # eligible counts on both sides of each register-path size (4K, 8K, 16K,
+    # 32K per row) and beyond it; 'nan' and 'const' make every key tie
+    for kind in ("normal", "ties", "special", "nan", "const"):
         scores = synth.scores((2, 3, S), seed=S + budget, kind=kind)
         _compare(kv, scores, s, w, budget, D=128 if S < 10000 else 0, seed=S)
 
