@@ -209,6 +209,81 @@ def bench_retention(kv, st, reps=50):
             "note": "8 rows of 4096 scores: launch- and latency-bound, not bandwidth-bound"}
 
 
+def bench_prefill(kv, w, layers=None, reps=1, seed=None):
+    """The target pipeline on a long-context workload: per layer the causal
+    LSE pass, the transposed future-attention pass (SUM over the group) and
+    retention + compaction of K/V to the budget, over every layer's own
+    resident inputs (generated before the timed region, one seed per layer:
+    3000 + l for the skewed workload, 4000 + l for the 36-layer prefill).  Each pass is timed by its own events; after one
+    untimed warm-up layer, `reps` passes over all layers are timed.
+    keys/s = layers * B * Hkv * S / (time of one pass over the layers)."""
+    dev = torch.device("cuda")
+    layers = layers or w.layers
+    base = seed if seed is not None else (4000 if w.layers > 1 else 3000)
+    ins = [synth.attention_inputs(w, seed=base + l, device=dev) for l in range(layers)]
+    d = kv.dims(w.B, w.Hq, w.Hkv, w.S, w.D)
+    lse = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device=dev)
+    mass = torch.empty((w.B, w.Hkv, w.S), dtype=torch.float32, device=dev)
+    tws = torch.empty(kv.workspace_bytes(kv.OP_FUTURE_TARGET, d, w.window), dtype=torch.uint8,
+                      device=dev)
+    fws = torch.empty(max(kv.workspace_bytes(kv.OP_FWD_LSE, d), 16), dtype=torch.uint8, device=dev)
+    sp = torch.empty((w.B, w.Hkv, w.budget), dtype=torch.int32, device=dev)
+    ss = torch.empty((w.B, w.Hkv, w.budget), dtype=torch.float32, device=dev)
+    kc = torch.empty((w.B, w.Hkv, w.budget, w.D), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+
+    def layer(i, ev=None):
+        q, k, v = ins[i]
+        if ev:
+            ev[0].record()
+        kv.fwd_lse(q, k, out=lse, workspace=fws)
+        if ev:
+            ev[1].record()
+        kv.future_attn_target(q, k, lse, w.window, agg="sum", out=mass, workspace=tws)
+        if ev:
+            ev[2].record()
+        kv.evict_select(mass, w.n_sink, w.window, w.budget, k, v, out_pos=sp, out_score=ss,
+                        out_k=kc, out_v=vc)
+        if ev:
+            ev[3].record()
+
+    layer(0)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps * layers)]
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for r in range(reps):
+        for i in range(layers):
+            layer(i, evs[r * layers + i])
+    b.record()
+    torch.cuda.synchronize()
+    n = reps * layers
+    ms_pass = a.elapsed_time(b) / reps
+    t_fwd = sum(e[0].elapsed_time(e[1]) for e in evs) / n
+    t_tr = sum(e[1].elapsed_time(e[2]) for e in evs) / n
+    t_sel = sum(e[2].elapsed_time(e[3]) for e in evs) / n
+    f_fwd, f_tr = target_flops(w)
+    rows = w.B * w.Hkv
+    sg_bytes = rows * (4 * w.S + 8 * w.budget) + rows * 2 * (2 * w.budget * w.D * 2)
+    tf = lambda f, ms: f / (ms / 1e3) / 1e12
+    keys = layers * w.B * w.Hkv * w.S
+    out = {"workload": w.name, "batch": w.B, "seq_len": w.S, "layers": layers, "window": w.window,
+           "budget": w.budget, "reps": reps, "ms_per_pass": ms_pass,
+           "keys_per_s": keys / (ms_pass / 1e3),
+           "per_layer_ms": {"fwd_lse": t_fwd, "future_attn_target": t_tr, "select_gather": t_sel},
+           "fwd_lse": {"flops": f_fwd, "tflops": tf(f_fwd, t_fwd),
+                       "frac": tf(f_fwd, t_fwd) / MFMA_BF16_PEAK_TFLOPS},
+           "future_attn_target": {"flops": f_tr, "tflops": tf(f_tr, t_tr),
+                                  "frac": tf(f_tr, t_tr) / MFMA_BF16_PEAK_TFLOPS},
+           "select_gather": {"bytes": sg_bytes, "achieved": sg_bytes / (t_sel / 1e3) / 1e9,
+                             "unit": "GB/s",
+                             "frac": sg_bytes / (t_sel / 1e3) / 1e9 / HBM_PEAK_GBS}}
+    del ins
+    torch.cuda.empty_cache()
+    return out
+
+
 def decode_bytes_per_step(w, layers):
     """Algorithmic HBM bytes of one decode step over all layers: the whole
     bounded K/V cache read once, the appended K/V rows written, the exiting
@@ -499,6 +574,8 @@ def main():
     ap.add_argument("--decode-layers", type=int, default=36)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the skewed 16k and the 36-layer 32k prefill workloads")
     ap.add_argument("--calibrate-copy", type=int, metavar="MIB", default=0,
                     help="only run a plain copy of MIB MiB (counter calibration)")
     a = ap.parse_args()
@@ -548,6 +625,11 @@ def main():
     }
     out["target_variants"] = bench_target_variants(kv, st)
     out["retention"] = bench_retention(kv, st)
+    if not a.no_long:
+        log("skewed-long: 4 x 16384, 2 timed passes")
+        out["skewed_long"] = bench_prefill(kv, synth.SKEWED, reps=2)
+        log("qwen3-8b-prefill: 36 layers x 32768, 1 timed pass")
+        out["prefill_36_layers"] = bench_prefill(kv, synth.QWEN8B, reps=1)
     if not a.no_decode:
         log(f"decode: {a.decode_steps} steps x {a.decode_layers} layers")
         out["decode"] = bench_decode(kv, a.decode_steps, a.decode_layers)
