@@ -10,13 +10,15 @@ indexing copy.  ``oracle.brute`` holds the dense S x S brute force that pins
 this oracle at tiny sizes.
 
 Method source: "KVpop -- Key-Value Cache Compression with Predictive Online
-Pruning" (arXiv 2607.05061v2), paperlayer.ai summary: App. D.1-D.4 (target),
+Pruning" (arXiv 2607.05061v2), paperlayer.ai summary: App. D.1-D.4 (target;
+D.3 sparse normalizer), App. C.1-C.2 (running top-k mask and its cutoffs),
 App. B.1-B.2 (aggregation, count normalisation), Sec. 3 and App. C.1
 (fixed-budget retention), App. E.2 and E.4 (scorer, delayed readout).
 
 Parity status per function (see the tests under tests/test_oracle_*.py):
-  lse, future_mass, select, gather, decode_attend, mlp_score, cache_step:
-  pinned (brute force, closed forms, invariants, hand-worked fixtures).
+  lse, future_mass, select, gather, decode_attend, mlp_score, cache_step,
+  running_topk, lse_sparse: pinned (brute force, closed forms, invariants,
+  hand-worked fixtures).
 """
 import ctypes
 import math
@@ -47,8 +49,11 @@ def _lib():
         lib.oracle_decode_attend.argtypes = [I, I, I, I, I, Dd, P, P, P, P, P, P, I]
         lib.oracle_mlp_score.argtypes = [I, I, I, I, I, P, P, P, P, P, P]
         lib.oracle_cache_step.argtypes = [I, I, I, I, I, I, I, I, P, P, P, P, P, P, P]
+        lib.oracle_running_topk.argtypes = [I, I, I, I, I, I, P, P, P, P]
+        lib.oracle_lse_sparse.argtypes = [I, I, I, I, I, Dd, P, P, P, P, I, I, I, L, P, P, I]
         for f in ("oracle_lse", "oracle_future_mass", "oracle_select", "oracle_decode_attend",
-                  "oracle_mlp_score", "oracle_cache_step"):
+                  "oracle_mlp_score", "oracle_cache_step", "oracle_running_topk",
+                  "oracle_lse_sparse"):
             getattr(lib, f).restype = ctypes.c_int
         _LIB = lib
     return _LIB
@@ -161,6 +166,55 @@ def select(scores, n_sink, window, budget):
     _check(_lib().oracle_select(B, Hkv, S, int(n_sink), int(window), int(budget), _ptr(sc),
                                 _ptr(sp), _ptr(ss)), "select")
     return sp, ss
+
+
+def running_topk(scores, n_sink, window, budget, log_decay=None):
+    """Running top-k retention mask (App. C.1) with Fenwick-tree cutoffs
+    (App. C.2) and per-head decay as static priorities (Sec. 3 teacher
+    policy, App. B.3).
+
+    scores [B,Hkv,S] float32; log_decay: None or [Hkv] float32 (-ln gamma_h).
+    Returns (keep_until int32 [B,Hkv,S], cutoff int32 [B,Hkv,S]): key t is
+    retained for queries t <= d < keep_until[t]; cutoff[d] is the k-th best
+    token of the pool at query d, or -1.
+    """
+    sc = _f32(scores)
+    B, Hkv, S = sc.shape
+    ld = None if log_decay is None else _f32(log_decay).reshape(Hkv)
+    until = np.empty((B, Hkv, S), np.int32)
+    cut = np.empty((B, Hkv, S), np.int32)
+    _check(_lib().oracle_running_topk(B, Hkv, S, int(n_sink), int(window), int(budget), _ptr(sc),
+                                      None if ld is None else _ptr(ld), _ptr(until), _ptr(cut)),
+           "running_topk")
+    return until, cut
+
+
+def lse_sparse(q, k, scores, n_sink, window, budget, log_decay=None, scale=None, rows=None,
+               nthreads=None):
+    """Sparse log-normalizer (App. D.3) over the retained set R_d of the
+    running top-k mask (App. C.1), built per query row from its definition.
+    Same shapes and ``rows`` convention as ``lse``."""
+    q = _f32(q)
+    k = _f32(k)
+    sc = _f32(scores)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    assert sc.shape == (B, Hkv, S)
+    ld = None if log_decay is None else _f32(log_decay).reshape(Hkv)
+    s_ = default_scale(D) if scale is None else float(scale)
+    if rows is None:
+        n = B * Hq * S
+        rp = None
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        n = rows.size
+        rp = _ptr(rows)
+    out = np.empty(n, np.float64)
+    _check(_lib().oracle_lse_sparse(B, Hq, Hkv, S, D, s_, _ptr(q), _ptr(k), _ptr(sc),
+                                    None if ld is None else _ptr(ld), int(n_sink), int(window),
+                                    int(budget), n, rp, _ptr(out), _threads(nthreads)),
+           "lse_sparse")
+    return out.reshape(B, Hq, S) if rows is None else out
 
 
 def gather(x, slot_pos):

@@ -127,3 +127,53 @@ def decode(q, kc, vc, slot_pos, scale=None):
             ls[b, g] = logsumexp(z)
             o[b, g] = np.exp(z - ls[b, g]) @ V
     return o, ls
+
+
+def priorities(scores_row, log_decay=0.0):
+    """Static priorities pi_t = sigma_t + lambda * t, each operation rounded
+    to float32 (numpy float32 scalars round after every operation)."""
+    lam = np.float32(log_decay)
+    return [np.float32(np.float32(scores_row[t]) + np.float32(lam * np.float32(t)))
+            for t in range(len(scores_row))]
+
+
+def running_sets(scores_row, n_sink, window, budget, log_decay=0.0):
+    """Per query d, the retained set R_d and the cutoff token of one row, by
+    sorting the pool P_d = [s, d - w] afresh at every d (Python's sorted).
+    Returns (list of sets R_d, list of cutoff tokens or -1)."""
+    S = len(scores_row)
+    k = budget - n_sink - window
+    pi = priorities(scores_row, log_decay)
+
+    def key(t):
+        s = float(pi[t])
+        return (math.isnan(s), 0.0 if math.isnan(s) else -s, t)
+
+    R, cut = [], []
+    for d in range(S):
+        pool = list(range(n_sink, d - window + 1))
+        chosen = sorted(pool, key=key)[:max(k, 0)]
+        sinks = set(range(min(n_sink, d + 1)))
+        win = set(range(max(d - window + 1, 0), d + 1))
+        R.append(sinks | win | set(chosen))
+        cut.append(chosen[-1] if k > 0 and len(pool) >= k else -1)
+    return R, cut
+
+
+def keep_until_from_sets(R, S):
+    """First query d >= t with t not in R_d (S if none), for every t."""
+    out = []
+    for t in range(S):
+        d = t
+        while d < S and t in R[d]:
+            d += 1
+        out.append(d)
+    return out
+
+
+def lse_masked(q, k, member, scale=None):
+    """LSE over an explicit membership mask member[b, h, d, t] (bool)."""
+    z = scores(q, k, scale)
+    G = z.shape[1] // member.shape[1]
+    m = np.repeat(member, G, axis=1)
+    return logsumexp(np.where(m, z, -np.inf), axis=-1)

@@ -14,7 +14,7 @@ LIB = os.path.join(HERE, "liboracle.so")
 
 def build(verbose: bool = False) -> str:
     # -O2 without fast-math: IEEE semantics (NaN compares, exact double sums)
-    cmd = ["gcc", "-std=c11", "-O2", "-fno-fast-math", "-fPIC", "-shared", "-pthread",
+    cmd = ["gcc", "-std=c11", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared", "-pthread",
            "-Wall", "-Wextra", "-o", LIB + ".tmp", SRC, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)

@@ -394,3 +394,178 @@ int oracle_cache_step(int B, int Hkv, int D, int n_sink, int window, int budget,
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------ */
+/* Running top-k retention mask (App. C.1 mask definition, App. C.2    */
+/* Fenwick-tree cutoffs; Sec. 3 teacher policy with per-head decay;    */
+/* App. B.3 temporal decay as static priorities; App. F fp32 ranking). */
+/* Per (b, h) row, at query position d:                                */
+/*   eligible pool  P_d = { t : s <= t <= d - w }                      */
+/*   selected       Sel_d = the k best of P_d (all of P_d if |P_d|<=k) */
+/*   retained       R_d = sinks [0, min(s, d+1)) U window (d-w, d]     */
+/*                        U Sel_d,   k = budget - s - w                */
+/* Ranking uses the static priority pi_t = sigma_t + lambda_h * t,     */
+/* both operations rounded to fp32 (lambda_h = -ln gamma_h >= 0; the  */
+/* decayed score sigma_t + (d - t) ln gamma_h orders keys the same way */
+/* at every d), under the retention order of oracle_select.            */
+/* Outputs per (b, h, position):                                       */
+/*   cutoff[d]     = the k-th best token of P_d (the teacher's cutoff  */
+/*                   token), or -1 while |P_d| < k or when k = 0       */
+/*   keep_until[t] = first query d >= t with t not in R_d, or S:       */
+/*                   t is retained exactly for queries t <= d < keep_until[t] */
+/* Cutoffs follow App. C.2: tokens enter a Fenwick tree over their     */
+/* ranks as they leave the window, and the k-th smallest rank present  */
+/* is found by a descent of the tree.                                  */
+/* ------------------------------------------------------------------ */
+static float priority(float sigma, float lambda, int t) {
+    float age = lambda * (float)t;   /* rounded to fp32 */
+    float pi = sigma + age;          /* rounded to fp32 */
+    return pi;
+}
+
+static int kth_in_fenwick(const int* tree, int n, int kth) {
+    /* smallest index i (0-based) with prefix count(0..i) >= kth */
+    int pos = 0, logn = 1;
+    while ((logn << 1) <= n) logn <<= 1;
+    for (int step = logn; step > 0; step >>= 1) {
+        if (pos + step <= n && tree[pos + step] < kth) {
+            pos += step;
+            kth -= tree[pos];
+        }
+    }
+    return pos; /* 1-based pos+1 holds it, i.e. 0-based index pos */
+}
+
+int oracle_running_topk(int B, int Hkv, int S, int n_sink, int window, int budget,
+                        const float* scores, const float* log_decay,
+                        int32_t* keep_until, int32_t* cutoff) {
+    if (B <= 0 || Hkv <= 0 || S <= 0 || n_sink < 0 || window < 0) return 1;
+    int kk = budget - n_sink - window;
+    if (kk < 0) return 1;
+    cand* e = (cand*)malloc(sizeof(cand) * (size_t)S);
+    int* rank = (int*)malloc(sizeof(int) * (size_t)S);
+    int* tok_of_rank = (int*)malloc(sizeof(int) * (size_t)S);
+    int* tree = (int*)malloc(sizeof(int) * (size_t)(S + 1));
+    int* cutrank = (int*)malloc(sizeof(int) * (size_t)S);
+    for (long row = 0; row < (long)B * Hkv; ++row) {
+        int h = (int)(row % Hkv);
+        float lam = log_decay ? log_decay[h] : 0.0f;
+        const float* sc = scores + row * S;
+        int32_t* until = keep_until + row * S;
+        int32_t* cut = cutoff ? cutoff + row * S : NULL;
+        /* ranks of every token that can become eligible: [s, S) */
+        int n_e = 0;
+        for (int p = n_sink; p < S; ++p) {
+            e[n_e].score = priority(sc[p], lam, p);
+            e[n_e].pos = p;
+            ++n_e;
+        }
+        qsort(e, (size_t)n_e, sizeof(cand), cand_cmp);
+        for (int r = 0; r < n_e; ++r) { rank[e[r].pos] = r; tok_of_rank[r] = e[r].pos; }
+        /* running cutoffs: token d - w enters the pool at query d */
+        for (int i = 0; i <= n_e; ++i) tree[i] = 0;
+        int count = 0;
+        for (int d = 0; d < S; ++d) {
+            int u = d - window;
+            if (u >= n_sink) {
+                for (int i = rank[u] + 1; i <= n_e; i += i & (-i)) tree[i] += 1;
+                ++count;
+            }
+            if (kk > 0 && count >= kk) cutrank[d] = kth_in_fenwick(tree, n_e, kk);
+            else cutrank[d] = -1;
+            if (cut) cut[d] = cutrank[d] >= 0 ? tok_of_rank[cutrank[d]] : -1;
+        }
+        /* keep_until: sinks stay; a long-range token is kept from t + w on
+         * while it is selected, and selection ends for good once k better
+         * tokens have entered the pool (cutoff ranks only decrease) */
+        for (int t = 0; t < S; ++t) {
+            if (t < n_sink) { until[t] = S; continue; }
+            long first = (long)t + window;
+            if (first >= S) { until[t] = S; continue; }
+            /* selected(d) for d >= first: pool not yet over k, or rank <= cutoff rank */
+            long lo = first, hi = S; /* find first d in [first, S) not selected */
+            while (lo < hi) {
+                long mid = (lo + hi) / 2;
+                int pool = (int)(mid - window - n_sink + 1);
+                int sel = kk > 0 && (pool <= kk || rank[t] <= cutrank[mid]);
+                if (sel) lo = mid + 1;
+                else hi = mid;
+            }
+            until[t] = (int32_t)lo;
+        }
+    }
+    free(e);
+    free(rank);
+    free(tok_of_rank);
+    free(tree);
+    free(cutrank);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Sparse log-normalizer (App. D.3: the target may reuse the           */
+/* normalizer of the fixed-budget sparse attention instead of the      */
+/* dense one; App. C.1 retained set R_d as above):                     */
+/*   LSE_d = log sum_{t in R_d} exp(scale * q_d . k_t)                 */
+/* R_d is built for each requested query row straight from its         */
+/* definition: the pool P_d is sorted in the retention order of the    */
+/* priorities and its first k entries are kept.                        */
+/* ------------------------------------------------------------------ */
+typedef struct {
+    int B, Hq, Hkv, S, D;
+    double scale;
+    const float *q, *k, *scores, *log_decay;
+    int n_sink, window, kk;
+    const long* rows;
+    double* out;
+} slse_ctx;
+
+static void slse_item(void* p, long i, double* z) {
+    slse_ctx* c = (slse_ctx*)p;
+    long r = c->rows ? c->rows[i] : i;
+    int d = (int)(r % c->S);
+    int g = (int)((r / c->S) % c->Hq);
+    int b = (int)(r / ((long)c->S * c->Hq));
+    int h = g / (c->Hq / c->Hkv);
+    const float* sc = c->scores + ((long)b * c->Hkv + h) * c->S;
+    float lam = c->log_decay ? c->log_decay[h] : 0.0f;
+    /* scratch: z[0..S) logits, then membership flags and the pool */
+    char* keep = (char*)(z + c->S);
+    cand* pool = (cand*)(keep + c->S + 8 - (c->S % 8));
+    for (int t = 0; t <= d; ++t) keep[t] = 0;
+    for (int t = 0; t <= d && t < c->n_sink; ++t) keep[t] = 1;          /* sinks */
+    for (int t = d - c->window + 1; t <= d; ++t) if (t >= 0) keep[t] = 1; /* window */
+    int n_pool = 0;
+    for (int t = c->n_sink; t <= d - c->window; ++t) {
+        pool[n_pool].score = priority(sc[t], lam, t);
+        pool[n_pool].pos = t;
+        ++n_pool;
+    }
+    qsort(pool, (size_t)n_pool, sizeof(cand), cand_cmp);
+    for (int j = 0; j < n_pool && j < c->kk; ++j) keep[pool[j].pos] = 1;
+    const float* qd = c->q + (((long)b * c->Hq + g) * c->S + d) * c->D;
+    const float* kh = c->k + ((long)b * c->Hkv + h) * (long)c->S * c->D;
+    double m = -INFINITY;
+    for (int t = 0; t <= d; ++t) {
+        if (!keep[t]) continue;
+        z[t] = c->scale * dot(qd, kh + (long)t * c->D, c->D);
+        if (z[t] > m) m = z[t];
+    }
+    if (m == -INFINITY) { c->out[i] = -INFINITY; return; }
+    double sum = 0.0;
+    for (int t = 0; t <= d; ++t) if (keep[t]) sum += exp(z[t] - m);
+    c->out[i] = m + log(sum);
+}
+
+int oracle_lse_sparse(int B, int Hq, int Hkv, int S, int D, double scale,
+                      const float* q, const float* k, const float* scores, const float* log_decay,
+                      int n_sink, int window, int budget, long n_rows, const long* rows,
+                      double* out, int nthreads) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || D <= 0 || Hq % Hkv) return 1;
+    if (n_sink < 0 || window < 0 || budget - n_sink - window < 0) return 1;
+    slse_ctx c = {B, Hq, Hkv, S, D, scale, q, k, scores, log_decay, n_sink, window,
+                  budget - n_sink - window, rows, out};
+    /* doubles: S logits + S flag bytes + S pool entries (8 bytes each) + slack */
+    run_items(slse_item, &c, n_rows, nthreads, 2L * S + S / 8 + 4);
+    return 0;
+}
