@@ -28,7 +28,8 @@ OP_FWD_LSE = 2
 
 EXPORTS = ("kvpop_abi_version", "kvpop_status_string", "kvpop_workspace_bytes", "kvpop_fwd_lse",
            "kvpop_future_attn_target", "kvpop_evict_select", "kvpop_decode_attend",
-           "kvpop_score_mlp", "kvpop_cache_step", "kvpop_decode_step")
+           "kvpop_score_mlp", "kvpop_cache_step", "kvpop_decode_step", "kvpop_running_topk",
+           "kvpop_fwd_lse_sparse")
 
 
 class KvpopError(RuntimeError):
@@ -60,6 +61,8 @@ def lib():
             "kvpop_status_string": (ctypes.c_char_p, [I]),
             "kvpop_workspace_bytes": (Z, [I, DP, I]),
             "kvpop_fwd_lse": (I, [DP, P, P, P, P, Z, P]),
+            "kvpop_running_topk": (I, [I, I, I, I, I, I, P, P, P, P, P]),
+            "kvpop_fwd_lse_sparse": (I, [DP, P, P, P, P, P, Z, P]),
             "kvpop_future_attn_target": (I, [DP, P, P, P, I, I, I, I, P, P, P, Z, P]),
             "kvpop_evict_select": (I, [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P]),
             "kvpop_decode_attend": (I, [DP, P, P, P, P, P, I, P, P, Z, P]),
@@ -125,6 +128,57 @@ def fwd_lse(q, k, scale=0.0, out=None, workspace=None):
     st = lib().kvpop_fwd_lse(ctypes.byref(d), _p(q), _p(k), _p(lse), _p(ws),
                              0 if ws is None else ws.numel() * ws.element_size(), _stream())
     _check("kvpop_fwd_lse", st)
+    return lse
+
+
+def running_topk(scores, n_sink, window, budget, log_decay=None, want_cutoff=True, out=None,
+                 out_cutoff=None):
+    """Running top-k retention mask (App. C.1) and its per-query cutoffs
+    (App. C.2) with per-head decay priorities (Sec. 3, App. B.3).
+
+    scores fp32 [B,Hkv,S]; log_decay None or fp32 [Hkv].  Returns
+    (keep_until int32 [B,Hkv,S], cutoff int32 [B,Hkv,S] or None).
+    """
+    _need(scores, torch.float32, "scores", 3)
+    B, Hkv, S = scores.shape
+    if log_decay is not None:
+        _need(log_decay, torch.float32, "log_decay")
+        if log_decay.numel() != Hkv:
+            raise ValueError("log_decay: expected one value per KV head")
+    until = out if out is not None else torch.empty((B, Hkv, S), dtype=torch.int32,
+                                                    device=scores.device)
+    _need(until, torch.int32, "keep_until")
+    cut = None
+    if want_cutoff:
+        cut = out_cutoff if out_cutoff is not None else torch.empty_like(until)
+        _need(cut, torch.int32, "cutoff")
+    st = lib().kvpop_running_topk(B, Hkv, S, int(n_sink), int(window), int(budget), _p(scores),
+                                  _p(log_decay), _p(until), _p(cut), _stream())
+    _check("kvpop_running_topk", st)
+    return until, cut
+
+
+def fwd_lse_sparse(q, k, keep_until, scale=0.0, out=None, workspace=None):
+    """Sparse causal log-normalizers LSE [B,Hq,S] fp32 over the running
+    top-k mask (App. D.3, C.1): key t counts for row d while
+    t <= d < keep_until[t]."""
+    _need(q, torch.bfloat16, "q", 4)
+    _need(k, torch.bfloat16, "k", 4)
+    _need(keep_until, torch.int32, "keep_until", 3)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, S, D) or tuple(keep_until.shape) != (B, Hkv, S):
+        raise ValueError("k / keep_until shape mismatch")
+    lse = out if out is not None else torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    _need(lse, torch.float32, "lse")
+    d = dims(B, Hq, Hkv, S, D, scale)
+    nbytes = workspace_bytes(OP_FWD_LSE, d)
+    ws = workspace if workspace is not None else (
+        torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None)
+    st = lib().kvpop_fwd_lse_sparse(ctypes.byref(d), _p(q), _p(k), _p(keep_until), _p(lse),
+                                    _p(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                    _stream())
+    _check("kvpop_fwd_lse_sparse", st)
     return lse
 
 

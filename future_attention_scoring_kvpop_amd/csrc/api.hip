@@ -85,7 +85,42 @@ kvpop_status kvpop_fwd_lse(const kvpop_dims* dims, const void* q, const void* k,
     if (!workspace || !aligned(workspace, 16)) return KVPOP_ERR_INVALID_ARGUMENT;
     if (workspace_bytes < p.partial_floats * sizeof(float)) return KVPOP_ERR_WORKSPACE_TOO_SMALL;
   }
-  return from_hip(kvpop::launch_fwd_lse(s, q, k, lse, (float*)workspace, stream));
+  return from_hip(kvpop::launch_fwd_lse(s, q, k, nullptr, lse, (float*)workspace, stream));
+}
+
+kvpop_status kvpop_running_topk(int batch, int n_kv_heads, int seq_len, int n_sink, int window,
+                                int budget, const float* scores, const float* log_decay,
+                                int32_t* keep_until, int32_t* cutoff, hipStream_t stream) {
+  if (batch <= 0 || n_kv_heads <= 0 || seq_len <= 0 || n_sink < 0 || window < 0)
+    return KVPOP_ERR_INVALID_ARGUMENT;
+  if (budget < n_sink + window || budget <= 0) return KVPOP_ERR_INVALID_ARGUMENT;
+  if (!scores || !keep_until) return KVPOP_ERR_INVALID_ARGUMENT;
+  if (!aligned(scores, 4) || !aligned(keep_until, 4) || (cutoff && !aligned(cutoff, 4)) ||
+      (log_decay && !aligned(log_decay, 4)))
+    return KVPOP_ERR_INVALID_ARGUMENT;
+  // positions, budgets and query indices stay far inside int32
+  if ((double)seq_len + window + budget > 2.0e9) return KVPOP_ERR_UNSUPPORTED;
+  if ((double)batch * n_kv_heads * ((seq_len + 255) / 256) > 2.0e9) return KVPOP_ERR_UNSUPPORTED;
+  return from_hip(kvpop::launch_running_topk(batch, n_kv_heads, seq_len, n_sink, window, budget,
+                                             scores, log_decay, keep_until, cutoff, stream));
+}
+
+kvpop_status kvpop_fwd_lse_sparse(const kvpop_dims* dims, const void* q, const void* k,
+                                  const int32_t* keep_until, float* lse, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  AttnShape s;
+  kvpop_status st = check_dims(dims, &s);
+  if (st != KVPOP_OK) return st;
+  if (!q || !k || !keep_until || !lse) return KVPOP_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(keep_until, 4) || !aligned(lse, 4))
+    return KVPOP_ERR_INVALID_ARGUMENT;
+  const kvpop::FwdPlan p = kvpop::plan_fwd(s);
+  if (p.partial_floats) {
+    if (!workspace || !aligned(workspace, 16)) return KVPOP_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < p.partial_floats * sizeof(float)) return KVPOP_ERR_WORKSPACE_TOO_SMALL;
+  }
+  return from_hip(kvpop::launch_fwd_lse(s, q, k, (const int*)keep_until, lse, (float*)workspace,
+                                        stream));
 }
 
 kvpop_status kvpop_future_attn_target(const kvpop_dims* dims, const void* q, const void* k,

@@ -24,6 +24,11 @@
 //     a small kernel merges them.
 //   * Work items are issued longest first and renumbered so that each XCD
 //     works through whole KV heads (their K stays in that XCD's L2).
+//   * Sparse normalizer (App. D.3 with the running top-k mask of App. C.1):
+//     key t takes part in row d only while t <= d < keep_until[t].  Each
+//     wave DMAs its own copy of the tile's 64 keep_until values into the
+//     stage beside the K rows and every tile is masked with one compare per
+//     score; the MFMA work is the same as the dense pass.
 #include <type_traits>
 
 #include "common.h"
@@ -57,9 +62,10 @@ __device__ __forceinline__ void wait_inflight(int n) {
   else wait_vmcnt<12>();
 }
 
-template <int D>
+template <int D, bool SPARSE>
 __global__ __launch_bounds__(kThreads, KVPOP_FWD_MIN_BLOCKS) void fwd_lse_kernel(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, float* __restrict__ lse,
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const int* __restrict__ keep_until,
+    float* __restrict__ lse,
     float2* __restrict__ part, int B, int Hq, int Hkv, int S, float c, float scale, int n_pb,
     int kmax, int n_pieces, int n_items, int snake_cus) {
   constexpr int NS = D / 16;           // MFMA k-slices
@@ -75,6 +81,15 @@ __global__ __launch_bounds__(kThreads, KVPOP_FWD_MIN_BLOCKS) void fwd_lse_kernel
     constexpr int j = decltype(J)::value;
     return j == 0 ? ks0 : j == 1 ? ks1 : j == 2 ? ks2 : ks3;
   };
+  // sparse mask: each wave's own copy of a stage's 64 keep_until values
+  constexpr int US = SPARSE ? kKT * (kThreads / 64) : 1;
+  __shared__ __attribute__((aligned(256))) int us0[US], us1[US], us2[kStages > 2 ? US : 1],
+      us3[kStages > 3 ? US : 1];
+  auto ust = [&](auto J) -> int* {
+    constexpr int j = decltype(J)::value;
+    return j == 0 ? us0 : j == 1 ? us1 : j == 2 ? us2 : us3;
+  };
+  constexpr int DPS = LPW + (SPARSE ? 1 : 0);  // DMA instructions per wave per stage
 
   const int G = Hq / Hkv;
   const int P = 128 / G;
@@ -119,6 +134,7 @@ __global__ __launch_bounds__(kThreads, KVPOP_FWD_MIN_BLOCKS) void fwd_lse_kernel
   const int g = h * G + gl;
 
   const bf16_t* kbase = k + ((size_t)b * Hkv + h) * (size_t)S * D;
+  const int* kuntil = SPARSE ? keep_until + ((size_t)b * Hkv + h) * (size_t)S : nullptr;
   auto issue = [&](auto J, int kt) {
     uint8_t* dst = kst(J);
 #pragma unroll
@@ -130,6 +146,8 @@ __global__ __launch_bounds__(kThreads, KVPOP_FWD_MIN_BLOCKS) void fwd_lse_kernel
       const int t = min(kt * kKT + row, S - 1);
       dma16(kbase + (size_t)t * D + lc * 8, dst + I * 1024);
     }
+    if constexpr (SPARSE)
+      dma4(kuntil + min(kt * kKT + lane, S - 1), ust(J) + wave * 64);
   };
 
   bf16x8 bq[NS];
@@ -152,7 +170,7 @@ __global__ __launch_bounds__(kThreads, KVPOP_FWD_MIN_BLOCKS) void fwd_lse_kernel
   auto step = [&](auto J, int i) {
     constexpr int j = decltype(J)::value;
     constexpr int jn = (j + kStages - 1) % kStages;
-    wait_inflight(LPW * min(kStages - 2, n_kt - 1 - i));
+    wait_inflight(DPS * min(kStages - 2, n_kt - 1 - i));
     wait_lgkmcnt0();
     bare_barrier();  // tile i is in LDS for every wave; tile i-1's stage is free
     if (i + kStages - 1 < n_kt) issue(std::integral_constant<int, jn>{}, kt0 + i + kStages - 1);
@@ -169,7 +187,24 @@ __global__ __launch_bounds__(kThreads, KVPOP_FWD_MIN_BLOCKS) void fwd_lse_kernel
         acc[sub] = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(arow + (((2 * s + half) ^ sw) << 4))),
                           bq[s], acc[sub]);
     }
-    if (t0 + kKT - 1 > p0 || t0 + kKT > k_end) {  // diagonal, past S or past the piece
+    if constexpr (SPARSE) {
+      // key row of register r: t0 + 32 sub + 8 (r/4) + 4 half + r%4; its
+      // keep_until values are four runs of four consecutive ints
+      const int* ut = ust(J) + wave * 64;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int4 u = *reinterpret_cast<const int4*>(ut + sub * 32 + 8 * r4 + 4 * half);
+          const int uu[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * r4 + e;
+            const int t = t0 + sub * 32 + 8 * r4 + 4 * half + e;
+            acc[sub][r] = (t > dpos || t >= k_end || dpos >= uu[e]) ? -INFINITY : acc[sub][r];
+          }
+        }
+    } else if (t0 + kKT - 1 > p0 || t0 + kKT > k_end) {  // diagonal, past S or past the piece
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
@@ -259,8 +294,8 @@ FwdPlan plan_fwd(const AttnShape& s) {
   return p;
 }
 
-hipError_t launch_fwd_lse(const AttnShape& s, const void* q, const void* k, float* lse,
-                          float* workspace, hipStream_t st) {
+hipError_t launch_fwd_lse(const AttnShape& s, const void* q, const void* k, const int* keep_until,
+                          float* lse, float* workspace, hipStream_t st) {
   const FwdPlan p = plan_fwd(s);
   const int n_items = s.B * s.Hkv * p.n_pb * p.n_pieces;
   const float c = s.scale * kLog2e;
@@ -269,14 +304,18 @@ hipError_t launch_fwd_lse(const AttnShape& s, const void* q, const void* k, floa
   const int snake_cus = n_items <= cus * KVPOP_FWD_MIN_BLOCKS && cus % 8 == 0 ? cus / 8 : 0;
   dim3 grid(n_items), block(kThreads);
   float2* part = reinterpret_cast<float2*>(workspace);
-  if (s.D == 128)
-    hipLaunchKernelGGL(fwd_lse_kernel<128>, grid, block, 0, st, (const bf16_t*)q, (const bf16_t*)k,
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, block, 0, st, (const bf16_t*)q, (const bf16_t*)k, keep_until,
                        lse, part, s.B, s.Hq, s.Hkv, s.S, c, s.scale, p.n_pb, p.kmax, p.n_pieces,
                        n_items, snake_cus);
-  else
-    hipLaunchKernelGGL(fwd_lse_kernel<64>, grid, block, 0, st, (const bf16_t*)q, (const bf16_t*)k,
-                       lse, part, s.B, s.Hq, s.Hkv, s.S, c, s.scale, p.n_pb, p.kmax, p.n_pieces,
-                       n_items, snake_cus);
+  };
+  if (s.D == 128) {
+    if (keep_until) go(fwd_lse_kernel<128, true>);
+    else go(fwd_lse_kernel<128, false>);
+  } else {
+    if (keep_until) go(fwd_lse_kernel<64, true>);
+    else go(fwd_lse_kernel<64, false>);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_pieces == 1) return e;
   const long rows = (long)s.B * s.Hq * s.S;

@@ -23,8 +23,15 @@ struct FwdPlan {
   size_t partial_floats;  // workspace floats (0 without split)
 };
 FwdPlan plan_fwd(const AttnShape& s);
-hipError_t launch_fwd_lse(const AttnShape& s, const void* q, const void* k, float* lse,
-                          float* workspace, hipStream_t st);
+// keep_until: nullable [B][Hkv][S]; when given, key t counts for row d only
+// while t <= d < keep_until[t] (the sparse normalizer)
+hipError_t launch_fwd_lse(const AttnShape& s, const void* q, const void* k, const int* keep_until,
+                          float* lse, float* workspace, hipStream_t st);
+
+// ---- running top-k mask ----
+hipError_t launch_running_topk(int B, int Hkv, int S, int n_sink, int window, int budget,
+                               const float* scores, const float* log_decay, int* keep_until,
+                               int* cutoff, hipStream_t st);
 
 // ---- transposed future-attention pass ----
 constexpr int kTgtMaxChunks = 64;

@@ -90,6 +90,50 @@ kvpop_status kvpop_fwd_lse(const kvpop_dims* dims, const void* q, const void* k,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * kvpop_running_topk -- running top-k retention mask and its cutoffs.
+ * App. C.1 (mask definition): at query position d the fixed-budget mask
+ * keeps the sinks [0, min(s, d+1)), the protected window (d-w, d] and the
+ * k = budget - s - w best tokens of the eligible pool P_d = [s, d-w] (all
+ * of P_d while it holds at most k).  App. C.2: the per-query cutoffs of that
+ * running top-k.  Sec. 3 (teacher policy) and App. B.3: a per-KV-head decay
+ * gamma_h in (0, 1) ranks by the static priority
+ *   pi_t = sigma_t + lambda_h * t,  lambda_h = -ln gamma_h,
+ * both operations rounded to fp32 (App. F: ranking in fp32); the order is
+ * that of kvpop_evict_select (higher first, lower position on ties, NaN
+ * last, -0 = +0).
+ *   scores:     fp32 [B][Hkv][S] (sigma; positions < s are ignored).
+ *   log_decay:  nullable fp32 [Hkv] (lambda_h; NULL = no decay).  Finite
+ *               values >= 0 are the intended use; any value still gives a
+ *               valid total order on pi.
+ *   keep_until: int32 [B][Hkv][S], written in full: key t is retained for
+ *               the queries t <= d < keep_until[t] (S: to the end).
+ *   cutoff:     nullable int32 [B][Hkv][S]: cutoff[d] = the k-th best token
+ *               of P_d (the teacher's cutoff token), -1 while |P_d| < k or
+ *               when k = 0.
+ * Errors: INVALID_ARGUMENT for non-positive sizes, s < 0, w < 0,
+ * budget < s + w, a NULL scores or keep_until, misaligned pointers.
+ * The result is exact (integer outputs, no rounding-order dependence).
+ */
+kvpop_status kvpop_running_topk(int batch, int n_kv_heads, int seq_len, int n_sink, int window,
+                                int budget, const float* scores, const float* log_decay,
+                                int32_t* keep_until, int32_t* cutoff, hipStream_t stream);
+
+/*
+ * kvpop_fwd_lse_sparse -- main causal pass with the sparse normalizer.
+ * App. D.3: the target may reuse the log-normalizer of the fixed-budget
+ * sparse attention instead of the dense one; App. C.1 gives its mask:
+ *   LSE[b][g][d] = log sum_{t <= d, d < keep_until[b][h][t]} exp(scale * q_d . k_t)
+ * with keep_until from kvpop_running_topk (h = g / G).  Same layouts,
+ * workspace and errors as kvpop_fwd_lse; keep_until is int32 [B][Hkv][S],
+ * 4-byte aligned.  A row whose retained set is empty gets -inf (the mask
+ * of kvpop_running_topk always keeps token d itself when w >= 1).  The
+ * result feeds kvpop_future_attn_target unchanged.
+ */
+kvpop_status kvpop_fwd_lse_sparse(const kvpop_dims* dims, const void* q, const void* k,
+                                  const int32_t* keep_until, float* lse, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
+/*
  * kvpop_future_attn_target -- transposed future-attention pass.
  * App. D.1-D.2 and D.4: keys take the role of queries; the original
  * log-normalizer is subtracted and queries d < t + w are masked, so for key

@@ -156,3 +156,27 @@ def test_python_binding_rejects_host_tensors():
     with pytest.raises(ValueError):
         kv.fwd_lse(torch.zeros(1, 2, 4, 64, dtype=torch.bfloat16),
                    torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16))
+
+
+def test_running_topk_and_sparse_lse_validation(lib):
+    # every call below fails its host-side checks before any launch
+    rt = lib.kvpop_running_topk
+    assert rt(1, 8, 4096, 4, 128, 100, GOOD, None, GOOD, None, None) == 1   # budget < s + w
+    assert rt(1, 8, 4096, -1, 128, 1024, GOOD, None, GOOD, None, None) == 1
+    assert rt(1, 8, 4096, 4, -2, 1024, GOOD, None, GOOD, None, None) == 1
+    assert rt(0, 8, 4096, 4, 128, 1024, GOOD, None, GOOD, None, None) == 1
+    assert rt(1, 8, 4096, 4, 128, 1024, None, None, GOOD, None, None) == 1
+    assert rt(1, 8, 4096, 4, 128, 1024, GOOD, None, None, None, None) == 1
+    assert rt(1, 8, 4096, 4, 128, 1024, P(0x10002), None, GOOD, None, None) == 1  # misaligned
+    assert rt(1, 8, 4096, 4, 128, 1024, GOOD, P(0x10001), GOOD, None, None) == 1
+    sp = lib.kvpop_fwd_lse_sparse
+    d = kv.dims(1, 32, 8, 4096, 128)
+    assert sp(ctypes.byref(d), GOOD, GOOD, None, GOOD, None, 0, None) == 1     # no mask
+    assert sp(ctypes.byref(d), GOOD, GOOD, P(0x10002), GOOD, None, 0, None) == 1
+    assert sp(None, GOOD, GOOD, GOOD, GOOD, None, 0, None) == 1
+    d = kv.dims(1, 32, 8, 4096, 96)
+    assert sp(ctypes.byref(d), GOOD, GOOD, GOOD, GOOD, None, 0, None) == 2      # D = 96
+    d = kv.dims(1, 32, 8, 4096, 128)
+    need = lib.kvpop_workspace_bytes(2, ctypes.byref(d), 0)
+    if need:
+        assert sp(ctypes.byref(d), GOOD, GOOD, GOOD, GOOD, GOOD, need - 16, None) == 3
