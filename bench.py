@@ -209,6 +209,87 @@ def bench_retention(kv, st, reps=50):
             "note": "8 rows of 4096 scores: launch- and latency-bound, not bandwidth-bound"}
 
 
+def live_pairs(until, S):
+    """Sum over queries d of |R_d|: key t is retained for d in [t, keep_until[t])."""
+    t = torch.arange(S, device=until.device, dtype=torch.int64)
+    return int((until.to(torch.int64) - t).clamp_min(0).sum().item())
+
+
+def bench_sparse(kv, st, reps=20):
+    """The target with the sparse normalizer (App. D.3) on the layer inputs:
+    the running top-k mask (App. C.1-C.2) over MLP-scorer scores of the
+    layer's keys with a per-head decay (lambda_h = 1e-4 * (h + 1)), the
+    sparse causal pass, and the transposed pass on its normalizers.  The
+    sparse pass executes every causal tile (masked), so its MFMA work is the
+    dense pass's; its algorithmic flops count the retained pairs only."""
+    w = st.w
+    dev = st.q.device
+    sc = kv.score_mlp(st.k, *st.mlp)
+    lam = torch.tensor([1e-4 * (h + 1) for h in range(w.Hkv)], dtype=torch.float32, device=dev)
+    until = torch.empty((w.B, w.Hkv, w.S), dtype=torch.int32, device=dev)
+    cut = torch.empty_like(until)
+
+    def t_ms(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    def mask():
+        kv.running_topk(sc, w.n_sink, w.window, w.budget, log_decay=lam, out=until, out_cutoff=cut)
+
+    def sparse_lse():
+        kv.fwd_lse_sparse(st.q, st.k, until, out=st.lse, workspace=st.fws)
+
+    def target():
+        kv.future_attn_target(st.q, st.k, st.lse, w.window, agg="sum", out=st.mass, workspace=st.ws)
+
+    def step():
+        mask()
+        sparse_lse()
+        target()
+
+    t_mask, t_lse, t_tr, t_step = t_ms(mask), t_ms(sparse_lse), t_ms(target), t_ms(step)
+    f_fwd, f_tr = target_flops(w)
+    f_live = 2.0 * w.D * w.Hq // w.Hkv * live_pairs(until, w.S)
+    tf = lambda f, ms: f / (ms / 1e3) / 1e12
+    return {"scores": "kvpop_score_mlp over the layer's keys", "log_decay": "1e-4 * (h + 1)",
+            "ms_per_step": t_step, "keys_per_s": w.B * w.Hkv * w.S / (t_step / 1e3),
+            "running_topk": {"ms": t_mask},
+            "fwd_lse_sparse": {"ms": t_lse, "executed_flops": f_fwd,
+                               "executed_frac": tf(f_fwd, t_lse) / MFMA_BF16_PEAK_TFLOPS,
+                               "retained_pair_flops": f_live,
+                               "retained_frac": tf(f_live, t_lse) / MFMA_BF16_PEAK_TFLOPS},
+            "future_attn_target": {"ms": t_tr, "tflops": tf(f_tr, t_tr),
+                                   "frac": tf(f_tr, t_tr) / MFMA_BF16_PEAK_TFLOPS}}
+
+
+def bench_running_topk_long(kv, w, reps=5):
+    """The running top-k mask alone at a long-context shape (8 KV heads of
+    seeded scores, budget of the workload)."""
+    sc = synth.scores((w.B, w.Hkv, w.S), seed=4000, device="cuda")
+    until = torch.empty(sc.shape, dtype=torch.int32, device="cuda")
+    cut = torch.empty_like(until)
+    kv.running_topk(sc, w.n_sink, w.window, w.budget, out=until, out_cutoff=cut)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        kv.running_topk(sc, w.n_sink, w.window, w.budget, out=until, out_cutoff=cut)
+    b.record()
+    torch.cuda.synchronize()
+    return {"workload": w.name, "rows": w.B * w.Hkv, "seq_len": w.S, "budget": w.budget,
+            "ms": a.elapsed_time(b) / reps}
+
+
 def bench_prefill(kv, w, layers=None, reps=1, seed=None):
     """The target pipeline on a long-context workload: per layer the causal
     LSE pass, the transposed future-attention pass (SUM over the group) and
@@ -625,11 +706,14 @@ def main():
     }
     out["target_variants"] = bench_target_variants(kv, st)
     out["retention"] = bench_retention(kv, st)
+    log("sparse normalizer: running top-k mask, sparse causal pass, transposed pass")
+    out["sparse_normalizer"] = bench_sparse(kv, st)
     if not a.no_long:
         log("skewed-long: 4 x 16384, 2 timed passes")
         out["skewed_long"] = bench_prefill(kv, synth.SKEWED, reps=2)
         log("qwen3-8b-prefill: 36 layers x 32768, 1 timed pass")
         out["prefill_36_layers"] = bench_prefill(kv, synth.QWEN8B, reps=1)
+        out["prefill_36_layers"]["running_topk_one_layer"] = bench_running_topk_long(kv, synth.QWEN8B)
     if not a.no_decode:
         log(f"decode: {a.decode_steps} steps x {a.decode_layers} layers")
         out["decode"] = bench_decode(kv, a.decode_steps, a.decode_layers)

@@ -100,7 +100,8 @@ kvpop_status kvpop_running_topk(int batch, int n_kv_heads, int seq_len, int n_si
     return KVPOP_ERR_INVALID_ARGUMENT;
   // positions, budgets and query indices stay far inside int32
   if ((double)seq_len + window + budget > 2.0e9) return KVPOP_ERR_UNSUPPORTED;
-  if ((double)batch * n_kv_heads * ((seq_len + 255) / 256) > 2.0e9) return KVPOP_ERR_UNSUPPORTED;
+  if (seq_len > kvpop::running_topk_max_len()) return KVPOP_ERR_UNSUPPORTED;
+  if ((double)batch * n_kv_heads * ((seq_len + 63) / 64) > 2.0e9) return KVPOP_ERR_UNSUPPORTED;
   return from_hip(kvpop::launch_running_topk(batch, n_kv_heads, seq_len, n_sink, window, budget,
                                              scores, log_decay, keep_until, cutoff, stream));
 }

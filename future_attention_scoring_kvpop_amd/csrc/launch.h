@@ -29,6 +29,7 @@ hipError_t launch_fwd_lse(const AttnShape& s, const void* q, const void* k, cons
                           float* lse, float* workspace, hipStream_t st);
 
 // ---- running top-k mask ----
+int running_topk_max_len();  // longest row the kernel takes
 hipError_t launch_running_topk(int B, int Hkv, int S, int n_sink, int window, int budget,
                                const float* scores, const float* log_decay, int* keep_until,
                                int* cutoff, hipStream_t st);

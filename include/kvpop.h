@@ -111,7 +111,8 @@ kvpop_status kvpop_fwd_lse(const kvpop_dims* dims, const void* q, const void* k,
  *               of P_d (the teacher's cutoff token), -1 while |P_d| < k or
  *               when k = 0.
  * Errors: INVALID_ARGUMENT for non-positive sizes, s < 0, w < 0,
- * budget < s + w, a NULL scores or keep_until, misaligned pointers.
+ * budget < s + w, a NULL scores or keep_until, misaligned pointers;
+ * UNSUPPORTED for seq_len > 65536.
  * The result is exact (integer outputs, no rounding-order dependence).
  */
 kvpop_status kvpop_running_topk(int batch, int n_kv_heads, int seq_len, int n_sink, int window,
