@@ -14,7 +14,7 @@ the single-call kvpop_decode_step are reported beside it) in steps/s with its
 HBM roofline, the roofline of the dominant kernel, and the CPU oracle timed
 on a bounded sample.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]   (defaults: K=20, W=50)
 """
 import argparse
 import json
@@ -87,15 +87,21 @@ class TargetStep:
         nb = kv.workspace_bytes(kv.OP_DECODE, dd)
         self.dws = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
 
-    def run(self, ev=None):
+    def run(self, ev=None, ev_target=None):
+        """One step.  ev: four events around the passes (instrumented
+        breakdown); ev_target: two events around the target call only."""
         kv, w = self.kv, self.w
         if ev:
             ev[0].record()
         kv.fwd_lse(self.q, self.k, out=self.lse, workspace=self.fws)
         if ev:
             ev[1].record()
+        if ev_target:
+            ev_target[0].record()
         kv.future_attn_target(self.q, self.k, self.lse, w.window, agg="sum", out=self.mass,
                               workspace=self.ws)
+        if ev_target:
+            ev_target[1].record()
         if ev:
             ev[2].record()
         kv.evict_select(self.mass, w.n_sink, w.window, w.budget, self.k, self.v, out_pos=self.sp,
@@ -109,26 +115,40 @@ class TargetStep:
 
 
 def bench_target(kv, steps, warmup):
+    """Timed region: `steps` steps between two events, with one more pair of
+    events around each step's target call (the dominant kernel; two events
+    per step cost ~1.5% of the step, four ~6%).  After it, the same number
+    of steps with events around every pass gives the per-pass breakdown."""
     w = synth.QWEN4B
     st = TargetStep(kv, w)
     for _ in range(warmup):
         st.run()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
+    E = lambda: torch.cuda.Event(enable_timing=True)
+    evt = [[E(), E()] for _ in range(steps)]
+    t0, t1 = E(), E()
     torch.cuda.synchronize()
     t0.record()
     for i in range(steps):
-        st.run(evs[i])
+        st.run(ev_target=evt[i])
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
-    t_fwd = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
-    t_tr = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
-    t_rest = sum(e[2].elapsed_time(e[3]) for e in evs) / steps
+    t_tr = sum(e[0].elapsed_time(e[1]) for e in evt) / steps
+    # instrumented breakdown (not the timed region)
+    evs = [[E() for _ in range(4)] for _ in range(steps)]
+    a, b = E(), E()
+    a.record()
+    for i in range(steps):
+        st.run(evs[i])
+    b.record()
+    torch.cuda.synchronize()
+    brk = {"ms_per_step": a.elapsed_time(b) / steps,
+           "fwd_lse": sum(e[0].elapsed_time(e[1]) for e in evs) / steps,
+           "future_attn_target": sum(e[1].elapsed_time(e[2]) for e in evs) / steps,
+           "select_gather_decode": sum(e[2].elapsed_time(e[3]) for e in evs) / steps}
     f_fwd, f_tr = target_flops(w)
-    return st, ms, t_fwd, t_tr, t_rest, f_fwd, f_tr
+    return st, ms, t_tr, brk, f_fwd, f_tr
 
 
 def target_flops_lookahead(w, lookahead):
@@ -650,7 +670,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--decode-steps", type=int, default=512)
     ap.add_argument("--decode-layers", type=int, default=36)
     ap.add_argument("--no-decode", action="store_true")
@@ -677,12 +697,13 @@ def main():
     torch.cuda.set_device(0)
 
     log(f"target step: {a.warmup} warmup + {a.steps} timed")
-    st, ms, t_fwd, t_tr, t_rest, f_fwd, f_tr = bench_target(kv, a.steps, a.warmup)
+    st, ms, t_tr, brk, f_fwd, f_tr = bench_target(kv, a.steps, a.warmup)
     w = st.w
     keys = w.B * w.Hkv * w.S
     value = keys / (ms / 1e3)
-    log(f"target step {ms:.4f} ms (fwd_lse {t_fwd:.4f}, future target {t_tr:.4f}, "
-        f"select+gather+decode {t_rest:.4f})")
+    t_fwd = brk["fwd_lse"]
+    log(f"target step {ms:.4f} ms (future target {t_tr:.4f}; instrumented: fwd_lse {t_fwd:.4f}, "
+        f"select+gather+decode {brk['select_gather_decode']:.4f})")
     achieved_tr = f_tr / (t_tr / 1e3) / 1e12
     achieved_fwd = f_fwd / (t_fwd / 1e3) / 1e12
     out = {
@@ -702,7 +723,10 @@ def main():
                                 "frac": achieved_fwd / MFMA_BF16_PEAK_TFLOPS},
                     "future_attn_target": {"ms": t_tr, "tflops": achieved_tr,
                                            "frac": achieved_tr / MFMA_BF16_PEAK_TFLOPS},
-                    "select_gather_decode": {"ms": t_rest}},
+                    "select_gather_decode": {"ms": brk["select_gather_decode"]},
+                    "instrumented_ms_per_step": brk["ms_per_step"],
+                    "note": "fwd_lse and select_gather_decode from a second loop with events "
+                            "around every pass; future_attn_target from the timed steps"},
     }
     out["target_variants"] = bench_target_variants(kv, st)
     out["retention"] = bench_retention(kv, st)
