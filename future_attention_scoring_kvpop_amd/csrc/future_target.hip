@@ -191,6 +191,12 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KVPO
   const int col = lane & 31, half = lane >> 5;
   const int frow = col * ROWB;      // this lane's query row in a tile
   const int sw = col & (CPR - 1);   // its swizzle
+  // byte offset of this lane's B fragment of k-slice s within a tile:
+  // loop-invariant, so each fragment read is one ds_read with the stage
+  // and tile base as its immediate offset
+  uint32_t foff[NS];
+#pragma unroll
+  for (int s2 = 0; s2 < NS; ++s2) foff[s2] = frow + (((2 * s2 + half) ^ sw) << 4);
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
@@ -312,7 +318,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KVPO
       const bool skip = ts >= S || d0 + kQT - 1 < ts + window ||
                         (lookahead >= 0 && d0 > ts + 31 + window + lookahead);
       if (!skip) {
-        const uint8_t* tile = qst(J) + tt * TILE + frow;
+        const uint8_t* tile = qst(J) + tt * TILE;
         float lraw = lst(J)[wave * 64 + (TPS == 2 ? tt * 32 + col : lane)];
         f32x16 acc;
 #pragma unroll
@@ -325,7 +331,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KVPO
           u32x4 bu[FG];
 #pragma unroll
           for (int s = 0; s < FG; ++s)
-            bu[s] = *reinterpret_cast<const u32x4*>(tile + (((2 * (s0 + s) + half) ^ sw) << 4));
+            bu[s] = *reinterpret_cast<const u32x4*>(tile + foff[s0 + s]);
           if constexpr (FG == 8)
             asm volatile("" ::"v"(bu[0]), "v"(bu[1]), "v"(bu[2]), "v"(bu[3]), "v"(bu[4]), "v"(bu[5]),
                          "v"(bu[6]), "v"(bu[7]), "v"(lraw));

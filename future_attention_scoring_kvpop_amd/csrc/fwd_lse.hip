@@ -167,6 +167,12 @@ __global__ __launch_bounds__(kThreads, KVPOP_FWD_MIN_BLOCKS) void fwd_lse_kernel
 
   float m = -INFINITY, l = 0.f;
   const int sw = col & (CPR - 1);
+  // byte offset of this lane's A fragment of k-slice s within a 32-key
+  // sub-tile: loop-invariant, so each read is one ds_read whose immediate
+  // offset holds the stage and sub-tile base
+  uint32_t foff[NS];
+#pragma unroll
+  for (int s2 = 0; s2 < NS; ++s2) foff[s2] = col * ROWB + (((2 * s2 + half) ^ sw) << 4);
   auto step = [&](auto J, int i) {
     constexpr int j = decltype(J)::value;
     constexpr int jn = (j + kStages - 1) % kStages;
@@ -181,11 +187,10 @@ __global__ __launch_bounds__(kThreads, KVPOP_FWD_MIN_BLOCKS) void fwd_lse_kernel
     for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[sub][r] = 0.f;
-      const uint8_t* arow = tile + (sub * 32 + col) * ROWB;
+      const uint8_t* sbase = tile + sub * 32 * ROWB;
 #pragma unroll
       for (int s = 0; s < NS; ++s)
-        acc[sub] = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(arow + (((2 * s + half) ^ sw) << 4))),
-                          bq[s], acc[sub]);
+        acc[sub] = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(sbase + foff[s])), bq[s], acc[sub]);
     }
     if constexpr (SPARSE) {
       // key row of register r: t0 + 32 sub + 8 (r/4) + 4 half + r%4; its
