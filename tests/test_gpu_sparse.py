@@ -81,6 +81,24 @@ def test_running_topk_full_size(kv, S, budget, w):
         assert (live <= budget).all() and (live[budget - 1:] == np.minimum(d[budget - 1:] + 1, budget)).all()
 
 
+@pytest.mark.parametrize("S,budget,w,s", [(40000, 5000, 256, 4), (65536, 6000, 128, 70),
+                                          (33000, 300, 16, 0)])
+def test_running_topk_longest_rows(kv, S, budget, w, s):
+    """Rows past 32768 positions take 16 segment waves per token block (the
+    longest rows the kernel takes are 65536); a small budget makes most
+    tokens leave early, a large one keeps many to the end."""
+    sc = synth.scores((1, 2, S), seed=S + budget, kind="ties" if S == 33000 else "normal")
+    u, c, ou, oc = _topk(kv, sc, s, w, budget, [0.0, 2e-5])
+    assert np.array_equal(u, ou)
+    assert np.array_equal(c, oc)
+
+
+def test_running_topk_rejects_rows_past_its_limit(kv):
+    sc = torch.zeros((1, 1, 65537), dtype=torch.float32, device="cuda")
+    with pytest.raises(kv.KvpopError):
+        kv.running_topk(sc, 4, 16, 64)
+
+
 def _sparse_oracle_rows(q, k, sc, s, w, budget, lam, rows):
     return oracle.lse_sparse(f32(q), f32(k), sc.numpy(), s, w, budget,
                              log_decay=None if lam is None else np.asarray(lam, np.float32),
