@@ -11,13 +11,14 @@ this oracle at tiny sizes.
 
 Method source: "KVpop -- Key-Value Cache Compression with Predictive Online
 Pruning" (arXiv 2607.05061v2), paperlayer.ai summary: App. D.1-D.4 (target;
-D.3 sparse normalizer), App. C.1-C.2 (running top-k mask and its cutoffs),
+D.3 sparse normalizer), App. C.1-C.2 (running top-k mask and its cutoffs), App. A and E.3-E.4 (the
+delayed stateful mLSTM scorer),
 App. B.1-B.2 (aggregation, count normalisation), Sec. 3 and App. C.1
 (fixed-budget retention), App. E.2 and E.4 (scorer, delayed readout).
 
 Parity status per function (see the tests under tests/test_oracle_*.py):
   lse, future_mass, select, gather, decode_attend, mlp_score, cache_step,
-  running_topk, lse_sparse: pinned (brute force, closed forms, invariants,
+  running_topk, lse_sparse, mlstm_scores: pinned (brute force, closed forms, invariants,
   hand-worked fixtures).
 """
 import ctypes
@@ -51,9 +52,10 @@ def _lib():
         lib.oracle_cache_step.argtypes = [I, I, I, I, I, I, I, I, P, P, P, P, P, P, P]
         lib.oracle_running_topk.argtypes = [I, I, I, I, I, I, P, P, P, P]
         lib.oracle_lse_sparse.argtypes = [I, I, I, I, I, Dd, P, P, P, P, I, I, I, L, P, P, I]
+        lib.oracle_mlstm_scores.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P]
         for f in ("oracle_lse", "oracle_future_mass", "oracle_select", "oracle_decode_attend",
                   "oracle_mlp_score", "oracle_cache_step", "oracle_running_topk",
-                  "oracle_lse_sparse"):
+                  "oracle_lse_sparse", "oracle_mlstm_scores"):
             getattr(lib, f).restype = ctypes.c_int
         _LIB = lib
     return _LIB
@@ -215,6 +217,36 @@ def lse_sparse(q, k, scores, n_sink, window, budget, log_decay=None, scale=None,
                                     int(budget), n, rp, _ptr(out), _threads(nthreads)),
            "lse_sparse")
     return out.reshape(B, Hq, S) if rows is None else out
+
+
+MLSTM_KEYS = ("wk", "wr", "wv", "wi", "bi", "wf", "bf", "wo", "bo")
+
+
+def mlstm_scores(keys, values, params, window, want_state=False):
+    """Delayed stateful mLSTM scores (App. A, E.1, E.3, E.4).
+
+    keys, values [B,Hkv,n,D] (float values); params: dict of the headwise
+    weights (MLSTM_KEYS; Wk, Wr [Hkv,P,2D], Wv [Hkv,E,2D], wi, wf [Hkv,2D],
+    bi, bf, bo [Hkv], wo [Hkv,E]).  Token u is read out once token u + w has
+    entered the state; returns scores [B,Hkv,n] float64 (NaN where never read
+    out) and, with want_state, the final (C [B,Hkv,E,2P], n [B,Hkv,2P],
+    m [B,Hkv]).
+    """
+    k = _f32(keys)
+    v = _f32(values)
+    B, Hkv, n, D = k.shape
+    pr = {name: _f32(params[name]) for name in MLSTM_KEYS}
+    P = pr["wk"].shape[1]
+    E = pr["wv"].shape[1]
+    F = 2 * P
+    sc = np.empty((B, Hkv, n), np.float64)
+    st = np.empty((B, Hkv, E * F + F + 1), np.float64) if want_state else None
+    _check(_lib().oracle_mlstm_scores(B, Hkv, n, D, P, E, int(window), _ptr(k), _ptr(v),
+                                      *[_ptr(pr[name]) for name in MLSTM_KEYS], _ptr(sc),
+                                      None if st is None else _ptr(st)), "mlstm_scores")
+    if not want_state:
+        return sc
+    return sc, (st[..., :E * F].reshape(B, Hkv, E, F), st[..., E * F:E * F + F], st[..., -1])
 
 
 def gather(x, slot_pos):

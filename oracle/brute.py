@@ -177,3 +177,40 @@ def lse_masked(q, k, member, scale=None):
     G = z.shape[1] // member.shape[1]
     m = np.repeat(member, G, axis=1)
     return logsumexp(np.where(m, z, -np.inf), axis=-1)
+
+
+def mlstm_scores_unstabilised(keys, values, params, window):
+    """The delayed mLSTM scores from the unstabilised recurrence, float64:
+    C_q = sum_{t<=q} (prod_{j=t+1..q} sigmoid(f_j)) exp(i_t) val_t phi_t^T (same
+    for n), h = C_q r / max(|n_q . r|, 1), sigma = wo . silu(h) + bo.  The
+    stabiliser m scales C and n by exp(-m) and the floor by the same factor,
+    so both forms give the same h."""
+    k = np.asarray(keys, np.float64)
+    v = np.asarray(values, np.float64)
+    B, H, n, D = k.shape
+    pr = {name: np.asarray(val, np.float64) for name, val in params.items()}
+
+    def hh(z):
+        a = np.exp(z - z.max())
+        b = np.exp(-z - (-z).max())
+        return np.concatenate([a / a.sum(), b / b.sum()])
+
+    out = np.full((B, H, n), np.nan)
+    for b in range(B):
+        for h in range(H):
+            x = np.concatenate([k[b, h], v[b, h]], axis=-1)  # [n, 2D]
+            ig = x @ pr["wi"][h] + pr["bi"][h]
+            fg = x @ pr["wf"][h] + pr["bf"][h]
+            sf = 1.0 / (1.0 + np.exp(-fg))
+            phi = np.stack([hh(pr["wk"][h] @ x[t]) for t in range(n)])
+            val = x @ pr["wv"][h].T
+            for q in range(window, n):
+                u = q - window
+                decay = np.array([np.prod(sf[t + 1:q + 1]) for t in range(q + 1)])
+                wgt = decay * np.exp(ig[:q + 1])
+                C = (val[:q + 1] * wgt[:, None]).T @ phi[:q + 1]
+                nr = (phi[:q + 1] * wgt[:, None]).sum(0)
+                r = hh(pr["wr"][h] @ x[u])
+                hv = C @ r / max(abs(nr @ r), 1.0)
+                out[b, h, u] = pr["wo"][h] @ (hv / (1.0 + np.exp(-hv))) + pr["bo"][h]
+    return out

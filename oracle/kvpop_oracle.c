@@ -569,3 +569,123 @@ int oracle_lse_sparse(int B, int Hq, int Hkv, int S, int D, double scale,
     run_items(slse_item, &c, n_rows, nthreads, 2L * S + S / 8 + 4);
     return 0;
 }
+
+/* ------------------------------------------------------------------ */
+/* Delayed stateful mLSTM scorer (App. A linear-attention background;  */
+/* App. E.1 headwise input x = [k; v]; App. E.3 matrix memory C, norm- */
+/* alizer n, scalar input/forget gates from headwise projections, the  */
+/* stabilised mLSTM form, Hedgehog features; App. E.4 delayed readout  */
+/* of u = q - w from the state through q, SiLU readout with a bias).   */
+/* Per KV head h and token t, x_t = [k_t; v_t] (2D values):            */
+/*   hedgehog(z) = [softmax(z); softmax(-z)]         (2P features)     */
+/*   phi_t  = hedgehog(Wk x_t),  val_t = Wv x_t      (E values)        */
+/*   ig_t   = wi.x_t + bi,   lf_t = log sigmoid(wf.x_t + bf)          */
+/*   m_t    = max(lf_t + m_{t-1}, ig_t)              (m_{-1} = -inf)   */
+/*   C_t    = exp(lf_t + m_{t-1} - m_t) C_{t-1} + exp(ig_t - m_t) val_t phi_t^T */
+/*   n_t    = exp(lf_t + m_{t-1} - m_t) n_{t-1} + exp(ig_t - m_t) phi_t */
+/* After token q has entered, token u = q - w is read out:             */
+/*   r = hedgehog(Wr x_u),  h = C_q r / max(|n_q . r|, exp(-m_q))      */
+/*   sigma_u = wo . silu(h) + bo,   silu(a) = a / (1 + exp(-a))        */
+/* Weights per head: Wk, Wr [P][2D], Wv [E][2D], wi, wf [2D], bi, bf,  */
+/* wo [E], bo.  scores[u] is NaN for tokens never read out (u + w      */
+/* beyond the last token).  state_out: nullable [B][Hkv][E*2P+2P+1],   */
+/* the final (C row-major [E][2P], n, m).                              */
+/* ------------------------------------------------------------------ */
+static void hedgehog(const double* z, int P, double* phi) {
+    double mx = -INFINITY, mn = INFINITY;
+    for (int j = 0; j < P; ++j) { if (z[j] > mx) mx = z[j]; if (z[j] < mn) mn = z[j]; }
+    double sp = 0.0, sn = 0.0;
+    for (int j = 0; j < P; ++j) { sp += exp(z[j] - mx); sn += exp(mn - z[j]); }
+    for (int j = 0; j < P; ++j) { phi[j] = exp(z[j] - mx) / sp; phi[P + j] = exp(mn - z[j]) / sn; }
+}
+
+static double log_sigmoid(double a) {
+    /* log(1 / (1 + exp(-a))), evaluated without overflow */
+    return a >= 0 ? -log1p(exp(-a)) : a - log1p(exp(a));
+}
+
+int oracle_mlstm_scores(int B, int Hkv, int n_tok, int D, int P, int E, int window,
+                        const float* keys, const float* values,
+                        const float* wk, const float* wr, const float* wv,
+                        const float* wi, const float* bi, const float* wf, const float* bf,
+                        const float* wo, const float* bo, double* scores, double* state_out) {
+    if (B <= 0 || Hkv <= 0 || n_tok < 0 || D <= 0 || P <= 0 || E <= 0 || window < 0) return 1;
+    const int X = 2 * D, F = 2 * P;
+    double* x = (double*)malloc(sizeof(double) * (size_t)X * (n_tok > 0 ? n_tok : 1));
+    double* C = (double*)malloc(sizeof(double) * (size_t)E * F);
+    double* nrm = (double*)malloc(sizeof(double) * F);
+    double* z = (double*)malloc(sizeof(double) * P);
+    double* phi = (double*)malloc(sizeof(double) * F);
+    double* val = (double*)malloc(sizeof(double) * E);
+    double* r = (double*)malloc(sizeof(double) * F);
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < Hkv; ++h) {
+            long row = (long)b * Hkv + h;
+            for (int t = 0; t < n_tok; ++t) {
+                const float* kt = keys + (row * n_tok + t) * D;
+                const float* vt = values + (row * n_tok + t) * D;
+                for (int c = 0; c < D; ++c) { x[(long)t * X + c] = kt[c]; x[(long)t * X + D + c] = vt[c]; }
+            }
+            for (int i = 0; i < E * F; ++i) C[i] = 0.0;
+            for (int j = 0; j < F; ++j) nrm[j] = 0.0;
+            double m = -INFINITY;
+            for (int t = 0; t < n_tok; ++t) scores[row * n_tok + t] = NAN;
+            for (int q = 0; q < n_tok; ++q) {
+                const double* xq = x + (long)q * X;
+                /* projections of the entering token */
+                for (int j = 0; j < P; ++j) {
+                    double s = 0.0;
+                    for (int c = 0; c < X; ++c) s += (double)wk[((long)h * P + j) * X + c] * xq[c];
+                    z[j] = s;
+                }
+                hedgehog(z, P, phi);
+                for (int e = 0; e < E; ++e) {
+                    double s = 0.0;
+                    for (int c = 0; c < X; ++c) s += (double)wv[((long)h * E + e) * X + c] * xq[c];
+                    val[e] = s;
+                }
+                double ig = bi[h], fg = bf[h];
+                for (int c = 0; c < X; ++c) {
+                    ig += (double)wi[(long)h * X + c] * xq[c];
+                    fg += (double)wf[(long)h * X + c] * xq[c];
+                }
+                double lf = log_sigmoid(fg);
+                double m_new = lf + m > ig ? lf + m : ig;
+                double fs = exp(lf + m - m_new); /* 0 for the first token */
+                double is = exp(ig - m_new);
+                for (int e = 0; e < E; ++e)
+                    for (int j = 0; j < F; ++j) C[e * F + j] = fs * C[e * F + j] + is * val[e] * phi[j];
+                for (int j = 0; j < F; ++j) nrm[j] = fs * nrm[j] + is * phi[j];
+                m = m_new;
+                /* delayed readout of u = q - w */
+                int u = q - window;
+                if (u < 0) continue;
+                const double* xu = x + (long)u * X;
+                for (int j = 0; j < P; ++j) {
+                    double s = 0.0;
+                    for (int c = 0; c < X; ++c) s += (double)wr[((long)h * P + j) * X + c] * xu[c];
+                    z[j] = s;
+                }
+                hedgehog(z, P, r);
+                double nr = 0.0;
+                for (int j = 0; j < F; ++j) nr += nrm[j] * r[j];
+                double den = fabs(nr) > exp(-m) ? fabs(nr) : exp(-m);
+                double sc = bo[h];
+                for (int e = 0; e < E; ++e) {
+                    double a = 0.0;
+                    for (int j = 0; j < F; ++j) a += C[e * F + j] * r[j];
+                    a /= den;
+                    sc += (double)wo[(long)h * E + e] * (a / (1.0 + exp(-a)));
+                }
+                scores[row * n_tok + u] = sc;
+            }
+            if (state_out) {
+                double* so = state_out + row * ((long)E * F + F + 1);
+                for (int i = 0; i < E * F; ++i) so[i] = C[i];
+                for (int j = 0; j < F; ++j) so[E * F + j] = nrm[j];
+                so[E * F + F] = m;
+            }
+        }
+    free(x); free(C); free(nrm); free(z); free(phi); free(val); free(r);
+    return 0;
+}
