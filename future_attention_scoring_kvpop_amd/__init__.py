@@ -29,13 +29,21 @@ OP_FWD_LSE = 2
 EXPORTS = ("kvpop_abi_version", "kvpop_status_string", "kvpop_workspace_bytes", "kvpop_fwd_lse",
            "kvpop_future_attn_target", "kvpop_evict_select", "kvpop_decode_attend",
            "kvpop_score_mlp", "kvpop_cache_step", "kvpop_decode_step", "kvpop_running_topk",
-           "kvpop_fwd_lse_sparse")
+           "kvpop_fwd_lse_sparse", "kvpop_mlstm_step")
 
 
 class KvpopError(RuntimeError):
     def __init__(self, fn, status):
         super().__init__(f"{fn}: {STATUS.get(status, status)} (status {status})")
         self.status = status
+
+
+class MlstmWeights(ctypes.Structure):
+    _fields_ = [("feat", ctypes.c_int), ("vdim", ctypes.c_int)] + [
+        (n, ctypes.c_void_p) for n in ("wk", "wr", "wv", "wi", "bi", "wf", "bf", "wo", "bo")]
+
+
+MLSTM_STATE_FLOATS = 64 * 64 + 64 + 4
 
 
 class Dims(ctypes.Structure):
@@ -62,6 +70,8 @@ def lib():
             "kvpop_workspace_bytes": (Z, [I, DP, I]),
             "kvpop_fwd_lse": (I, [DP, P, P, P, P, Z, P]),
             "kvpop_running_topk": (I, [I, I, I, I, I, I, P, P, P, P, P]),
+            "kvpop_mlstm_step": (I, [I, I, I, I, I, I, I, P, P, P, P, ctypes.POINTER(MlstmWeights),
+                                     P, P, P]),
             "kvpop_fwd_lse_sparse": (I, [DP, P, P, P, P, P, Z, P]),
             "kvpop_future_attn_target": (I, [DP, P, P, P, I, I, I, I, P, P, P, Z, P]),
             "kvpop_evict_select": (I, [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P]),
@@ -156,6 +166,43 @@ def running_topk(scores, n_sink, window, budget, log_decay=None, want_cutoff=Tru
                                   _p(log_decay), _p(until), _p(cut), _stream())
     _check("kvpop_running_topk", st)
     return until, cut
+
+
+def mlstm_state(B, Hkv, device="cuda"):
+    """An empty mLSTM scorer state [B,Hkv,MLSTM_STATE_FLOATS]: C = 0, n = 0, m = -inf."""
+    st = torch.zeros((B, Hkv, MLSTM_STATE_FLOATS), dtype=torch.float32, device=device)
+    st[..., 64 * 64 + 64] = float("-inf")
+    return st
+
+
+def mlstm_step(k_new, v_new, params, state, pos_q, n_sink, window, k_cache=None, v_cache=None,
+               slot_score=None):
+    """One step of the delayed stateful mLSTM scorer (App. A, E.1, E.3, E.4):
+    token pos_q enters the state; with slot_score (and the caches), token
+    pos_q - w is read out into its ring slot's score.  params: dict of fp32
+    device tensors wk, wr [Hkv,32,2D], wv [Hkv,64,2D], wi, wf [Hkv,2D],
+    bi, bf, bo [Hkv], wo [Hkv,64]."""
+    _need(k_new, torch.bfloat16, "k_new", 3)
+    _need(v_new, torch.bfloat16, "v_new", 3)
+    _need(state, torch.float32, "state", 3)
+    B, Hkv, D = k_new.shape
+    budget = 0
+    if slot_score is not None:
+        _need(slot_score, torch.float32, "slot_score", 3)
+        _need(k_cache, torch.bfloat16, "k_cache", 4)
+        _need(v_cache, torch.bfloat16, "v_cache", 4)
+        budget = slot_score.shape[-1]
+    elif k_cache is not None:
+        budget = k_cache.shape[2]
+    for n in ("wk", "wr", "wv", "wi", "bi", "wf", "bf", "wo", "bo"):
+        _need(params[n], torch.float32, n)
+    w = MlstmWeights(params["wk"].shape[1], params["wv"].shape[1],
+                     *[params[n].data_ptr() for n in ("wk", "wr", "wv", "wi", "bi", "wf", "bf", "wo", "bo")])
+    st = lib().kvpop_mlstm_step(B, Hkv, D, int(n_sink), int(window),
+                                int(budget) if budget else int(n_sink) + int(window), int(pos_q),
+                                _p(k_new), _p(v_new), _p(k_cache), _p(v_cache), ctypes.byref(w),
+                                _p(state), _p(slot_score), _stream())
+    _check("kvpop_mlstm_step", st)
 
 
 def fwd_lse_sparse(q, k, keep_until, scale=0.0, out=None, workspace=None):

@@ -18,7 +18,7 @@ LIB = os.path.join(PKG, "libkvpop.so")
 ARCH = os.environ.get("KVPOP_ARCH", "gfx950")
 
 SOURCES = ["api.hip", "fwd_lse.hip", "future_target.hip", "select.hip", "decode.hip",
-           "cache_step.hip", "decode_step.hip", "running_topk.hip"]
+           "cache_step.hip", "decode_step.hip", "running_topk.hip", "mlstm.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,

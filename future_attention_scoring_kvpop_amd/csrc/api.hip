@@ -88,6 +88,33 @@ kvpop_status kvpop_fwd_lse(const kvpop_dims* dims, const void* q, const void* k,
   return from_hip(kvpop::launch_fwd_lse(s, q, k, nullptr, lse, (float*)workspace, stream));
 }
 
+kvpop_status kvpop_mlstm_step(int batch, int n_kv_heads, int head_dim, int n_sink, int window,
+                              int budget, int pos_q, const void* k_new, const void* v_new,
+                              const void* k_cache, const void* v_cache,
+                              const kvpop_mlstm_weights* w, float* state, float* slot_score,
+                              hipStream_t stream) {
+  if (batch <= 0 || n_kv_heads <= 0 || n_sink < 0 || window < 1 || pos_q < 0)
+    return KVPOP_ERR_INVALID_ARGUMENT;
+  if (budget < n_sink + window) return KVPOP_ERR_INVALID_ARGUMENT;
+  if (head_dim != 64 && head_dim != 128) return KVPOP_ERR_UNSUPPORTED;
+  if (!w || !k_new || !v_new || !state) return KVPOP_ERR_INVALID_ARGUMENT;
+  if (w->feat != kvpop::kMlstmFeat || w->vdim != kvpop::kMlstmVdim) return KVPOP_ERR_UNSUPPORTED;
+  const float* ws[9] = {w->wk, w->wr, w->wv, w->wi, w->bi, w->wf, w->bf, w->wo, w->bo};
+  for (const float* p : ws)
+    if (!p || !aligned(p, 4)) return KVPOP_ERR_INVALID_ARGUMENT;
+  if (slot_score && (!k_cache || !v_cache || !aligned(slot_score, 4) || !aligned(k_cache, 2) ||
+                     !aligned(v_cache, 2)))
+    return KVPOP_ERR_INVALID_ARGUMENT;
+  if (!aligned(k_new, 2) || !aligned(v_new, 2) || !aligned(state, 16))
+    return KVPOP_ERR_INVALID_ARGUMENT;
+  if ((double)batch * n_kv_heads > 2.0e9 || (double)batch * n_kv_heads * budget * head_dim > 9.0e15)
+    return KVPOP_ERR_UNSUPPORTED;
+  const kvpop::MlstmWeights mw{w->wk, w->wr, w->wv, w->wi, w->bi, w->wf, w->bf, w->wo, w->bo};
+  return from_hip(kvpop::launch_mlstm_step(batch, n_kv_heads, head_dim, n_sink, window, budget,
+                                           pos_q, k_new, v_new, k_cache, v_cache, mw, state,
+                                           slot_score, stream));
+}
+
 kvpop_status kvpop_running_topk(int batch, int n_kv_heads, int seq_len, int n_sink, int window,
                                 int budget, const float* scores, const float* log_decay,
                                 int32_t* keep_until, int32_t* cutoff, hipStream_t stream) {
@@ -224,7 +251,7 @@ kvpop_status kvpop_cache_step(int batch, int n_kv_heads, int head_dim, int n_sin
   if (!k_new || !v_new || !k_cache || !v_cache || !slot_pos || !slot_score)
     return KVPOP_ERR_INVALID_ARGUMENT;
   const bool mlp = w1 != nullptr;
-  if (mlp == (scores_r != nullptr)) return KVPOP_ERR_INVALID_ARGUMENT;
+  if (mlp && scores_r) return KVPOP_ERR_INVALID_ARGUMENT;
   if (mlp && (!b1 || !w2 || !b2)) return KVPOP_ERR_INVALID_ARGUMENT;
   if (mlp && (hidden < 1 || hidden > 64)) return KVPOP_ERR_UNSUPPORTED;
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
@@ -253,7 +280,7 @@ kvpop_status kvpop_decode_step(const kvpop_dims* dims, int n_sink, int window, i
     return KVPOP_ERR_INVALID_ARGUMENT;
   if (o_dtype != KVPOP_OUT_F32 && o_dtype != KVPOP_OUT_BF16) return KVPOP_ERR_INVALID_ARGUMENT;
   const bool mlp = w1 != nullptr;
-  if (mlp == (scores_r != nullptr)) return KVPOP_ERR_INVALID_ARGUMENT;
+  if (mlp && scores_r) return KVPOP_ERR_INVALID_ARGUMENT;
   if (mlp && (!b1 || !w2 || !b2)) return KVPOP_ERR_INVALID_ARGUMENT;
   if (mlp && (hidden < 1 || hidden > 64)) return KVPOP_ERR_UNSUPPORTED;
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||

@@ -116,7 +116,8 @@ __device__ __forceinline__ void cache_step_row(
   const int ring_u = n_sink + kk + ((u % window) + window) % window;
   const int slot = q < n_sink ? q : n_sink + kk + (q % window);  // where q is written
   const int r = q - delay;                // the token scored at this step
-  const bool scoring = r >= n_sink;
+  // no scorer given (neither weights nor a score): nothing is scored here
+  const bool scoring = r >= n_sink && (w1 != nullptr || scores_r != nullptr);
   const int rslot = n_sink + kk + ((r % window) + window) % window;
   const bool use_mlp = scoring && w1 != nullptr;
 

@@ -28,6 +28,18 @@ FwdPlan plan_fwd(const AttnShape& s);
 hipError_t launch_fwd_lse(const AttnShape& s, const void* q, const void* k, const int* keep_until,
                           float* lse, float* workspace, hipStream_t st);
 
+// ---- delayed stateful mLSTM scorer (one decoding step) ----
+constexpr int kMlstmFeat = 32;   // projected features per Hedgehog half
+constexpr int kMlstmVdim = 64;   // value features
+constexpr int kMlstmStateFloats = kMlstmVdim * 2 * kMlstmFeat + 2 * kMlstmFeat + 4;  // C, n, m, pad
+struct MlstmWeights {
+  const float *wk, *wr, *wv, *wi, *bi, *wf, *bf, *wo, *bo;
+};
+hipError_t launch_mlstm_step(int B, int Hkv, int D, int n_sink, int window, int budget, int pos_q,
+                             const void* k_new, const void* v_new, const void* kc, const void* vc,
+                             const MlstmWeights& w, float* state, float* slot_score,
+                             hipStream_t st);
+
 // ---- running top-k mask ----
 int running_topk_max_len();  // longest row the kernel takes
 hipError_t launch_running_topk(int B, int Hkv, int S, int n_sink, int window, int budget,

@@ -234,11 +234,13 @@ kvpop_status kvpop_score_mlp(int batch, int n_kv_heads, int n_tok, int head_dim,
  *      ring slot s + k + (pos_q mod w), its score set to quiet NaN.
  *  (c) delayed scoring: token r = pos_q - delay (when r >= s) receives its
  *      score in its ring slot: the MLP of kvpop_score_mlp on its cached key
- *      when w1 != NULL, else scores_r[b][h].
+ *      when w1 != NULL, else scores_r[b][h]; with neither, nothing is scored
+ *      here (for scorers that score the exiting token themselves before the
+ *      step, such as kvpop_mlstm_step).
  *   k_new, v_new: bf16 [B][Hkv][D]; the cache state (k_cache, v_cache bf16
  *   [B][Hkv][budget][D], slot_pos int32 and slot_score fp32
  *   [B][Hkv][budget]) is updated in place.  Requires w >= 1,
- *   0 <= delay < w, and exactly one of {w1 (with b1, w2, b2, hidden)} and
+ *   0 <= delay < w, and at most one of {w1 (with b1, w2, b2, hidden)} and
  *   scores_r.
  * Bit-exact and deterministic given the same scores.
  */
@@ -248,6 +250,46 @@ kvpop_status kvpop_cache_step(int batch, int n_kv_heads, int head_dim, int n_sin
                               const float* w2, const float* b2, int hidden,
                               const float* scores_r, void* k_cache, void* v_cache,
                               int32_t* slot_pos, float* slot_score, hipStream_t stream);
+
+/*
+ * kvpop_mlstm_step -- one decoding step of the delayed stateful mLSTM scorer.
+ * App. A (a running key-value summary and normalizer updated by rank-one
+ * outer products), App. E.1 (headwise input x = [k; v]), App. E.3 (mLSTM
+ * matrix memory C and normalizer n with scalar input and forget gates from
+ * headwise projections, stabilised form, Hedgehog features), App. E.4 (at
+ * query q the state has taken tokens through q and the newly eligible
+ * token u = q - w is read out).  Per (b, h), with x_q = [k_new; v_new]:
+ *   hedgehog(z) = [softmax(z); softmax(-z)]
+ *   phi = hedgehog(Wk x_q), val = Wv x_q, ig = wi.x_q + bi,
+ *   lf = log sigmoid(wf.x_q + bf), m' = max(lf + m, ig),
+ *   C' = e^(lf + m - m') C + e^(ig - m') val phi^T,  n' likewise with phi;
+ * then, when slot_score != NULL and u = pos_q - w >= s, with x_u = the
+ * cached [K; V] rows of u's ring slot s + k + (u mod w):
+ *   r = hedgehog(Wr x_u), h = C' r / max(|n'.r|, e^(-m')),
+ *   slot_score[b][h][ring slot of u] = wo.silu(h) + bo.
+ * Called before kvpop_cache_step of the same position with no scorer, it
+ * gives the exit decision of u the score from the state through pos_q.
+ *   w: feat = 32 (P), vdim = 64 (E); Wk, Wr fp32 [Hkv][P][2D], Wv
+ *      [Hkv][E][2D], wi, wf [Hkv][2D], bi, bf, bo [Hkv], wo [Hkv][E].
+ *   state: fp32 [B][Hkv][KVPOP_MLSTM_STATE_FLOATS], 16-byte aligned: C
+ *      row-major [E][2P], then n [2P], then m, then 3 unused floats.  An
+ *      empty state is C = 0, n = 0, m = -inf; it is updated in place.
+ *   k_cache, v_cache: bf16 [B][Hkv][budget][D], read only (u's ring slot).
+ *   slot_score: nullable fp32 [B][Hkv][budget]; NULL updates the state only.
+ * Errors: INVALID_ARGUMENT for non-positive sizes, w < 1, budget < s + w,
+ * pos_q < 0, NULL or misaligned pointers; UNSUPPORTED for D not 64 or 128
+ * or other feature sizes.  fp32 arithmetic; deterministic.
+ */
+#define KVPOP_MLSTM_STATE_FLOATS (64 * 64 + 64 + 4)
+typedef struct {
+    int feat, vdim;
+    const float *wk, *wr, *wv, *wi, *bi, *wf, *bf, *wo, *bo;
+} kvpop_mlstm_weights;
+kvpop_status kvpop_mlstm_step(int batch, int n_kv_heads, int head_dim, int n_sink, int window,
+                              int budget, int pos_q, const void* k_new, const void* v_new,
+                              const void* k_cache, const void* v_cache,
+                              const kvpop_mlstm_weights* w, float* state, float* slot_score,
+                              hipStream_t stream);
 
 /*
  * kvpop_decode_step -- one bounded-cache decode step, then decode attention

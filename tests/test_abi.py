@@ -127,7 +127,7 @@ def test_mlp_and_cache_step_validation(lib):
     assert step(budget=200) == 1
     assert step(pos=-1) == 1
     assert step(w1=GOOD) == 1                 # both an MLP and given scores
-    assert step(w1=None, sr=None) == 1        # neither
+    # neither is valid (no delayed scoring): it passes validation and would launch
     assert step(w1=GOOD, sr=None, hidden=65) == 2
 
 
@@ -145,7 +145,6 @@ def test_decode_step_validation(lib):
     assert call(q=None) == 1
     assert call(o_dtype=2) == 1
     assert call(w1=GOOD) == 1                 # both an MLP and given scores
-    assert call(w1=None, sr=None) == 1        # neither
     assert call(w1=GOOD, sr=None, hidden=65) == 2
     assert call(d=kv.dims(64, 32, 8, 200, 128)) == 1  # budget < s + w
     assert call(d=kv.dims(64, 32, 8, 4096, 96)) == 2  # head dim
@@ -181,3 +180,30 @@ def test_running_topk_and_sparse_lse_validation(lib):
     need = lib.kvpop_workspace_bytes(2, ctypes.byref(d), 0)
     if need:
         assert sp(ctypes.byref(d), GOOD, GOOD, GOOD, GOOD, GOOD, need - 16, None) == 3
+
+
+def test_mlstm_step_validation(lib):
+    def weights(feat=32, vdim=64, missing=None):
+        ptrs = {n: 0x10000 for n in ("wk", "wr", "wv", "wi", "bi", "wf", "bf", "wo", "bo")}
+        if missing:
+            ptrs[missing] = None
+        return kv.MlstmWeights(feat, vdim, *[ptrs[n] for n in ("wk", "wr", "wv", "wi", "bi", "wf",
+                                                               "bf", "wo", "bo")])
+
+    def call(w=None, D=128, window=256, budget=4096, pos=40000, state=GOOD, ss=GOOD, kc=GOOD):
+        w = w if w is not None else weights()
+        return lib.kvpop_mlstm_step(64, 8, D, 4, window, budget, pos, GOOD, GOOD, kc, kc,
+                                    ctypes.byref(w), state, ss, None)
+
+    assert call(window=0) == 1
+    assert call(budget=200) == 1
+    assert call(pos=-1) == 1
+    assert call(D=96) == 2
+    assert call(w=weights(feat=16)) == 2
+    assert call(w=weights(vdim=32)) == 2
+    assert call(w=weights(missing="wo")) == 1
+    assert call(state=None) == 1
+    assert call(state=P(0x10004)) == 1        # state rows need 16-byte alignment
+    assert call(kc=None) == 1                 # a readout needs the caches
+    assert lib.kvpop_mlstm_step(64, 8, 128, 4, 256, 4096, 0, GOOD, GOOD, GOOD, GOOD, None, GOOD,
+                                GOOD, None) == 1
