@@ -523,6 +523,40 @@ def bench_decode(kv, steps, layers, seed=5):
     # positions after the fused run (kvpop_decode_step, the primary figure)
     ms, wall = timed(one_fused_step, S, "fused decode step")
     ms_two, _ = timed(one_step, S + steps, "cache step + attention")
+
+    # the same decode with the delayed stateful mLSTM scorer in place of the
+    # MLP: per layer, the scorer takes the new token and scores the exiting
+    # one (kvpop_mlstm_step), then kvpop_decode_step with no scorer of its own
+    # keeps or drops it and attends.  Random-init scorer per layer (weights
+    # N(0, 1/fan_in), forget-gate bias +3, input-gate bias 0); its state
+    # starts empty at the first timed step (the per-step work does not depend
+    # on the state's contents).
+    mls, states = [], []
+    for layer in range(layers):
+        g = torch.Generator(device=dev)
+        g.manual_seed(7000 + layer)
+        X = 2 * D
+        r = lambda *sh: torch.randn(sh, generator=g, device=dev, dtype=torch.float32)
+        mls.append({"wk": r(Hkv, 32, X) / X ** 0.5, "wr": r(Hkv, 32, X) / X ** 0.5,
+                    "wv": r(Hkv, 64, X) / X ** 0.5, "wi": r(Hkv, X) / X ** 0.5,
+                    "bi": torch.zeros(Hkv, device=dev), "wf": r(Hkv, X) / X ** 0.5,
+                    "bf": torch.full((Hkv,), 3.0, device=dev), "wo": r(Hkv, 64) / 8.0,
+                    "bo": torch.zeros(Hkv, device=dev)})
+        states.append(kv.mlstm_state(B, Hkv, device=dev))
+
+    def one_mlstm_step(i, pos):
+        for layer in range(layers):
+            kc, vc, sp, ss = caches[layer]
+            kv.mlstm_step(ks[i, layer], vs[i, layer], mls[layer], states[layer], pos, w.n_sink,
+                          w.window, kc, vc, ss)
+            kv.decode_step(qs[i, layer], kc, vc, sp, ss, ks[i, layer], vs[i, layer], pos, w.n_sink,
+                           w.window, 0, out_dtype=torch.bfloat16, want_lse=False, out=o,
+                           workspace=dws)
+
+    for i in range(2):  # warm-up of the new kernel
+        one_mlstm_step(i, S + 2 * steps + i)
+    ms_ml, _ = timed(one_mlstm_step, S + 2 * steps + 2, "mLSTM scorer + decode step")
+    ml_extra = layers * B * Hkv * (2 * 4 * (64 * 64 + 64 + 4) + 2 * D * 2)  # state r+w, x_u
     sps = steps / (ms / 1e3)
     by = decode_bytes_per_step(w, layers)
     att_bytes = B * Hkv * 2 * bud * D * 2 + B * Hq * D * 2 * 2
@@ -538,6 +572,12 @@ def bench_decode(kv, steps, layers, seed=5):
                       "value": steps / (ms_two / 1e3), "unit": "steps/s",
                       "ms_per_step": ms_two / steps,
                       "hbm_frac": by * steps / (ms_two / 1e3) / 1e9 / HBM_PEAK_GBS},
+        "mlstm_scorer": {"entry_points": "kvpop_mlstm_step + kvpop_decode_step (no scorer)",
+                         "value": steps / (ms_ml / 1e3), "unit": "steps/s",
+                         "ms_per_step": ms_ml / steps, "bytes_per_step": by + ml_extra,
+                         "hbm_frac": (by + ml_extra) * steps / (ms_ml / 1e3) / 1e9 / HBM_PEAK_GBS,
+                         "note": "scorer state 16.7 KB per (sequence, layer, KV head) read and "
+                                 "written per step; random-init weights"},
         "attend_kernel": {"ms": t_att_ms, "bytes": att_bytes,
                           "achieved": att_bytes / (t_att_ms / 1e3) / 1e9, "unit": "GB/s",
                           "frac": att_bytes / (t_att_ms / 1e3) / 1e9 / HBM_PEAK_GBS},
