@@ -310,13 +310,14 @@ def bench_running_topk_long(kv, w, reps=5):
             "ms": a.elapsed_time(b) / reps}
 
 
-def bench_prefill(kv, w, layers=None, reps=1, seed=None):
+def bench_prefill(kv, w, layers=None, reps=1, seed=None, warm=1):
     """The target pipeline on a long-context workload: per layer the causal
     LSE pass, the transposed future-attention pass (SUM over the group) and
     retention + compaction of K/V to the budget, over every layer's own
     resident inputs (generated before the timed region, one seed per layer:
-    3000 + l for the skewed workload, 4000 + l for the 36-layer prefill).  Each pass is timed by its own events; after one
-    untimed warm-up layer, `reps` passes over all layers are timed.
+    3000 + l for the skewed workload, 4000 + l for the 36-layer prefill).
+    Each pass is timed by its own events; after `warm` untimed warm-up
+    layers, `reps` passes over all layers are timed.
     keys/s = layers * B * Hkv * S / (time of one pass over the layers)."""
     dev = torch.device("cuda")
     layers = layers or w.layers
@@ -348,7 +349,8 @@ def bench_prefill(kv, w, layers=None, reps=1, seed=None):
         if ev:
             ev[3].record()
 
-    layer(0)
+    for i in range(warm):
+        layer(i % layers)
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps * layers)]
     a = torch.cuda.Event(enable_timing=True)
@@ -773,8 +775,8 @@ def main():
     log("sparse normalizer: running top-k mask, sparse causal pass, transposed pass")
     out["sparse_normalizer"] = bench_sparse(kv, st)
     if not a.no_long:
-        log("skewed-long: 4 x 16384, 2 timed passes")
-        out["skewed_long"] = bench_prefill(kv, synth.SKEWED, reps=2)
+        log("skewed-long: 4 x 16384, 3 warm-up and 4 timed passes")
+        out["skewed_long"] = bench_prefill(kv, synth.SKEWED, reps=4, warm=3)
         log("qwen3-8b-prefill: 36 layers x 32768, 1 timed pass")
         out["prefill_36_layers"] = bench_prefill(kv, synth.QWEN8B, reps=1)
         out["prefill_36_layers"]["running_topk_one_layer"] = bench_running_topk_long(kv, synth.QWEN8B)
