@@ -29,7 +29,7 @@ OP_FWD_LSE = 2
 EXPORTS = ("kvpop_abi_version", "kvpop_status_string", "kvpop_workspace_bytes", "kvpop_fwd_lse",
            "kvpop_future_attn_target", "kvpop_evict_select", "kvpop_decode_attend",
            "kvpop_score_mlp", "kvpop_cache_step", "kvpop_decode_step", "kvpop_running_topk",
-           "kvpop_fwd_lse_sparse", "kvpop_mlstm_step")
+           "kvpop_fwd_lse_sparse", "kvpop_mlstm_step", "kvpop_decode_step_mlstm")
 
 
 class KvpopError(RuntimeError):
@@ -72,6 +72,8 @@ def lib():
             "kvpop_running_topk": (I, [I, I, I, I, I, I, P, P, P, P, P]),
             "kvpop_mlstm_step": (I, [I, I, I, I, I, I, I, P, P, P, P, ctypes.POINTER(MlstmWeights),
                                      P, P, P]),
+            "kvpop_decode_step_mlstm": (I, [DP, I, I, I, P, P, ctypes.POINTER(MlstmWeights), P, P, P,
+                                            P, P, P, P, I, P, P, Z, P]),
             "kvpop_fwd_lse_sparse": (I, [DP, P, P, P, P, P, Z, P]),
             "kvpop_future_attn_target": (I, [DP, P, P, P, I, I, I, I, P, P, P, Z, P]),
             "kvpop_evict_select": (I, [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P]),
@@ -203,6 +205,47 @@ def mlstm_step(k_new, v_new, params, state, pos_q, n_sink, window, k_cache=None,
                                 _p(k_new), _p(v_new), _p(k_cache), _p(v_cache), ctypes.byref(w),
                                 _p(state), _p(slot_score), _stream())
     _check("kvpop_mlstm_step", st)
+
+
+def _mlstm_weights(params):
+    names = ("wk", "wr", "wv", "wi", "bi", "wf", "bf", "wo", "bo")
+    for n in names:
+        _need(params[n], torch.float32, n)
+    return MlstmWeights(params["wk"].shape[1], params["wv"].shape[1],
+                        *[params[n].data_ptr() for n in names])
+
+
+def decode_step_mlstm(q, k_cache, v_cache, slot_pos, slot_score, k_new, v_new, params, state,
+                      pos_q, n_sink, window, out_dtype=torch.float32, want_lse=True, scale=0.0,
+                      out=None, out_lse=None, workspace=None):
+    """mlstm_step, cache_step with no scorer and decode_attend in one call
+    (App. E.3-E.4, Sec. 3, App. C.1): o [B,Hq,D], lse [B,Hq]."""
+    _need(q, torch.bfloat16, "q", 3)
+    _need(k_cache, torch.bfloat16, "k_cache", 4)
+    _need(v_cache, torch.bfloat16, "v_cache", 4)
+    _need(slot_pos, torch.int32, "slot_pos", 3)
+    _need(slot_score, torch.float32, "slot_score", 3)
+    _need(k_new, torch.bfloat16, "k_new", 3)
+    _need(v_new, torch.bfloat16, "v_new", 3)
+    _need(state, torch.float32, "state", 3)
+    B, Hq, D = q.shape
+    Hkv, budget = k_cache.shape[1], k_cache.shape[2]
+    w = _mlstm_weights(params)
+    d = dims(B, Hq, Hkv, budget, D, scale)
+    o = out if out is not None else torch.empty((B, Hq, D), dtype=out_dtype, device=q.device)
+    lse = out_lse if out_lse is not None else (
+        torch.empty((B, Hq), dtype=torch.float32, device=q.device) if want_lse else None)
+    nbytes = workspace_bytes(OP_DECODE, d)
+    ws = workspace if workspace is not None else (
+        torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None)
+    st = lib().kvpop_decode_step_mlstm(ctypes.byref(d), int(n_sink), int(window), int(pos_q),
+                                       _p(k_new), _p(v_new), ctypes.byref(w), _p(state),
+                                       _p(k_cache), _p(v_cache), _p(slot_pos), _p(slot_score),
+                                       _p(q), _p(o), 1 if o.dtype == torch.bfloat16 else 0, _p(lse),
+                                       _p(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                       _stream())
+    _check("kvpop_decode_step_mlstm", st)
+    return o, lse
 
 
 def fwd_lse_sparse(q, k, keep_until, scale=0.0, out=None, workspace=None):

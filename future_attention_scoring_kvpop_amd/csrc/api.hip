@@ -115,6 +115,41 @@ kvpop_status kvpop_mlstm_step(int batch, int n_kv_heads, int head_dim, int n_sin
                                            slot_score, stream));
 }
 
+kvpop_status kvpop_decode_step_mlstm(const kvpop_dims* dims, int n_sink, int window, int pos_q,
+                                     const void* k_new, const void* v_new,
+                                     const kvpop_mlstm_weights* w, float* state, void* k_cache,
+                                     void* v_cache, int32_t* slot_pos, float* slot_score,
+                                     const void* q, void* o, kvpop_out_dtype o_dtype, float* lse,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  AttnShape s;
+  kvpop_status st = check_dims(dims, &s);
+  if (st != KVPOP_OK) return st;
+  const int budget = s.S;
+  if (n_sink < 0 || window < 1 || budget < n_sink + window || pos_q < 0)
+    return KVPOP_ERR_INVALID_ARGUMENT;
+  if (!w || !k_new || !v_new || !state || !k_cache || !v_cache || !slot_pos || !slot_score || !q ||
+      !o)
+    return KVPOP_ERR_INVALID_ARGUMENT;
+  if (o_dtype != KVPOP_OUT_F32 && o_dtype != KVPOP_OUT_BF16) return KVPOP_ERR_INVALID_ARGUMENT;
+  if (w->feat != kvpop::kMlstmFeat || w->vdim != kvpop::kMlstmVdim) return KVPOP_ERR_UNSUPPORTED;
+  const float* ws[9] = {w->wk, w->wr, w->wv, w->wi, w->bi, w->wf, w->bf, w->wo, w->bo};
+  for (const float* p : ws)
+    if (!p || !aligned(p, 4)) return KVPOP_ERR_INVALID_ARGUMENT;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(slot_pos, 4) || !aligned(slot_score, 4) ||
+      !aligned(state, 16) || !aligned(q, 16) || !aligned(o, 4) || (lse && !aligned(lse, 4)))
+    return KVPOP_ERR_INVALID_ARGUMENT;
+  const kvpop::DecodePlan p = kvpop::plan_decode(s);
+  if (p.workspace_floats) {
+    if (!workspace || !aligned(workspace, 16)) return KVPOP_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < p.workspace_floats * sizeof(float)) return KVPOP_ERR_WORKSPACE_TOO_SMALL;
+  }
+  const kvpop::MlstmWeights mw{w->wk, w->wr, w->wv, w->wi, w->bi, w->wf, w->bf, w->wo, w->bo};
+  return from_hip(kvpop::launch_decode_step_mlstm(
+      s, n_sink, window, pos_q, k_new, v_new, mw, state, k_cache, v_cache, slot_pos, slot_score, q,
+      o, o_dtype == KVPOP_OUT_BF16 ? 1 : 0, lse, (float*)workspace, stream));
+}
+
 kvpop_status kvpop_running_topk(int batch, int n_kv_heads, int seq_len, int n_sink, int window,
                                 int budget, const float* scores, const float* log_decay,
                                 int32_t* keep_until, int32_t* cutoff, hipStream_t stream) {

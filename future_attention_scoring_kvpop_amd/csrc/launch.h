@@ -40,6 +40,15 @@ hipError_t launch_mlstm_step(int B, int Hkv, int D, int n_sink, int window, int 
                              const MlstmWeights& w, float* state, float* slot_score,
                              hipStream_t st);
 
+// mLSTM scorer step, cache step with no scorer, then decode attention (one
+// launch when the decode plan needs no slot split)
+struct AttnShape;
+hipError_t launch_decode_step_mlstm(const AttnShape& s, int n_sink, int window, int pos_q,
+                                    const void* k_new, const void* v_new, const MlstmWeights& w,
+                                    float* state, void* kc, void* vc, int32_t* slot_pos,
+                                    float* slot_score, const void* q, void* o, int o_bf16,
+                                    float* lse, float* workspace, hipStream_t st);
+
 // ---- running top-k mask ----
 int running_topk_max_len();  // longest row the kernel takes
 hipError_t launch_running_topk(int B, int Hkv, int S, int n_sink, int window, int budget,

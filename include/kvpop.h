@@ -292,6 +292,26 @@ kvpop_status kvpop_mlstm_step(int batch, int n_kv_heads, int head_dim, int n_sin
                               hipStream_t stream);
 
 /*
+ * kvpop_decode_step_mlstm -- one decode step with the delayed mLSTM scorer:
+ * kvpop_mlstm_step (the new token enters the scorer state, the exiting
+ * token u = pos_q - w is scored into its ring slot), then kvpop_cache_step
+ * with no scorer of its own (u is kept or dropped on that score, the new
+ * token enters), then kvpop_decode_attend over the updated cache.  App. E.3,
+ * E.4 and Sec. 3 (the scorer reads out the token leaving the window, which
+ * is judged at once), App. C.1 (attention over the retained entries).
+ * Same effect, bit for bit, as the three calls with the same arguments
+ * (dims->seq_len is the budget); when B * Hkv rows fill the device they run
+ * in one launch.  Arguments and errors as for those calls; workspace:
+ * kvpop_workspace_bytes(KVPOP_OP_DECODE, dims, 0) bytes.
+ */
+kvpop_status kvpop_decode_step_mlstm(const kvpop_dims* dims, int n_sink, int window, int pos_q,
+                                     const void* k_new, const void* v_new,
+                                     const kvpop_mlstm_weights* w, float* state, void* k_cache,
+                                     void* v_cache, int32_t* slot_pos, float* slot_score,
+                                     const void* q, void* o, kvpop_out_dtype o_dtype, float* lse,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * kvpop_decode_step -- one bounded-cache decode step, then decode attention
  * over the updated cache.  Sec. 3, App. C.1 and App. E.4: the token leaving
  * the window is kept or dropped, the new token enters its ring slot, the

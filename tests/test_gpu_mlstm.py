@@ -145,3 +145,40 @@ def test_decode_with_mlstm_scores_bit_exact_cache(kv, fused):
     sel = np.zeros((B, H, n), bool)
     sel[:, :, s:n - w] = True
     assert_close(got[sel], ref[sel], SC_ATOL, SC_RTOL, "mlstm scores in decode")
+
+
+@pytest.mark.parametrize("B,H,G,D,budget,pos", [(64, 8, 4, 128, 300, 5000), (2, 2, 4, 128, 300, 5000),
+                                                (3, 4, 2, 64, 100, 777)])
+def test_fused_decode_step_mlstm_matches_the_calls(kv, B, H, G, D, budget, pos):
+    """kvpop_decode_step_mlstm = kvpop_mlstm_step + kvpop_decode_step (no
+    scorer), bit for bit: state, slot positions and scores, caches, o, lse.
+    The first shape takes the one-launch path, the others the split plan."""
+    s, w = 4, 64
+    g = torch.Generator(device="cuda").manual_seed(B + budget)
+    kc = torch.randn((B, H, budget, D), generator=g, device="cuda").to(torch.bfloat16)
+    vc = torch.randn((B, H, budget, D), generator=g, device="cuda").to(torch.bfloat16)
+    sp = torch.arange(budget, dtype=torch.int32, device="cuda").repeat(B, H, 1)
+    sp[..., s:budget - w] = torch.randint(s, pos - w, (B, H, budget - w - s), generator=g,
+                                          device="cuda", dtype=torch.int32)
+    ring = [0] * w
+    for p_ in range(pos - w, pos):  # token p sits in ring slot (budget - w) + p mod w
+        ring[p_ % w] = p_
+    sp[..., budget - w:] = torch.tensor(ring, dtype=torch.int32, device="cuda")
+    ss = torch.randn((B, H, budget), generator=g, device="cuda")
+    kn = torch.randn((B, H, D), generator=g, device="cuda").to(torch.bfloat16)
+    vn = torch.randn((B, H, D), generator=g, device="cuda").to(torch.bfloat16)
+    q = torch.randn((B, H * G, D), generator=g, device="cuda").to(torch.bfloat16)
+    prd = {a: t.cuda() for a, t in _params(H, D, seed=B).items()}
+    state = kv.mlstm_state(B, H)
+    for t in range(5):  # a non-empty state
+        kv.mlstm_step(kn, vn, prd, state, t, s, w)
+    copies = [x.clone() for x in (kc, vc, sp, ss, state)]
+    kv.mlstm_step(kn, vn, prd, state, pos, s, w, kc, vc, ss)
+    o1, l1 = kv.decode_step(q, kc, vc, sp, ss, kn, vn, pos, s, w, 0)
+    kc2, vc2, sp2, ss2, st2 = copies
+    o2, l2 = kv.decode_step_mlstm(q, kc2, vc2, sp2, ss2, kn, vn, prd, st2, pos, s, w)
+    torch.cuda.synchronize()
+    for a, b_, name in ((kc, kc2, "k cache"), (vc, vc2, "v cache"), (sp, sp2, "slot_pos"),
+                        (o1, o2, "o"), (l1, l2, "lse"), (state, st2, "state")):
+        assert torch.equal(a, b_), name
+    assert torch.equal(torch.nan_to_num(ss, nan=7.0), torch.nan_to_num(ss2, nan=7.0))
