@@ -100,8 +100,9 @@ kvpop_status kvpop_mlstm_step(int batch, int n_kv_heads, int head_dim, int n_sin
   if (!w || !k_new || !v_new || !state) return KVPOP_ERR_INVALID_ARGUMENT;
   if (w->feat != kvpop::kMlstmFeat || w->vdim != kvpop::kMlstmVdim) return KVPOP_ERR_UNSUPPORTED;
   const float* ws[9] = {w->wk, w->wr, w->wv, w->wi, w->bi, w->wf, w->bf, w->wo, w->bo};
-  for (const float* p : ws)
-    if (!p || !aligned(p, 4)) return KVPOP_ERR_INVALID_ARGUMENT;
+  for (int i = 0; i < 9; ++i)  // weight rows are read 16 bytes at a time
+    if (!ws[i] || !aligned(ws[i], (i == 4 || i == 6 || i == 7 || i == 8) ? 4 : 16))
+      return KVPOP_ERR_INVALID_ARGUMENT;
   if (slot_score && (!k_cache || !v_cache || !aligned(slot_score, 4) || !aligned(k_cache, 2) ||
                      !aligned(v_cache, 2)))
     return KVPOP_ERR_INVALID_ARGUMENT;
@@ -133,8 +134,9 @@ kvpop_status kvpop_decode_step_mlstm(const kvpop_dims* dims, int n_sink, int win
   if (o_dtype != KVPOP_OUT_F32 && o_dtype != KVPOP_OUT_BF16) return KVPOP_ERR_INVALID_ARGUMENT;
   if (w->feat != kvpop::kMlstmFeat || w->vdim != kvpop::kMlstmVdim) return KVPOP_ERR_UNSUPPORTED;
   const float* ws[9] = {w->wk, w->wr, w->wv, w->wi, w->bi, w->wf, w->bf, w->wo, w->bo};
-  for (const float* p : ws)
-    if (!p || !aligned(p, 4)) return KVPOP_ERR_INVALID_ARGUMENT;
+  for (int i = 0; i < 9; ++i)  // weight rows are read 16 bytes at a time
+    if (!ws[i] || !aligned(ws[i], (i == 4 || i == 6 || i == 7 || i == 8) ? 4 : 16))
+      return KVPOP_ERR_INVALID_ARGUMENT;
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
       !aligned(v_cache, 16) || !aligned(slot_pos, 4) || !aligned(slot_score, 4) ||
       !aligned(state, 16) || !aligned(q, 16) || !aligned(o, 4) || (lse && !aligned(lse, 4)))

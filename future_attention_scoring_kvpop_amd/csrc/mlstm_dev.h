@@ -15,13 +15,16 @@
 //   r = hedgehog(Wr x_u);  h = C' r / max(|n'.r|, e^(-m'));  score_u = wo.silu(h) + bo
 //
 // gfx950 mapping: one 256-thread workgroup per (b, KV head) row.  The
-// projections are dot products of length 2D: one wave per output, lanes
-// striding the input so every weight row is read coalesced (the weights of
-// a layer stay L2-resident across the batch).  Gates, the stabiliser and
-// the Hedgehog softmaxes run on one wave; then each thread owns 16
-// consecutive entries of one row of C (64 x 64, 16 KB per row, read and
-// written once per step), updates them in registers and forms its part of
-// C' r, reduced over the 4 threads of the row with two lane swaps.
+// projections are dot products of length 2D: thread o computes output o
+// whole, reading its weight row 16 bytes at a time (the weights of a layer
+// stay L2-resident across the batch) and the input from LDS as broadcast
+// reads, so no projection needs a cross-lane reduction.  The Hedgehog
+// softmaxes take their max and sums from LDS the same way (wave 0 for the
+// entering token and the gates, wave 1 for the read-out token).  Each
+// thread then owns 16 consecutive entries of one row of C (64 x 64, 16 KB
+// per row, read and written once per step), updates them in registers and
+// forms its part of C' r, reduced over the 4 threads of the row with two
+// lane swaps.
 #pragma once
 
 #include "common.h"
@@ -41,23 +44,26 @@ __device__ __forceinline__ float wave_sum64(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
   return v;
 }
-__device__ __forceinline__ float wave_max64(float v) {
+// Hedgehog features of the kP values z[0..kP) in LDS, without lane
+// shuffles: lane j receives feature j (softmax(z) for j < kP, softmax(-z)
+// after); every lane reads all of z (broadcast reads) for the max and min,
+// lane j writes its exponential to tmp, and every lane sums its half back.
+__device__ __forceinline__ float hedgehog_lds(const float* z, float* tmp, int lane) {
+  float mx = -INFINITY, mn = INFINITY;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-
-// Hedgehog features of the kP values z (lane j < kP holds z[j]); lane j of
-// the wave receives feature j (softmax(z) for j < kP, softmax(-z) after).
-__device__ __forceinline__ float hedgehog_lane(float z, int lane) {
-  const bool own = lane < kP;
-  const float mx = wave_max64(own ? z : -INFINITY);
-  const float mn = -wave_max64(own ? -z : -INFINITY);
-  const float ep = own ? expf(z - mx) : 0.f;
-  const float en = own ? expf(mn - z) : 0.f;
-  const float sp = wave_sum64(ep), sn = wave_sum64(en);
-  const float zj = __shfl(z, lane & (kP - 1));
-  return lane < kP ? expf(zj - mx) / sp : expf(mn - zj) / sn;
+  for (int j = 0; j < kP; ++j) {
+    mx = fmaxf(mx, z[j]);
+    mn = fminf(mn, z[j]);
+  }
+  const int j = lane & (kP - 1);
+  const float ex = lane < kP ? expf(z[j] - mx) : expf(mn - z[j]);
+  tmp[lane] = ex;
+  __builtin_amdgcn_wave_barrier();
+  const float* half = tmp + (lane < kP ? 0 : kP);
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < kP; ++i) sum += half[i];
+  return ex / sum;
 }
 
 __device__ __forceinline__ float log_sigmoid(float a) {
@@ -80,6 +86,7 @@ __device__ __forceinline__ void mlstm_row(
   __shared__ float phi[kF], rr[kF], val[kE];
   __shared__ float gate[4];          // fs, is, m', e^(-m')
   __shared__ float hpart[kE];
+  __shared__ __attribute__((aligned(16))) float hh_tmp[2][kF];
 
   const int h = row % Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -101,9 +108,13 @@ __device__ __forceinline__ void mlstm_row(
   }
   __syncthreads();
 
-  // projections: output o is wave (o % 4)'s; lanes stride the input
+  // projections: thread o computes output o over the whole input, reading
+  // its weight row 16 bytes at a time and the input from LDS (all lanes of
+  // a wave read the same 16 bytes: a broadcast), so no output needs a
+  // cross-lane reduction
   const int n_out = NOUT + (readout ? kP : 0);
-  for (int o = wave; o < n_out; o += 4) {
+  if (tid < n_out) {
+    const int o = tid;
     const float* w;
     const float* x = xs;
     if (o < kP) w = wt.wk + ((size_t)h * kP + o) * X;
@@ -114,20 +125,27 @@ __device__ __forceinline__ void mlstm_row(
       w = wt.wr + ((size_t)h * kP + (o - NOUT)) * X;
       x = xu;
     }
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < XPL; ++i) s = fmaf(w[lane + 64 * i], x[lane + 64 * i], s);
-    s = wave_sum64(s);
-    if (lane == 0) proj[o] = s;
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll 8
+    for (int i = 0; i < X; i += 4) {
+      const float4 wv = *reinterpret_cast<const float4*>(w + i);
+      const float4 xv = *reinterpret_cast<const float4*>(x + i);
+      s0 = fmaf(wv.x, xv.x, s0);
+      s1 = fmaf(wv.y, xv.y, s1);
+      s2 = fmaf(wv.z, xv.z, s2);
+      s3 = fmaf(wv.w, xv.w, s3);
+    }
+    proj[o] = (s0 + s1) + (s2 + s3);
   }
   __syncthreads();
 
   float* st = state + (size_t)row * kMlstmStateFloats;
+
+  // Hedgehog features: wave 0 those of the entering token (and the gates),
+  // wave 1 those of the read-out token
   if (wave == 0) {
-    const float pk = hedgehog_lane(lane < kP ? proj[lane] : 0.f, lane);
-    phi[lane] = pk;
+    phi[lane] = hedgehog_lds(proj, hh_tmp[0], lane);
     val[lane] = proj[kP + lane];
-    if (readout) rr[lane] = hedgehog_lane(lane < kP ? proj[NOUT + lane] : 0.f, lane);
     if (lane == 0) {
       const float ig = proj[kP + kE] + wt.bi[h];
       const float lf = log_sigmoid(proj[kP + kE + 1] + wt.bf[h]);
@@ -138,6 +156,8 @@ __device__ __forceinline__ void mlstm_row(
       gate[2] = mn;
       gate[3] = expf(-mn);
     }
+  } else if (wave == 1 && readout) {
+    rr[lane] = hedgehog_lds(proj + NOUT, hh_tmp[1], lane);
   }
   __syncthreads();
 

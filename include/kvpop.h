@@ -270,7 +270,8 @@ kvpop_status kvpop_cache_step(int batch, int n_kv_heads, int head_dim, int n_sin
  * Called before kvpop_cache_step of the same position with no scorer, it
  * gives the exit decision of u the score from the state through pos_q.
  *   w: feat = 32 (P), vdim = 64 (E); Wk, Wr fp32 [Hkv][P][2D], Wv
- *      [Hkv][E][2D], wi, wf [Hkv][2D], bi, bf, bo [Hkv], wo [Hkv][E].
+ *      [Hkv][E][2D], wi, wf [Hkv][2D] (these five 16-byte aligned), bi,
+ *      bf, bo [Hkv], wo [Hkv][E].
  *   state: fp32 [B][Hkv][KVPOP_MLSTM_STATE_FLOATS], 16-byte aligned: C
  *      row-major [E][2P], then n [2P], then m, then 3 unused floats.  An
  *      empty state is C = 0, n = 0, m = -inf; it is updated in place.
