@@ -194,21 +194,35 @@ __global__ __launch_bounds__(kThreads, KVPOP_FWD_MIN_BLOCKS) void fwd_lse_kernel
     }
     if constexpr (SPARSE) {
       // key row of register r: t0 + 32 sub + 8 (r/4) + 4 half + r%4; its
-      // keep_until values are four runs of four consecutive ints
+      // keep_until values are four runs of four consecutive ints.  Below
+      // the diagonal (and inside the piece) only keep_until can mask.
       const int* ut = ust(J) + wave * 64;
+      if (t0 + kKT - 1 > p0 || t0 + kKT > k_end) {  // diagonal, past S or past the piece
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
+        for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int4 u = *reinterpret_cast<const int4*>(ut + sub * 32 + 8 * r4 + 4 * half);
-          const int uu[4] = {u.x, u.y, u.z, u.w};
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int4 u = *reinterpret_cast<const int4*>(ut + sub * 32 + 8 * r4 + 4 * half);
+            const int uu[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * r4 + e;
-            const int t = t0 + sub * 32 + 8 * r4 + 4 * half + e;
-            acc[sub][r] = (t > dpos || t >= k_end || dpos >= uu[e]) ? -INFINITY : acc[sub][r];
+            for (int e = 0; e < 4; ++e) {
+              const int t = t0 + sub * 32 + 8 * r4 + 4 * half + e;
+              acc[sub][4 * r4 + e] =
+                  (t > dpos || t >= k_end || dpos >= uu[e]) ? -INFINITY : acc[sub][4 * r4 + e];
+            }
           }
-        }
+      } else {
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int4 u = *reinterpret_cast<const int4*>(ut + sub * 32 + 8 * r4 + 4 * half);
+            acc[sub][4 * r4 + 0] = dpos >= u.x ? -INFINITY : acc[sub][4 * r4 + 0];
+            acc[sub][4 * r4 + 1] = dpos >= u.y ? -INFINITY : acc[sub][4 * r4 + 1];
+            acc[sub][4 * r4 + 2] = dpos >= u.z ? -INFINITY : acc[sub][4 * r4 + 2];
+            acc[sub][4 * r4 + 3] = dpos >= u.w ? -INFINITY : acc[sub][4 * r4 + 3];
+          }
+      }
     } else if (t0 + kKT - 1 > p0 || t0 + kKT > k_end) {  // diagonal, past S or past the piece
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
