@@ -735,7 +735,7 @@ def main():
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the KVpop hot path is sharded by (batch, KV head) with no "
-              "communication, and this build runs on a single MI355X; use --gpus 1.", flush=True)
+              "communication, and the library runs on one MI355X; use --gpus 1.", flush=True)
         sys.exit(2)
 
     if a.calibrate_copy:

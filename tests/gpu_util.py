@@ -1,6 +1,6 @@
 """Shared helpers of the GPU parity tests (no test functions here).
 
-Tolerances (BASELINE target of the build, fp32 accumulation of bf16 inputs):
+Tolerances (the parity bar for fp32 accumulation of bf16 inputs):
   LSE      |gpu - oracle| <= 1e-3
   mass     |gpu - oracle| <= 1e-5 + 2e-3 |oracle|
   decode o |gpu - oracle| <= 1e-5 + 2e-3 |oracle| (fp32 output);
