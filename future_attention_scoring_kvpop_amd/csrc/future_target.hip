@@ -93,6 +93,12 @@ namespace {
 #ifndef KVPOP_TGT_SMALL_KEYS
 #define KVPOP_TGT_SMALL_KEYS 0
 #endif
+// wave priority raised around a tile's MFMA burst (1; ~2% faster than 0:
+// the arbiter then feeds the matrix core first while other waves of the
+// SIMD run their exp2 work) or around the exp2 work instead (2; the same)
+#ifndef KVPOP_TGT_SETPRIO
+#define KVPOP_TGT_SETPRIO 1
+#endif
 
 constexpr int kQT = 32;                    // queries per LDS tile
 constexpr int kStages = KVPOP_TGT_STAGES;  // query tiles in the LDS ring
@@ -326,6 +332,8 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KVPO
         // fragment reads in groups of FG, each group issued before one wait
         // (the next group's reads overlap this group's MFMAs)
         constexpr int FG = KVPOP_TGT_FRAG_GROUP;
+        if constexpr (KVPOP_TGT_SETPRIO == 1) __builtin_amdgcn_s_setprio(1);
+        if constexpr (KVPOP_TGT_SETPRIO == 2) __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int s0 = 0; s0 < NS; s0 += FG) {
           u32x4 bu[FG];
@@ -344,6 +352,8 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KVPO
             acc = mfma32(ka[s0 + s], bq, acc);
           }
         }
+        if constexpr (KVPOP_TGT_SETPRIO == 1) __builtin_amdgcn_s_setprio(0);
+        if constexpr (KVPOP_TGT_SETPRIO == 2) __builtin_amdgcn_s_setprio(1);
         // queries past the sequence end get L = +inf, so their terms vanish
         const float L2 = d0 + col < S ? lraw * kLog2e : __builtin_inff();
         const bool full = d0 >= ts + 31 + window &&
