@@ -25,6 +25,7 @@ AGG = {"sum": 0, "mean": 1, "max": 2}
 OP_FUTURE_TARGET = 0
 OP_DECODE = 1
 OP_FWD_LSE = 2
+OP_FWD_LSE_SPARSE = 3
 
 EXPORTS = ("kvpop_abi_version", "kvpop_status_string", "kvpop_workspace_bytes", "kvpop_fwd_lse",
            "kvpop_future_attn_target", "kvpop_evict_select", "kvpop_decode_attend",
@@ -74,7 +75,7 @@ def lib():
                                      P, P, P]),
             "kvpop_decode_step_mlstm": (I, [DP, I, I, I, P, P, ctypes.POINTER(MlstmWeights), P, P, P,
                                             P, P, P, P, I, P, P, Z, P]),
-            "kvpop_fwd_lse_sparse": (I, [DP, P, P, P, P, P, Z, P]),
+            "kvpop_fwd_lse_sparse": (I, [DP, P, P, P, I, P, P, Z, P]),
             "kvpop_future_attn_target": (I, [DP, P, P, P, I, I, I, I, P, P, P, Z, P]),
             "kvpop_evict_select": (I, [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P]),
             "kvpop_decode_attend": (I, [DP, P, P, P, P, P, I, P, P, Z, P]),
@@ -248,10 +249,12 @@ def decode_step_mlstm(q, k_cache, v_cache, slot_pos, slot_score, k_new, v_new, p
     return o, lse
 
 
-def fwd_lse_sparse(q, k, keep_until, scale=0.0, out=None, workspace=None):
+def fwd_lse_sparse(q, k, keep_until, budget=0, scale=0.0, out=None, workspace=None):
     """Sparse causal log-normalizers LSE [B,Hq,S] fp32 over the running
     top-k mask (App. D.3, C.1): key t counts for row d while
-    t <= d < keep_until[t]."""
+    t <= d < keep_until[t].  ``budget`` is the budget keep_until was made
+    with: each block of queries then attends over its listed keys only
+    (0: every causal key is read and tested)."""
     _need(q, torch.bfloat16, "q", 4)
     _need(k, torch.bfloat16, "k", 4)
     _need(keep_until, torch.int32, "keep_until", 3)
@@ -262,12 +265,12 @@ def fwd_lse_sparse(q, k, keep_until, scale=0.0, out=None, workspace=None):
     lse = out if out is not None else torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
     _need(lse, torch.float32, "lse")
     d = dims(B, Hq, Hkv, S, D, scale)
-    nbytes = workspace_bytes(OP_FWD_LSE, d)
+    nbytes = workspace_bytes(OP_FWD_LSE_SPARSE, d, budget)
     ws = workspace if workspace is not None else (
         torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None)
-    st = lib().kvpop_fwd_lse_sparse(ctypes.byref(d), _p(q), _p(k), _p(keep_until), _p(lse),
-                                    _p(ws), 0 if ws is None else ws.numel() * ws.element_size(),
-                                    _stream())
+    st = lib().kvpop_fwd_lse_sparse(ctypes.byref(d), _p(q), _p(k), _p(keep_until), int(budget),
+                                    _p(lse), _p(ws),
+                                    0 if ws is None else ws.numel() * ws.element_size(), _stream())
     _check("kvpop_fwd_lse_sparse", st)
     return lse
 

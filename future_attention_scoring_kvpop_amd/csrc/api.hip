@@ -70,6 +70,11 @@ size_t kvpop_workspace_bytes(int op, const kvpop_dims* dims, int window) {
   }
   if (op == KVPOP_OP_DECODE) return kvpop::plan_decode(s).workspace_floats * sizeof(float);
   if (op == KVPOP_OP_FWD_LSE) return kvpop::plan_fwd(s).partial_floats * sizeof(float);
+  if (op == KVPOP_OP_FWD_LSE_SPARSE) {  // the third argument is the budget
+    if (window < 0) return 0;
+    if (window == 0) return kvpop::plan_fwd(s).partial_floats * sizeof(float);
+    return kvpop::plan_fwd_sparse(s, window).workspace_bytes;
+  }
   return 0;
 }
 
@@ -85,7 +90,7 @@ kvpop_status kvpop_fwd_lse(const kvpop_dims* dims, const void* q, const void* k,
     if (!workspace || !aligned(workspace, 16)) return KVPOP_ERR_INVALID_ARGUMENT;
     if (workspace_bytes < p.partial_floats * sizeof(float)) return KVPOP_ERR_WORKSPACE_TOO_SMALL;
   }
-  return from_hip(kvpop::launch_fwd_lse(s, q, k, nullptr, lse, (float*)workspace, stream));
+  return from_hip(kvpop::launch_fwd_lse(s, q, k, nullptr, 0, lse, workspace, stream));
 }
 
 kvpop_status kvpop_mlstm_step(int batch, int n_kv_heads, int head_dim, int n_sink, int window,
@@ -171,21 +176,22 @@ kvpop_status kvpop_running_topk(int batch, int n_kv_heads, int seq_len, int n_si
 }
 
 kvpop_status kvpop_fwd_lse_sparse(const kvpop_dims* dims, const void* q, const void* k,
-                                  const int32_t* keep_until, float* lse, void* workspace,
-                                  size_t workspace_bytes, hipStream_t stream) {
+                                  const int32_t* keep_until, int budget, float* lse,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
   AttnShape s;
   kvpop_status st = check_dims(dims, &s);
   if (st != KVPOP_OK) return st;
-  if (!q || !k || !keep_until || !lse) return KVPOP_ERR_INVALID_ARGUMENT;
+  if (!q || !k || !keep_until || !lse || budget < 0) return KVPOP_ERR_INVALID_ARGUMENT;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(keep_until, 4) || !aligned(lse, 4))
     return KVPOP_ERR_INVALID_ARGUMENT;
-  const kvpop::FwdPlan p = kvpop::plan_fwd(s);
-  if (p.partial_floats) {
-    if (!workspace || !aligned(workspace, 16)) return KVPOP_ERR_INVALID_ARGUMENT;
-    if (workspace_bytes < p.partial_floats * sizeof(float)) return KVPOP_ERR_WORKSPACE_TOO_SMALL;
+  const size_t need = budget > 0 ? kvpop::plan_fwd_sparse(s, budget).workspace_bytes
+                                 : kvpop::plan_fwd(s).partial_floats * sizeof(float);
+  if (need) {
+    if (!workspace || !aligned(workspace, budget > 0 ? 256 : 16)) return KVPOP_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < need) return KVPOP_ERR_WORKSPACE_TOO_SMALL;
   }
-  return from_hip(kvpop::launch_fwd_lse(s, q, k, (const int*)keep_until, lse, (float*)workspace,
-                                        stream));
+  return from_hip(
+      kvpop::launch_fwd_lse(s, q, k, (const int*)keep_until, budget, lse, workspace, stream));
 }
 
 kvpop_status kvpop_future_attn_target(const kvpop_dims* dims, const void* q, const void* k,

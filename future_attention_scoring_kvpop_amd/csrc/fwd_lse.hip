@@ -25,10 +25,23 @@
 //   * Work items are issued longest first and renumbered so that each XCD
 //     works through whole KV heads (their K stays in that XCD's L2).
 //   * Sparse normalizer (App. D.3 with the running top-k mask of App. C.1):
-//     key t takes part in row d only while t <= d < keep_until[t].  Each
-//     wave DMAs its own copy of the tile's 64 keep_until values into the
-//     stage beside the K rows and every tile is masked with one compare per
-//     score; the MFMA work is the same as the dense pass.
+//     key t takes part in row d only while t <= d < keep_until[t].
+//     - Listed mode (a budget is given): keylist_kernel writes, per row
+//       block [p0, p1), the keys still retained at p0: first those retained
+//       through p1 - 1 (no test), then those leaving inside the block and
+//       the block's own keys, padded to whole tiles with the position S.
+//       With the running top-k mask at most budget + P keys qualify
+//       (budget - 1 retained before p0, P new), so a block walks about
+//       budget + P keys instead of its whole causal row.  K rows are
+//       gathered through the list by the same DMA, one tile ahead; each
+//       wave keeps its own copy of the tile's list and of the gathered
+//       keep_until values, and only tiles past the unconditional keys test
+//       each score (t <= d and d < keep_until[t]).  A block whose list
+//       would not fit (keep_until not made with that budget) walks its
+//       whole causal row through the same code with the list t = 0, 1, ...
+//     - Masked mode (no budget): every causal tile is read as in the dense
+//       pass and each score is tested against keep_until.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -62,12 +75,95 @@ __device__ __forceinline__ void wait_inflight(int n) {
   else wait_vmcnt<12>();
 }
 
-template <int D, bool SPARSE>
+enum { kDense = 0, kMasked = 1, kListed = 2 };
+
+// Key lists of the listed sparse mode: one workgroup per (b, KV head, row
+// block).  lists[blk][0, cap) receives the keys t < p0 with keep_until[t]
+// >= p1 (in position order), then those with p0 < keep_until[t] < p1 and
+// the block's own keys [p0, p1), then the padding S up to a whole tile;
+// hdr[blk] = (tiles, first tile holding a conditional key), or (-1, 0)
+// when the list does not fit in cap entries (or its conditional part in
+// kPartMax).
+constexpr int kPartMax = 256;
+__global__ __launch_bounds__(256) void keylist_kernel(const int* __restrict__ keep_until,
+                                                      int* __restrict__ lists,
+                                                      int2* __restrict__ hdr, int S, int n_pb,
+                                                      int P, int cap) {
+  __shared__ int part[kPartMax];
+  __shared__ int wcnt[2][4];
+  const int blk = blockIdx.x;
+  const int bh = blk / n_pb, pb = blk - bh * n_pb;
+  const int p0 = pb * P, p1 = min(S, p0 + P);
+  const int* u = keep_until + (size_t)bh * S;
+  int* list = lists + (size_t)blk * cap;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const uint64_t below = (1ull << lane) - 1;
+  int n_full = 0, n_part = 0;  // same value in every thread
+  constexpr int kU = 4;        // loads in flight per thread
+  for (int base = 0; base < p0; base += 256 * kU) {
+    int ut[kU];
+#pragma unroll
+    for (int x = 0; x < kU; ++x) {
+      const int t = base + x * 256 + tid;
+      ut[x] = t < p0 ? u[t] : 0;
+    }
+#pragma unroll
+    for (int x = 0; x < kU; ++x) {
+      const int t = base + x * 256 + tid;
+      const bool full = t < p0 && ut[x] >= p1;
+      const bool cond = t < p0 && ut[x] > p0 && ut[x] < p1;
+      const uint64_t bf = __ballot(full), bc = __ballot(cond);
+      if (lane == 0) {
+        wcnt[0][w] = __popcll(bf);
+        wcnt[1][w] = __popcll(bc);
+      }
+      __syncthreads();
+      int of = 0, oc = 0, tf = 0, tc = 0;
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        const int cf = wcnt[0][y], cc = wcnt[1][y];
+        if (y < w) {
+          of += cf;
+          oc += cc;
+        }
+        tf += cf;
+        tc += cc;
+      }
+      if (full) {
+        const int pos = n_full + of + __popcll(bf & below);
+        if (pos < cap) list[pos] = t;
+      }
+      if (cond) {
+        const int pos = n_part + oc + __popcll(bc & below);
+        if (pos < kPartMax) part[pos] = t;
+      }
+      n_full += tf;
+      n_part += tc;
+      __syncthreads();  // wcnt is rewritten next round
+    }
+  }
+  for (int t = p0 + tid; t < p1; t += 256) {
+    const int pos = n_part + (t - p0);
+    if (pos < kPartMax) part[pos] = t;
+  }
+  n_part += p1 - p0;
+  __syncthreads();
+  const int count = n_full + n_part;
+  const bool fits = count <= cap && n_part <= kPartMax;
+  const int n_t = (count + kKT - 1) / kKT;
+  if (fits)
+    for (int x = tid; x < n_t * kKT - n_full; x += 256) list[n_full + x] = x < n_part ? part[x] : S;
+  if (tid == 0) hdr[blk] = fits ? make_int2(n_t, n_full / kKT) : make_int2(-1, 0);
+}
+
+template <int D, int MODE>
 __global__ __launch_bounds__(kThreads, KVPOP_FWD_MIN_BLOCKS) void fwd_lse_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const int* __restrict__ keep_until,
-    float* __restrict__ lse,
+    const int2* __restrict__ hdr, const int* __restrict__ lists, int cap, float* __restrict__ lse,
     float2* __restrict__ part, int B, int Hq, int Hkv, int S, float c, float scale, int n_pb,
     int kmax, int n_pieces, int n_items, int snake_cus) {
+  constexpr bool SPARSE = MODE != kDense;
+  static_assert(MODE != kListed || kStages == 2, "the listed mode pairs list slots with stages");
   constexpr int NS = D / 16;           // MFMA k-slices
   constexpr int CPR = D / 8;           // 16-byte chunks per row
   constexpr int ROWB = D * 2;          // bytes per K row
@@ -89,7 +185,15 @@ __global__ __launch_bounds__(kThreads, KVPOP_FWD_MIN_BLOCKS) void fwd_lse_kernel
     constexpr int j = decltype(J)::value;
     return j == 0 ? us0 : j == 1 ? us1 : j == 2 ? us2 : us3;
   };
-  constexpr int DPS = LPW + (SPARSE ? 1 : 0);  // DMA instructions per wave per stage
+  // listed mode: each wave's own copy of a tile's 64 list entries, in the
+  // slot of the stage that tile is loaded into
+  constexpr int LS = MODE == kListed ? kKT * (kThreads / 64) : 1;
+  __shared__ __attribute__((aligned(256))) int lt0[LS], lt1[LS];
+  auto lst = [&](auto J) -> int* {
+    constexpr int j = decltype(J)::value;
+    return j == 0 ? lt0 : lt1;
+  };
+  constexpr int DPS = LPW + (SPARSE ? 1 : 0) + (MODE == kListed ? 1 : 0);  // DMAs per wave per stage
 
   const int G = Hq / Hkv;
   const int P = 128 / G;
@@ -122,7 +226,22 @@ __global__ __launch_bounds__(kThreads, KVPOP_FWD_MIN_BLOCKS) void fwd_lse_kernel
   if (k_begin >= n_keys) return;  // this row block needs fewer pieces
   const int k_end = min(n_keys, k_begin + kmax);
   const int kt0 = k_begin / kKT;
-  const int n_kt = (k_end - k_begin + kKT - 1) / kKT;
+  int n_kt = (k_end - k_begin + kKT - 1) / kKT;
+  // listed mode: tiles of the block's list, first tile with a test, and
+  // whether the list is the identity (a block whose list did not fit)
+  int ft = 0;
+  bool ident = true;
+  const int* blist = nullptr;
+  if constexpr (MODE == kListed) {
+    const int blk = bh * n_pb + pb;
+    const int2 hh = hdr[blk];
+    if (hh.x >= 0) {
+      n_kt = hh.x;
+      ft = hh.y;
+      ident = false;
+      blist = lists + (size_t)blk * cap;
+    }
+  }
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -149,6 +268,31 @@ __global__ __launch_bounds__(kThreads, KVPOP_FWD_MIN_BLOCKS) void fwd_lse_kernel
     if constexpr (SPARSE)
       dma4(kuntil + min(kt * kKT + lane, S - 1), ust(J) + wave * 64);
   };
+  // listed mode: K rows and keep_until values of the tile whose list is in
+  // slot J, gathered into stage J
+  auto issue_listed = [&](auto J) {
+    uint8_t* dst = kst(J);
+    const int* lw = lst(J) + wave * 64;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      const int I = wave * LPW + j;
+      const int row = I * ROWS_PER_LOAD + lane / CPR;
+      const int pc = lane % CPR;
+      const int lc = pc ^ (row & (CPR - 1));
+      const int t = min(lw[row], S - 1);
+      dma16(kbase + (size_t)t * D + lc * 8, dst + I * 1024);
+    }
+    dma4(kuntil + min(lw[lane], S - 1), ust(J) + wave * 64);
+  };
+  // listed mode: list entries of tile i into slot J
+  auto fill_list = [&](auto J, int i) {
+    if (ident) {
+      lst(J)[wave * 64 + lane] = i * kKT + lane;
+    } else {
+      wait_lgkmcnt0();  // this wave's reads of the slot are done before the DMA refills it
+      dma4(blist + i * kKT + lane, lst(J) + wave * 64);
+    }
+  };
 
   bf16x8 bq[NS];
   {
@@ -161,9 +305,17 @@ __global__ __launch_bounds__(kThreads, KVPOP_FWD_MIN_BLOCKS) void fwd_lse_kernel
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
-  if (0 < n_kt) issue(I0{}, kt0);
-  if (1 < n_kt && kStages > 2) issue(I1{}, kt0 + 1);
-  if (2 < n_kt && kStages > 3) issue(I2{}, kt0 + 2);
+  if constexpr (MODE == kListed) {
+    fill_list(I0{}, 0);
+    if (1 < n_kt) fill_list(I1{}, 1);
+    wait_vmcnt<0>();
+    wait_lgkmcnt0();
+    issue_listed(I0{});
+  } else {
+    if (0 < n_kt) issue(I0{}, kt0);
+    if (1 < n_kt && kStages > 2) issue(I1{}, kt0 + 1);
+    if (2 < n_kt && kStages > 3) issue(I2{}, kt0 + 2);
+  }
 
   float m = -INFINITY, l = 0.f;
   const int sw = col & (CPR - 1);
@@ -179,7 +331,10 @@ __global__ __launch_bounds__(kThreads, KVPOP_FWD_MIN_BLOCKS) void fwd_lse_kernel
     wait_inflight(DPS * min(kStages - 2, n_kt - 1 - i));
     wait_lgkmcnt0();
     bare_barrier();  // tile i is in LDS for every wave; tile i-1's stage is free
-    if (i + kStages - 1 < n_kt) issue(std::integral_constant<int, jn>{}, kt0 + i + kStages - 1);
+    if (i + kStages - 1 < n_kt) {
+      if constexpr (MODE == kListed) issue_listed(std::integral_constant<int, jn>{});
+      else issue(std::integral_constant<int, jn>{}, kt0 + i + kStages - 1);
+    }
     const int t0 = (kt0 + i) * kKT;
     const uint8_t* tile = kst(J);
     f32x16 acc[2];
@@ -192,7 +347,27 @@ __global__ __launch_bounds__(kThreads, KVPOP_FWD_MIN_BLOCKS) void fwd_lse_kernel
       for (int s = 0; s < NS; ++s)
         acc[sub] = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(sbase + foff[s])), bq[s], acc[sub]);
     }
-    if constexpr (SPARSE) {
+    if constexpr (MODE == kListed) {
+      // key of register r: entry 32 sub + 8 (r/4) + 4 half + r%4 of the
+      // tile's list; tiles before ft hold only keys retained for the block
+      if (ident || i >= ft) {
+        const int* tl = lst(J) + wave * 64;
+        const int* ut = ust(J) + wave * 64;
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int4 tv = *reinterpret_cast<const int4*>(tl + sub * 32 + 8 * r4 + 4 * half);
+            const int4 uv = *reinterpret_cast<const int4*>(ut + sub * 32 + 8 * r4 + 4 * half);
+            acc[sub][4 * r4 + 0] = ((tv.x > dpos) | (dpos >= uv.x)) ? -INFINITY : acc[sub][4 * r4 + 0];
+            acc[sub][4 * r4 + 1] = ((tv.y > dpos) | (dpos >= uv.y)) ? -INFINITY : acc[sub][4 * r4 + 1];
+            acc[sub][4 * r4 + 2] = ((tv.z > dpos) | (dpos >= uv.z)) ? -INFINITY : acc[sub][4 * r4 + 2];
+            acc[sub][4 * r4 + 3] = ((tv.w > dpos) | (dpos >= uv.w)) ? -INFINITY : acc[sub][4 * r4 + 3];
+          }
+      }
+      // slot J is free again: the list of tile i + 2 goes there
+      if (i + 2 < n_kt) fill_list(J, i + 2);
+    } else if constexpr (SPARSE) {
       // key row of register r: t0 + 32 sub + 8 (r/4) + 4 half + r%4; its
       // keep_until values are four runs of four consecutive ints.  Below
       // the diagonal (and inside the piece) only keep_until can mask.
@@ -208,7 +383,7 @@ __global__ __launch_bounds__(kThreads, KVPOP_FWD_MIN_BLOCKS) void fwd_lse_kernel
             for (int e = 0; e < 4; ++e) {
               const int t = t0 + sub * 32 + 8 * r4 + 4 * half + e;
               acc[sub][4 * r4 + e] =
-                  (t > dpos || t >= k_end || dpos >= uu[e]) ? -INFINITY : acc[sub][4 * r4 + e];
+                  ((t > dpos) | (t >= k_end) | (dpos >= uu[e])) ? -INFINITY : acc[sub][4 * r4 + e];
             }
           }
       } else {
@@ -229,7 +404,7 @@ __global__ __launch_bounds__(kThreads, KVPOP_FWD_MIN_BLOCKS) void fwd_lse_kernel
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int t = t0 + sub * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          acc[sub][r] = (t > dpos || t >= k_end) ? -INFINITY : acc[sub][r];
+          acc[sub][r] = ((t > dpos) | (t >= k_end)) ? -INFINITY : acc[sub][r];
         }
     }
     float mx = m;
@@ -313,9 +488,25 @@ FwdPlan plan_fwd(const AttnShape& s) {
   return p;
 }
 
-hipError_t launch_fwd_lse(const AttnShape& s, const void* q, const void* k, const int* keep_until,
-                          float* lse, float* workspace, hipStream_t st) {
+SparsePlan plan_fwd_sparse(const AttnShape& s, int budget) {
+  SparsePlan sp;
   const FwdPlan p = plan_fwd(s);
+  sp.n_blocks = (long)s.B * s.Hkv * p.n_pb;
+  const long keys = std::min<long>(s.S, (long)budget + p.P);
+  sp.cap = (int)((keys + kKT - 1) / kKT * kKT);
+  sp.list_offset = ((size_t)sp.n_blocks * sizeof(int2) + 255) / 256 * 256;
+  sp.workspace_bytes = sp.list_offset + (size_t)sp.n_blocks * sp.cap * sizeof(int);
+  return sp;
+}
+
+hipError_t launch_fwd_lse(const AttnShape& s, const void* q, const void* k, const int* keep_until,
+                          int budget, float* lse, void* workspace, hipStream_t st) {
+  const bool listed = keep_until && budget > 0;
+  FwdPlan p = plan_fwd(s);
+  if (listed) {  // whole rows: a listed block walks about budget + P keys
+    p.kmax = (s.S + kKT - 1) / kKT * kKT;
+    p.n_pieces = 1;
+  }
   const int n_items = s.B * s.Hkv * p.n_pb * p.n_pieces;
   const float c = s.scale * kLog2e;
   // one resident round (four workgroups per CU): deal each XCD's blocks in a snake
@@ -323,17 +514,34 @@ hipError_t launch_fwd_lse(const AttnShape& s, const void* q, const void* k, cons
   const int snake_cus = n_items <= cus * KVPOP_FWD_MIN_BLOCKS && cus % 8 == 0 ? cus / 8 : 0;
   dim3 grid(n_items), block(kThreads);
   float2* part = reinterpret_cast<float2*>(workspace);
+  const int2* hdr = nullptr;
+  const int* lists = nullptr;
+  int cap = 0;
+  if (listed) {
+    const SparsePlan sp = plan_fwd_sparse(s, budget);
+    int2* h = reinterpret_cast<int2*>(workspace);
+    int* l = reinterpret_cast<int*>(reinterpret_cast<char*>(workspace) + sp.list_offset);
+    hipLaunchKernelGGL(keylist_kernel, dim3((unsigned)sp.n_blocks), dim3(256), 0, st, keep_until,
+                       l, h, s.S, p.n_pb, p.P, sp.cap);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hdr = h;
+    lists = l;
+    cap = sp.cap;
+  }
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, block, 0, st, (const bf16_t*)q, (const bf16_t*)k, keep_until,
-                       lse, part, s.B, s.Hq, s.Hkv, s.S, c, s.scale, p.n_pb, p.kmax, p.n_pieces,
-                       n_items, snake_cus);
+                       hdr, lists, cap, lse, part, s.B, s.Hq, s.Hkv, s.S, c, s.scale, p.n_pb,
+                       p.kmax, p.n_pieces, n_items, snake_cus);
   };
   if (s.D == 128) {
-    if (keep_until) go(fwd_lse_kernel<128, true>);
-    else go(fwd_lse_kernel<128, false>);
+    if (listed) go(fwd_lse_kernel<128, kListed>);
+    else if (keep_until) go(fwd_lse_kernel<128, kMasked>);
+    else go(fwd_lse_kernel<128, kDense>);
   } else {
-    if (keep_until) go(fwd_lse_kernel<64, true>);
-    else go(fwd_lse_kernel<64, false>);
+    if (listed) go(fwd_lse_kernel<64, kListed>);
+    else if (keep_until) go(fwd_lse_kernel<64, kMasked>);
+    else go(fwd_lse_kernel<64, kDense>);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_pieces == 1) return e;

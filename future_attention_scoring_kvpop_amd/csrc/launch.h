@@ -23,10 +23,21 @@ struct FwdPlan {
   size_t partial_floats;  // workspace floats (0 without split)
 };
 FwdPlan plan_fwd(const AttnShape& s);
+// Workspace of the listed sparse pass: a header per row block, then one
+// key list of cap entries per row block at list_offset.
+struct SparsePlan {
+  long n_blocks;
+  int cap;
+  size_t list_offset;
+  size_t workspace_bytes;
+};
+SparsePlan plan_fwd_sparse(const AttnShape& s, int budget);
 // keep_until: nullable [B][Hkv][S]; when given, key t counts for row d only
-// while t <= d < keep_until[t] (the sparse normalizer)
+// while t <= d < keep_until[t] (the sparse normalizer).  budget > 0 selects
+// the listed pass (workspace from plan_fwd_sparse), else every causal key
+// is tested (workspace from plan_fwd).
 hipError_t launch_fwd_lse(const AttnShape& s, const void* q, const void* k, const int* keep_until,
-                          float* lse, float* workspace, hipStream_t st);
+                          int budget, float* lse, void* workspace, hipStream_t st);
 
 // ---- delayed stateful mLSTM scorer (one decoding step) ----
 constexpr int kMlstmFeat = 32;   // projected features per Hedgehog half

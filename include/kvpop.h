@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define KVPOP_ABI_VERSION 1
+#define KVPOP_ABI_VERSION 2
 
 typedef enum {
     KVPOP_OK = 0,
@@ -69,6 +69,7 @@ typedef struct {
 #define KVPOP_OP_FUTURE_TARGET 0
 #define KVPOP_OP_DECODE 1
 #define KVPOP_OP_FWD_LSE 2
+#define KVPOP_OP_FWD_LSE_SPARSE 3 /* third argument: the budget */
 
 int kvpop_abi_version(void);
 const char* kvpop_status_string(kvpop_status s);
@@ -124,15 +125,28 @@ kvpop_status kvpop_running_topk(int batch, int n_kv_heads, int seq_len, int n_si
  * App. D.3: the target may reuse the log-normalizer of the fixed-budget
  * sparse attention instead of the dense one; App. C.1 gives its mask:
  *   LSE[b][g][d] = log sum_{t <= d, d < keep_until[b][h][t]} exp(scale * q_d . k_t)
- * with keep_until from kvpop_running_topk (h = g / G).  Same layouts,
- * workspace and errors as kvpop_fwd_lse; keep_until is int32 [B][Hkv][S],
- * 4-byte aligned.  A row whose retained set is empty gets -inf (the mask
- * of kvpop_running_topk always keeps token d itself when w >= 1).  The
- * result feeds kvpop_future_attn_target unchanged.
+ * with keep_until from kvpop_running_topk (h = g / G); keep_until is int32
+ * [B][Hkv][S], 4-byte aligned; q, k and lse as for kvpop_fwd_lse.
+ *   budget:    the budget keep_until was made with (> 0), or 0.  With a
+ *              budget the pass first lists, for every block of P = 128/G
+ *              query positions, the keys still retained at its first query
+ *              (at most budget + P for a running top-k mask) and attends
+ *              over those only; a block whose list would exceed that bound
+ *              (keep_until made otherwise) walks its whole causal row, so
+ *              the result is the same for any keep_until.  With 0 every
+ *              causal key is read and tested.
+ *   workspace: kvpop_workspace_bytes(KVPOP_OP_FWD_LSE_SPARSE, dims, budget)
+ *              bytes, 256-byte aligned with a budget (16 without), no
+ *              initialisation needed; it may be NULL when that is zero.
+ * A row whose retained set is empty gets -inf (the mask of
+ * kvpop_running_topk always keeps token d itself when w >= 1).  The result
+ * feeds kvpop_future_attn_target unchanged.
+ * Errors: as kvpop_fwd_lse; INVALID_ARGUMENT for a NULL keep_until or a
+ * negative budget.
  */
 kvpop_status kvpop_fwd_lse_sparse(const kvpop_dims* dims, const void* q, const void* k,
-                                  const int32_t* keep_until, float* lse, void* workspace,
-                                  size_t workspace_bytes, hipStream_t stream);
+                                  const int32_t* keep_until, int budget, float* lse,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * kvpop_future_attn_target -- transposed future-attention pass.

@@ -35,7 +35,7 @@ def test_exports_match_header(lib):
     assert names == set(kv.EXPORTS), names ^ set(kv.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.kvpop_abi_version() == 1
+    assert lib.kvpop_abi_version() == 2
     for s in range(5):
         assert lib.kvpop_status_string(s)
 
@@ -171,15 +171,25 @@ def test_running_topk_and_sparse_lse_validation(lib):
     assert rt(1, 8, 65537, 4, 128, 1024, GOOD, None, GOOD, None, None) == 2     # longest row 65536
     sp = lib.kvpop_fwd_lse_sparse
     d = kv.dims(1, 32, 8, 4096, 128)
-    assert sp(ctypes.byref(d), GOOD, GOOD, None, GOOD, None, 0, None) == 1     # no mask
-    assert sp(ctypes.byref(d), GOOD, GOOD, P(0x10002), GOOD, None, 0, None) == 1
-    assert sp(None, GOOD, GOOD, GOOD, GOOD, None, 0, None) == 1
+    assert sp(ctypes.byref(d), GOOD, GOOD, None, 0, GOOD, None, 0, None) == 1     # no mask
+    assert sp(ctypes.byref(d), GOOD, GOOD, P(0x10002), 0, GOOD, None, 0, None) == 1
+    assert sp(ctypes.byref(d), GOOD, GOOD, GOOD, -1, GOOD, None, 0, None) == 1    # budget < 0
+    assert sp(None, GOOD, GOOD, GOOD, 0, GOOD, None, 0, None) == 1
     d = kv.dims(1, 32, 8, 4096, 96)
-    assert sp(ctypes.byref(d), GOOD, GOOD, GOOD, GOOD, None, 0, None) == 2      # D = 96
+    assert sp(ctypes.byref(d), GOOD, GOOD, GOOD, 0, GOOD, None, 0, None) == 2      # D = 96
     d = kv.dims(1, 32, 8, 4096, 128)
-    need = lib.kvpop_workspace_bytes(2, ctypes.byref(d), 0)
+    need = lib.kvpop_workspace_bytes(3, ctypes.byref(d), 0)
+    assert need == lib.kvpop_workspace_bytes(2, ctypes.byref(d), 0)
     if need:
-        assert sp(ctypes.byref(d), GOOD, GOOD, GOOD, GOOD, GOOD, need - 16, None) == 3
+        assert sp(ctypes.byref(d), GOOD, GOOD, GOOD, 0, GOOD, GOOD, need - 16, None) == 3
+    # with a budget: a header per block of 32 queries (8 heads x 128 blocks),
+    # then 1024 + 32 listed keys per block
+    need = lib.kvpop_workspace_bytes(3, ctypes.byref(d), 1024)
+    assert need == 8 * 128 * 8 + 8 * 128 * 1088 * 4
+    assert lib.kvpop_workspace_bytes(3, ctypes.byref(d), -1) == 0
+    assert sp(ctypes.byref(d), GOOD, GOOD, GOOD, 1024, GOOD, None, 0, None) == 1   # no workspace
+    assert sp(ctypes.byref(d), GOOD, GOOD, GOOD, 1024, GOOD, P(0x10010), need, None) == 1  # 256 B
+    assert sp(ctypes.byref(d), GOOD, GOOD, GOOD, 1024, GOOD, GOOD, need - 1, None) == 3
 
 
 def test_mlstm_step_validation(lib):

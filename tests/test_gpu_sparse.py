@@ -11,7 +11,11 @@ App. F (fp32 ranking).
 keep_until and cutoff are integer outputs of an fp32 ranking that both sides
 take in fp32: they must match bit for bit.  The sparse LSE has the dense
 pass's tolerance (|err| <= 1e-3) and the target mass on top of it
-(|err| <= 1e-5 + 2e-3 |ref|).
+(|err| <= 1e-5 + 2e-3 |ref|).  The sparse pass runs in both of its modes:
+listed (the budget is given: each block of queries walks the keys still
+retained at its first query) and tested (every causal key is read and
+tested); a listed call whose lists overflow (keep_until not made with that
+budget) must still give the exact set's normalizers.
 """
 import numpy as np
 import pytest
@@ -20,6 +24,7 @@ import torch
 import oracle
 import synth
 from gpu_util import LSE_ATOL, MASS_ATOL, MASS_RTOL, assert_close, ensure_built, f32
+from oracle import brute
 
 pytestmark = pytest.mark.gpu
 
@@ -112,10 +117,10 @@ def test_tiny_sparse_target_full_parity(kv):
     wl = synth.TINY
     q, k, _ = synth.attention_inputs(wl, seed=1)
     sc = synth.scores((wl.B, wl.Hkv, wl.S), seed=21)
-    for lam in (None, [0.02]):
+    for lam, budget in ((None, 0), ([0.02], 0), (None, wl.budget), ([0.02], wl.budget)):
         ld = None if lam is None else torch.tensor(lam, dtype=torch.float32).cuda()
         u, _ = kv.running_topk(sc.cuda(), wl.n_sink, wl.window, wl.budget, log_decay=ld)
-        lse = kv.fwd_lse_sparse(q.cuda(), k.cuda(), u)
+        lse = kv.fwd_lse_sparse(q.cuda(), k.cuda(), u, budget)
         mass = kv.future_attn_target(q.cuda(), k.cuda(), lse, wl.window)
         torch.cuda.synchronize()
         ol = oracle.lse_sparse(f32(q), f32(k), sc.numpy(), wl.n_sink, wl.window, wl.budget,
@@ -129,8 +134,9 @@ def test_tiny_sparse_target_full_parity(kv):
         assert (f32(lse) <= f32(dense) + 1e-4).all()
 
 
-@pytest.mark.parametrize("G,D", [(4, 128), (2, 64), (1, 128)])
-def test_mid_size_sparse_target(kv, G, D):
+@pytest.mark.parametrize("listed", [False, True])
+@pytest.mark.parametrize("G,D", [(4, 128), (2, 64), (1, 128), (8, 128)])
+def test_mid_size_sparse_target(kv, G, D, listed):
     """B=2, 2 KV heads, S=1100 (ragged against every tile): sparse LSE and the
     target on it, against the oracle in full."""
     wl = synth.Workload("mid", 2, 2 * G, 2, D, 1100, 64, 4, 400, rope=True, std=0.5)
@@ -139,7 +145,7 @@ def test_mid_size_sparse_target(kv, G, D):
     lam = [0.0, 2e-3]
     u, _ = kv.running_topk(sc.cuda(), wl.n_sink, wl.window, wl.budget,
                            log_decay=torch.tensor(lam, dtype=torch.float32).cuda())
-    lse = kv.fwd_lse_sparse(q.cuda(), k.cuda(), u)
+    lse = kv.fwd_lse_sparse(q.cuda(), k.cuda(), u, wl.budget if listed else 0)
     mass = kv.future_attn_target(q.cuda(), k.cuda(), lse, wl.window)
     torch.cuda.synchronize()
     ol = oracle.lse_sparse(f32(q), f32(k), sc.numpy(), wl.n_sink, wl.window, wl.budget,
@@ -157,13 +163,17 @@ def test_layer_shape_sparse_lse_sampled_rows(kv):
     q, k, _ = synth.attention_inputs(wl, seed=7, device="cuda")
     sc = synth.scores((wl.B, wl.Hkv, wl.S), seed=77)
     u, _ = kv.running_topk(sc.cuda(), wl.n_sink, wl.window, wl.budget)
-    lse = kv.fwd_lse_sparse(q, k, u)
+    lse = kv.fwd_lse_sparse(q, k, u, wl.budget)
+    tested = kv.fwd_lse_sparse(q, k, u)
     torch.cuda.synchronize()
     rng = np.random.default_rng(3)
     d = np.concatenate([[0, 1, wl.budget - 1, wl.budget, wl.S - 1], rng.integers(0, wl.S, 27)])
     rows = np.array([g * wl.S + x for g in range(wl.Hq) for x in d], np.int64)
     ref = _sparse_oracle_rows(q.cpu(), k.cpu(), sc, wl.n_sink, wl.window, wl.budget, None, rows)
-    assert_close(f32(lse).reshape(-1)[rows], ref, LSE_ATOL, 0, "sparse lse rows")
+    assert_close(f32(lse).reshape(-1)[rows], ref, LSE_ATOL, 0, "sparse lse rows (listed)")
+    assert_close(f32(tested).reshape(-1)[rows], ref, LSE_ATOL, 0, "sparse lse rows (tested)")
+    # every row: the two modes sum the same set in a different order
+    assert_close(f32(lse), f32(tested), LSE_ATOL, 0, "listed against tested, all rows")
 
 
 def test_sparse_equals_dense_when_nothing_is_evicted(kv):
@@ -175,9 +185,47 @@ def test_sparse_equals_dense_when_nothing_is_evicted(kv):
     u, _ = kv.running_topk(sc, wl.n_sink, wl.window, wl.budget)
     a = kv.fwd_lse_sparse(q, k, u)
     b = kv.fwd_lse(q, k)
+    c = kv.fwd_lse_sparse(q, k, u, wl.budget)
     torch.cuda.synchronize()
     assert (u.cpu().numpy() == wl.S).all()
     assert torch.equal(a, b)
+    assert_close(f32(c), f32(b), LSE_ATOL, 0, "listed, nothing evicted")
+
+
+def _arbitrary_until(B, H, S, seed, kind):
+    """keep_until arrays that no running top-k of a small budget makes."""
+    rng = np.random.default_rng(seed)
+    t = np.arange(S)
+    if kind == "uniform":  # each key leaves at a random later query
+        u = t + 1 + (rng.random((B, H, S)) * (S - t)).astype(np.int64)
+    elif kind == "mass_exit":  # most keys leave together inside one query block
+        u = np.broadcast_to(np.where(t < S // 2, S // 2 + 3, S), (B, H, S)).copy()
+        u[..., :4] = S
+    else:  # keys never retained or retained at their own query only: empty rows
+        u = rng.integers(0, 3, (B, H, S)) + t - 1
+        u[..., 100::5] = S
+    return np.clip(u, 0, S).astype(np.int32)
+
+
+@pytest.mark.parametrize("kind", ["uniform", "mass_exit", "empty_rows"])
+@pytest.mark.parametrize("budget", [0, 24, 200, 100000])
+def test_sparse_lse_any_keep_until(kv, kind, budget):
+    """keep_until not made by the running top-k (and budgets that do not
+    bound it): blocks whose list overflows walk their whole causal row, the
+    others their list; every row must be the LSE over {t <= d < keep_until[t]}
+    (brute force over the explicit membership mask; -inf for an empty set)."""
+    wl = synth.Workload("any", 1, 4, 2, 128, 650, 16, 4, 64, rope=False, std=1.0)
+    q, k, _ = synth.attention_inputs(wl, seed=31)
+    u = _arbitrary_until(1, 2, wl.S, 5, kind)
+    got = kv.fwd_lse_sparse(q.cuda(), k.cuda(), torch.from_numpy(u).cuda(), budget)
+    torch.cuda.synchronize()
+    d = np.arange(wl.S)
+    member = (d[None, None, None, :] <= d[None, None, :, None]) & (d[None, None, :, None] < u[:, :, None, :])
+    ref = brute.lse_masked(f32(q), f32(k), member)
+    g = f32(got)
+    assert np.array_equal(np.isneginf(g), np.isneginf(ref)), "empty rows"
+    fin = np.isfinite(ref)
+    assert_close(g[fin], ref[fin], LSE_ATOL, 0, f"lse over any keep_until ({kind}, budget {budget})")
 
 
 def test_sparse_abi_errors(kv):
@@ -191,6 +239,7 @@ def test_sparse_abi_errors(kv):
     assert L.kvpop_running_topk(1, 1, 64, 4, 16, 30, None, None, pu, None, None) == 1
     assert L.kvpop_running_topk(0, 1, 64, 4, 16, 30, p, None, pu, None, None) == 1
     d = kv.dims(1, 2, 1, 64, 96)
-    assert L.kvpop_fwd_lse_sparse(ctypes.byref(d), p, p, pu, p, None, 0, None) == 2  # D = 96
+    assert L.kvpop_fwd_lse_sparse(ctypes.byref(d), p, p, pu, 0, p, None, 0, None) == 2  # D = 96
     d = kv.dims(1, 2, 1, 64, 64)
-    assert L.kvpop_fwd_lse_sparse(ctypes.byref(d), p, p, None, p, None, 0, None) == 1
+    assert L.kvpop_fwd_lse_sparse(ctypes.byref(d), p, p, None, 0, p, None, 0, None) == 1
+    assert L.kvpop_fwd_lse_sparse(ctypes.byref(d), p, p, pu, 16, p, None, 0, None) == 1  # no workspace
