@@ -41,8 +41,8 @@ FP32_VECTOR_PEAK_TFS = 157.3     # MI355X fp32 vector (counts packed FMA; one FM
 # the kernel code it was taken on (sources_digest): bench reports null once
 # that changes.
 TRAFFIC_SOURCES = ("future_target.hip", "common.h", "launch.h")
-TRAFFIC = {"sha256": "636021f94b8101d5400c107d008d33b83ade640f805014dbffbdc814467c5819",
-           "fetch_bytes": 2 * (22914.5 + 325.0) * 1024, "write_bytes": (577.7 + 128.0) * 1024}
+TRAFFIC = {"sha256": "2680e749021cdc622038ebce49365a3827392d31c3e2d79cfdcd018d50410731",
+           "fetch_bytes": 2 * (23013.5 + 325.0) * 1024, "write_bytes": (577.6 + 128.0) * 1024}
 METRIC = "future-attn target keys/s + MFMA util; bounded-cache decode steps/s + HBM util"
 
 
