@@ -241,13 +241,15 @@ def listed_flops(until, S, G, D):
     rounded up to whole 64-key tiles, for 128 query rows."""
     P = 128 // G
     nb = (S + P - 1) // P
-    p0 = torch.arange(nb, device=until.device, dtype=torch.int64) * P
     t = torch.arange(S, device=until.device, dtype=torch.int64)
     u = until.to(torch.int64).reshape(-1, 1, S)
-    alive = ((t[None, None, :] < p0[None, :, None]) & (u > p0[None, :, None])).sum(-1)
-    n = alive + (torch.clamp(p0 + P, max=S) - p0)[None, :]
-    tiles = (n + 63) // 64
-    return float(tiles.sum().item()) * 2.0 * D * 64 * 128
+    tiles = 0
+    for c0 in range(0, nb, 128):  # blocks in groups, to bound the temporaries
+        p0 = torch.arange(c0, min(nb, c0 + 128), device=until.device, dtype=torch.int64) * P
+        alive = ((t[None, None, :] < p0[None, :, None]) & (u > p0[None, :, None])).sum(-1)
+        n = alive + (torch.clamp(p0 + P, max=S) - p0)[None, :]
+        tiles += int(((n + 63) // 64).sum().item())
+    return float(tiles) * 2.0 * D * 64 * 128
 
 
 def bench_sparse(kv, st, reps=20):
@@ -320,23 +322,52 @@ def bench_sparse(kv, st, reps=20):
                                    "frac": tf(f_tr, t_tr) / MFMA_BF16_PEAK_TFLOPS}}
 
 
-def bench_running_topk_long(kv, w, reps=5):
-    """The running top-k mask alone at a long-context shape (8 KV heads of
-    seeded scores, budget of the workload)."""
-    sc = synth.scores((w.B, w.Hkv, w.S), seed=4000, device="cuda")
-    until = torch.empty(sc.shape, dtype=torch.int32, device="cuda")
+def bench_sparse_long(kv, w, reps=3):
+    """The sparse normalizer on one long-context layer (8 KV heads, the
+    workload's budget, seeded scores): the running top-k mask alone, then
+    the listed sparse causal pass (key lists + pass), with the dense causal
+    pass on the same inputs timed beside it."""
+    dev = "cuda"
+    q, k, _ = synth.attention_inputs(w, seed=4000, device=dev)
+    sc = synth.scores((w.B, w.Hkv, w.S), seed=4000, device=dev)
+    until = torch.empty(sc.shape, dtype=torch.int32, device=dev)
     cut = torch.empty_like(until)
-    kv.running_topk(sc, w.n_sink, w.window, w.budget, out=until, out_cutoff=cut)
-    torch.cuda.synchronize()
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(reps):
-        kv.running_topk(sc, w.n_sink, w.window, w.budget, out=until, out_cutoff=cut)
-    b.record()
-    torch.cuda.synchronize()
+    d = kv.dims(w.B, w.Hq, w.Hkv, w.S, w.D)
+    sws = torch.empty(kv.workspace_bytes(kv.OP_FWD_LSE_SPARSE, d, w.budget), dtype=torch.uint8,
+                      device=dev)
+    nb = kv.workspace_bytes(kv.OP_FWD_LSE, d)
+    dws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+    lse = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device=dev)
+
+    def t_ms(fn):
+        fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    t_mask = t_ms(lambda: kv.running_topk(sc, w.n_sink, w.window, w.budget, out=until,
+                                          out_cutoff=cut))
+    t_listed = t_ms(lambda: kv.fwd_lse_sparse(q, k, until, w.budget, out=lse, workspace=sws))
+    t_dense = t_ms(lambda: kv.fwd_lse(q, k, out=lse, workspace=dws))
+    G = w.Hq // w.Hkv
+    f_live = 2.0 * w.D * G * live_pairs(until, w.S)
+    f_exec = listed_flops(until, w.S, G, w.D)
+    f_dense, _ = target_flops(w)
+    tf = lambda f, ms: f / (ms / 1e3) / 1e12
     return {"workload": w.name, "rows": w.B * w.Hkv, "seq_len": w.S, "budget": w.budget,
-            "ms": a.elapsed_time(b) / reps}
+            "running_topk_ms": t_mask,
+            "fwd_lse_sparse": {"mode": "listed", "ms": t_listed, "executed_flops": f_exec,
+                               "executed_frac": tf(f_exec, t_listed) / MFMA_BF16_PEAK_TFLOPS,
+                               "retained_pair_flops": f_live,
+                               "retained_frac": tf(f_live, t_listed) / MFMA_BF16_PEAK_TFLOPS,
+                               "workspace_bytes": sws.numel()},
+            "dense_fwd_lse": {"ms": t_dense, "frac": tf(f_dense, t_dense) / MFMA_BF16_PEAK_TFLOPS}}
 
 
 def bench_prefill(kv, w, layers=None, reps=1, seed=None, warm=1):
@@ -819,7 +850,7 @@ def main():
         out["skewed_long"] = bench_prefill(kv, synth.SKEWED, reps=4, warm=3)
         log("qwen3-8b-prefill: 36 layers x 32768, 1 timed pass")
         out["prefill_36_layers"] = bench_prefill(kv, synth.QWEN8B, reps=1)
-        out["prefill_36_layers"]["running_topk_one_layer"] = bench_running_topk_long(kv, synth.QWEN8B)
+        out["prefill_36_layers"]["sparse_one_layer"] = bench_sparse_long(kv, synth.QWEN8B)
     if not a.no_decode:
         log(f"decode: {a.decode_steps} steps x {a.decode_layers} layers")
         out["decode"] = bench_decode(kv, a.decode_steps, a.decode_layers)

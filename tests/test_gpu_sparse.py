@@ -176,6 +176,29 @@ def test_layer_shape_sparse_lse_sampled_rows(kv):
     assert_close(f32(lse), f32(tested), LSE_ATOL, 0, "listed against tested, all rows")
 
 
+def test_prefill_shape_listed_sparse_lse_sampled_rows(kv):
+    """The 32k-prefill layer shape (32 q / 8 KV heads, S = 32768, budget
+    8192, RoPE) in the listed launch the bench times (lists of up to 8256
+    keys per block of 32 queries): sampled rows of every head against the
+    oracle, and every row against the tested mode."""
+    wl = synth.QWEN8B
+    q, k, _ = synth.attention_inputs(wl, seed=9, device="cuda")
+    sc = synth.scores((wl.B, wl.Hkv, wl.S), seed=99)
+    lam = torch.tensor([0.0, 1e-5, 0.0, 1e-4, 0.0, 3e-5, 0.0, 2e-4], dtype=torch.float32)
+    u, _ = kv.running_topk(sc.cuda(), wl.n_sink, wl.window, wl.budget, log_decay=lam.cuda())
+    lse = kv.fwd_lse_sparse(q, k, u, wl.budget)
+    tested = kv.fwd_lse_sparse(q, k, u)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    d = np.concatenate([[0, wl.budget - 1, wl.budget, wl.budget + 31, wl.S - 1],
+                        rng.integers(0, wl.S, 7)])
+    rows = np.array([g * wl.S + x for g in range(wl.Hq) for x in d], np.int64)
+    ref = _sparse_oracle_rows(q.cpu(), k.cpu(), sc, wl.n_sink, wl.window, wl.budget,
+                              lam.numpy(), rows)
+    assert_close(f32(lse).reshape(-1)[rows], ref, LSE_ATOL, 0, "32k sparse lse rows (listed)")
+    assert_close(f32(lse), f32(tested), LSE_ATOL, 0, "32k listed against tested, all rows")
+
+
 def test_sparse_equals_dense_when_nothing_is_evicted(kv):
     """A budget covering the whole sequence keeps every key: the sparse pass
     must give the dense pass's normalizers."""
