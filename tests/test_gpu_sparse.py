@@ -251,6 +251,25 @@ def test_sparse_lse_any_keep_until(kv, kind, budget):
     assert_close(g[fin], ref[fin], LSE_ATOL, 0, f"lse over any keep_until ({kind}, budget {budget})")
 
 
+@pytest.mark.parametrize("S", [1, 2, 63, 65, 130])
+@pytest.mark.parametrize("budget", [0, 8, 1000])
+def test_sparse_lse_short_rows(kv, S, budget):
+    """Sequences shorter than one key tile or one query block, and just past
+    them (G = 4, P = 32), in both modes, against brute force."""
+    wl = synth.Workload("short", 1, 8, 2, 64, S, 4, 1, 8, rope=False, std=1.0)
+    q, k, _ = synth.attention_inputs(wl, seed=S)
+    u = _arbitrary_until(1, 2, S, S + 1, "uniform")
+    got = kv.fwd_lse_sparse(q.cuda(), k.cuda(), torch.from_numpy(u).cuda(), budget)
+    torch.cuda.synchronize()
+    d = np.arange(S)
+    member = (d[None, None, None, :] <= d[None, None, :, None]) & (d[None, None, :, None] < u[:, :, None, :])
+    ref = brute.lse_masked(f32(q), f32(k), member)
+    g = f32(got)
+    assert np.array_equal(np.isneginf(g), np.isneginf(ref))
+    fin = np.isfinite(ref)
+    assert_close(g[fin], ref[fin], LSE_ATOL, 0, f"short rows S={S} budget={budget}")
+
+
 def test_sparse_abi_errors(kv):
     import ctypes
     L = kv.lib()
