@@ -115,9 +115,12 @@ def _same_state(g, o, what):
 
 
 @pytest.mark.parametrize("s,w,k,delay,D", [(4, 16, 40, 5, 128), (1, 8, 6, 0, 64), (0, 4, 3, 3, 128),
-                                           (2, 5, 0, 2, 64), (4, 256, 3836, 16, 128)])
+                                           (2, 5, 0, 2, 64), (4, 256, 3836, 16, 128),
+                                           (4, 256, 5000, 16, 128)])  # > 4096 kept: multi-pass scan
 def test_cache_step_bit_exact_with_given_scores(kv, s, w, k, delay, D):
-    """Decisions from identical fp32 scores must match the oracle bit for bit."""
+    """Decisions from identical fp32 scores must match the oracle bit for bit.
+    The last case keeps more long-range tokens than one pass of the step's
+    worst-token scan covers (4096), so the scan runs in several passes."""
     B, Hkv = 3, 2
     budget = s + w + k
     S0 = max(2 * budget, s + w + 3)
