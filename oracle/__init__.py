@@ -11,14 +11,14 @@ this oracle at tiny sizes.
 
 Method source: "KVpop -- Key-Value Cache Compression with Predictive Online
 Pruning" (arXiv 2607.05061v2), paperlayer.ai summary: App. D.1-D.4 (target;
-D.3 sparse normalizer), App. C.1-C.2 (running top-k mask and its cutoffs), App. A and E.3-E.4 (the
+D.3 sparse normalizer; D.4 and App. I the main pass's attention output), App. C.1-C.2 (running top-k mask and its cutoffs), App. A and E.3-E.4 (the
 delayed stateful mLSTM scorer),
 App. B.1-B.2 (aggregation, count normalisation), Sec. 3 and App. C.1
 (fixed-budget retention), App. E.2 and E.4 (scorer, delayed readout).
 
 Parity status per function (see the tests under tests/test_oracle_*.py):
   lse, future_mass, select, gather, decode_attend, mlp_score, cache_step,
-  running_topk, lse_sparse, mlstm_scores: pinned (brute force, closed forms, invariants,
+  running_topk, lse_sparse, mlstm_scores, attn_out: pinned (brute force, closed forms, invariants,
   hand-worked fixtures).
 """
 import ctypes
@@ -53,9 +53,10 @@ def _lib():
         lib.oracle_running_topk.argtypes = [I, I, I, I, I, I, P, P, P, P]
         lib.oracle_lse_sparse.argtypes = [I, I, I, I, I, Dd, P, P, P, P, I, I, I, L, P, P, I]
         lib.oracle_mlstm_scores.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P]
+        lib.oracle_attn_out.argtypes = [I, I, I, I, I, Dd, P, P, P, P, P, I, I, I, L, P, P, P, P, I]
         for f in ("oracle_lse", "oracle_future_mass", "oracle_select", "oracle_decode_attend",
                   "oracle_mlp_score", "oracle_cache_step", "oracle_running_topk",
-                  "oracle_lse_sparse", "oracle_mlstm_scores"):
+                  "oracle_lse_sparse", "oracle_mlstm_scores", "oracle_attn_out"):
             getattr(lib, f).restype = ctypes.c_int
         _LIB = lib
     return _LIB
@@ -217,6 +218,52 @@ def lse_sparse(q, k, scores, n_sink, window, budget, log_decay=None, scale=None,
                                     int(budget), n, rp, _ptr(out), _threads(nthreads)),
            "lse_sparse")
     return out.reshape(B, Hq, S) if rows is None else out
+
+
+def attn_out(q, k, v, scores=None, n_sink=0, window=0, budget=0, log_decay=None, scale=None,
+             rows=None, want_abs=True, nthreads=None):
+    """Attention output of the main pass (App. D.4 first step; App. I, the
+    sparse student attention over the fixed-budget mask of App. C.1).
+
+    q [B,Hq,S,D], k, v [B,Hkv,S,D] (float values).  scores None: dense
+    causal rows R_d = [0, d]; else fp32 [B,Hkv,S] with n_sink, window,
+    budget (and log_decay) give the running top-k mask's R_d.  Returns
+    (o, o_abs, lse): o[..., c] = sum_{t in R_d} p_dt v_t[c], o_abs the same
+    with |v_t[c]| (None unless want_abs), lse the row's natural-log
+    normalizer; shapes [B,Hq,S,D] / [B,Hq,S], or [n,D] / [n] over ``rows``.
+    """
+    q = _f32(q)
+    k = _f32(k)
+    v = _f32(v)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    assert k.shape == (B, Hkv, S, D) and v.shape == k.shape
+    sc = None if scores is None else _f32(scores)
+    if sc is not None:
+        assert sc.shape == (B, Hkv, S)
+    ld = None if log_decay is None else _f32(log_decay).reshape(Hkv)
+    s_ = default_scale(D) if scale is None else float(scale)
+    if rows is None:
+        n = B * Hq * S
+        rp = None
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        n = rows.size
+        rp = _ptr(rows)
+    o = np.empty((n, D), np.float64)
+    oa = np.empty((n, D), np.float64) if want_abs else None
+    ls = np.empty(n, np.float64)
+    _check(_lib().oracle_attn_out(B, Hq, Hkv, S, D, s_, _ptr(q), _ptr(k), _ptr(v),
+                                  None if sc is None else _ptr(sc),
+                                  None if ld is None else _ptr(ld), int(n_sink), int(window),
+                                  int(budget), n, rp, _ptr(ls), _ptr(o),
+                                  None if oa is None else _ptr(oa), _threads(nthreads)),
+           "attn_out")
+    if rows is None:
+        o = o.reshape(B, Hq, S, D)
+        oa = None if oa is None else oa.reshape(B, Hq, S, D)
+        ls = ls.reshape(B, Hq, S)
+    return o, oa, ls
 
 
 MLSTM_KEYS = ("wk", "wr", "wv", "wi", "bi", "wf", "bf", "wo", "bo")

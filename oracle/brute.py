@@ -179,6 +179,19 @@ def lse_masked(q, k, member, scale=None):
     return logsumexp(np.where(m, z, -np.inf), axis=-1)
 
 
+def attn_masked(q, k, v, member, scale=None):
+    """Softmax attention output over an explicit membership mask
+    member[b, h, d, t] (bool), float64: the probability matrix of the
+    masked rows times V.  Returns (o [B,Hq,S,D], lse [B,Hq,S])."""
+    z = scores(q, k, scale)
+    G = z.shape[1] // member.shape[1]
+    m = np.repeat(member, G, axis=1)
+    zm = np.where(m, z, -np.inf)
+    ls = logsumexp(zm, axis=-1)
+    p = np.where(m, np.exp(zm - ls[..., None]), 0.0)
+    return np.matmul(p, repeat_kv(v, G)), ls
+
+
 def mlstm_scores_unstabilised(keys, values, params, window):
     """The delayed mLSTM scores from the unstabilised recurrence, float64:
     C_q = sum_{t<=q} (prod_{j=t+1..q} sigmoid(f_j)) exp(i_t) val_t phi_t^T (same

@@ -571,6 +571,100 @@ int oracle_lse_sparse(int B, int Hq, int Hkv, int S, int D, double scale,
 }
 
 /* ------------------------------------------------------------------ */
+/* Attention output of the main pass (App. D.4, first step: the main   */
+/* attention pass of the model, whose per-query normalizers the target */
+/* reuses; App. I: the sparse student attention, over the fixed-budget */
+/* mask of App. C.1, supplies the normalizers in the paper's default). */
+/* For query row d of head g (KV head h = g / G):                      */
+/*   R_d    = [0, d] (dense causal) or, given scores, the retained set */
+/*            of the running top-k mask built as for oracle_lse_sparse */
+/*   p_dt   = exp(scale * q_d . k_t - LSE_d),  t in R_d                */
+/*   LSE_d  = log sum_{t in R_d} exp(scale * q_d . k_t)                */
+/*   O_d[c] = sum_{t in R_d} p_dt v_t[c]                               */
+/*   A_d[c] = sum_{t in R_d} p_dt |v_t[c]|   (the scale of O_d[c]'s    */
+/*            sensitivity to a relative change of each p_dt)           */
+/* An empty R_d gives LSE = -inf and O = A = 0.                        */
+/* ------------------------------------------------------------------ */
+typedef struct {
+    int B, Hq, Hkv, S, D;
+    double scale;
+    const float *q, *k, *v, *scores, *log_decay;
+    int n_sink, window, kk;
+    const long* rows;
+    double *lse, *o, *o_abs;
+} attn_ctx;
+
+static void attn_item(void* p, long i, double* z) {
+    attn_ctx* c = (attn_ctx*)p;
+    long r = c->rows ? c->rows[i] : i;
+    int d = (int)(r % c->S);
+    int g = (int)((r / c->S) % c->Hq);
+    int b = (int)(r / ((long)c->S * c->Hq));
+    int h = g / (c->Hq / c->Hkv);
+    char* keep = (char*)(z + c->S);
+    cand* pool = (cand*)(keep + c->S + 8 - (c->S % 8));
+    for (int t = 0; t <= d; ++t) keep[t] = c->scores ? 0 : 1;
+    if (c->scores) {  /* sinks, window and the k best of the pool P_d = [s, d-w] */
+        const float* sc = c->scores + ((long)b * c->Hkv + h) * c->S;
+        float lam = c->log_decay ? c->log_decay[h] : 0.0f;
+        for (int t = 0; t <= d && t < c->n_sink; ++t) keep[t] = 1;
+        for (int t = d - c->window + 1; t <= d; ++t) if (t >= 0) keep[t] = 1;
+        int n_pool = 0;
+        for (int t = c->n_sink; t <= d - c->window; ++t) {
+            pool[n_pool].score = priority(sc[t], lam, t);
+            pool[n_pool].pos = t;
+            ++n_pool;
+        }
+        qsort(pool, (size_t)n_pool, sizeof(cand), cand_cmp);
+        for (int j = 0; j < n_pool && j < c->kk; ++j) keep[pool[j].pos] = 1;
+    }
+    const float* qd = c->q + (((long)b * c->Hq + g) * c->S + d) * c->D;
+    const float* kh = c->k + ((long)b * c->Hkv + h) * (long)c->S * c->D;
+    const float* vh = c->v + ((long)b * c->Hkv + h) * (long)c->S * c->D;
+    double* o = c->o + i * c->D;
+    double* a = c->o_abs ? c->o_abs + i * c->D : NULL;
+    for (int e = 0; e < c->D; ++e) { o[e] = 0.0; if (a) a[e] = 0.0; }
+    double m = -INFINITY;
+    for (int t = 0; t <= d; ++t) {
+        if (!keep[t]) continue;
+        z[t] = c->scale * dot(qd, kh + (long)t * c->D, c->D);
+        if (z[t] > m) m = z[t];
+    }
+    if (m == -INFINITY) { c->lse[i] = -INFINITY; return; }
+    double sum = 0.0;
+    for (int t = 0; t <= d; ++t) if (keep[t]) sum += exp(z[t] - m);
+    double lse = m + log(sum);
+    c->lse[i] = lse;
+    for (int t = 0; t <= d; ++t) {
+        if (!keep[t]) continue;
+        double pt = exp(z[t] - lse);
+        const float* vt = vh + (long)t * c->D;
+        for (int e = 0; e < c->D; ++e) {
+            o[e] += pt * (double)vt[e];
+            if (a) a[e] += pt * fabs((double)vt[e]);
+        }
+    }
+}
+
+/* scores == NULL: dense causal rows; otherwise the running top-k mask    */
+/* with sinks, window, budget and the nullable per-head log_decay.        */
+/* rows: flat indices (b*Hq + g)*S + d, or NULL for all rows in order;    */
+/* lse [n_rows], o and o_abs [n_rows][D] (o_abs nullable).                */
+int oracle_attn_out(int B, int Hq, int Hkv, int S, int D, double scale,
+                    const float* q, const float* k, const float* v, const float* scores,
+                    const float* log_decay, int n_sink, int window, int budget,
+                    long n_rows, const long* rows, double* lse, double* o, double* o_abs,
+                    int nthreads) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || D <= 0 || Hq % Hkv) return 1;
+    if (scores && (n_sink < 0 || window < 0 || budget - n_sink - window < 0)) return 1;
+    attn_ctx c = {B, Hq, Hkv, S, D, scale, q, k, v, scores, log_decay, n_sink, window,
+                  budget - n_sink - window, rows, lse, o, o_abs};
+    /* doubles: S logits + S flag bytes + S pool entries (8 bytes each) + slack */
+    run_items(attn_item, &c, n_rows, nthreads, 2L * S + S / 8 + 4);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* Delayed stateful mLSTM scorer (App. A linear-attention background;  */
 /* App. E.1 headwise input x = [k; v]; App. E.3 matrix memory C, norm- */
 /* alizer n, scalar input/forget gates from headwise projections, the  */
