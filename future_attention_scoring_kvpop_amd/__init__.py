@@ -30,7 +30,9 @@ OP_FWD_LSE_SPARSE = 3
 EXPORTS = ("kvpop_abi_version", "kvpop_status_string", "kvpop_workspace_bytes", "kvpop_fwd_lse",
            "kvpop_future_attn_target", "kvpop_evict_select", "kvpop_decode_attend",
            "kvpop_score_mlp", "kvpop_cache_step", "kvpop_decode_step", "kvpop_running_topk",
-           "kvpop_fwd_lse_sparse", "kvpop_mlstm_step", "kvpop_decode_step_mlstm")
+           "kvpop_fwd_lse_sparse", "kvpop_mlstm_step", "kvpop_decode_step_mlstm",
+           "kvpop_decode_attend_noalloc")
+DECODE_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 
 class KvpopError(RuntimeError):
@@ -79,6 +81,7 @@ def lib():
             "kvpop_future_attn_target": (I, [DP, P, P, P, I, I, I, I, P, P, P, Z, P]),
             "kvpop_evict_select": (I, [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P]),
             "kvpop_decode_attend": (I, [DP, P, P, P, P, P, I, P, P, Z, P]),
+            "kvpop_decode_attend_noalloc": (I, [DP, P, P, P, P, P, I, P, P]),
             "kvpop_score_mlp": (I, [I, I, I, I, I, P, P, P, P, P, P, P]),
             "kvpop_cache_step": (I, [I, I, I, I, I, I, I, I, P, P, P, P, P, P, I, P, P, P, P, P, P]),
             "kvpop_decode_step": (I, [DP, I, I, I, I, P, P, P, P, P, P, I, P, P, P, P, P, P, P, I, P,
@@ -344,6 +347,29 @@ def decode_attend(q, k_cache, v_cache, slot_pos, out_dtype=torch.float32, want_l
                                    _p(o), 1 if o.dtype == torch.bfloat16 else 0, _p(lse), _p(ws),
                                    0 if ws is None else ws.numel(), _stream())
     _check("kvpop_decode_attend", st)
+    return o, lse
+
+
+def decode_attend_noalloc(q, k_cache, v_cache, slot_pos, out_dtype=torch.float32, want_lse=True,
+                          scale=0.0, out=None, out_lse=None):
+    """decode_attend through kvpop_decode_attend_noalloc: no workspace, the
+    library's fixed device array holds the split partials (for callers that
+    cannot allocate; the outputs are still the caller's)."""
+    _need(q, torch.bfloat16, "q", 3)
+    _need(k_cache, torch.bfloat16, "k_cache", 4)
+    _need(v_cache, torch.bfloat16, "v_cache", 4)
+    _need(slot_pos, torch.int32, "slot_pos", 3)
+    B, Hq, D = q.shape
+    Hkv, n = k_cache.shape[1], k_cache.shape[2]
+    d = dims(B, Hq, Hkv, n, D, scale)
+    o = out if out is not None else torch.empty((B, Hq, D), dtype=out_dtype, device=q.device)
+    lse = out_lse if out_lse is not None else (
+        torch.empty((B, Hq), dtype=torch.float32, device=q.device) if want_lse else None)
+    st = lib().kvpop_decode_attend_noalloc(ctypes.byref(d), _p(q), _p(k_cache), _p(v_cache),
+                                           _p(slot_pos), _p(o),
+                                           1 if o.dtype == torch.bfloat16 else 0, _p(lse),
+                                           _stream())
+    _check("kvpop_decode_attend_noalloc", st)
     return o, lse
 
 

@@ -269,6 +269,24 @@ kvpop_status kvpop_decode_attend(const kvpop_dims* dims, const void* q, const vo
                                        stream));
 }
 
+kvpop_status kvpop_decode_attend_noalloc(const kvpop_dims* dims, const void* q,
+                                         const void* k_cache, const void* v_cache,
+                                         const int32_t* slot_pos, void* o,
+                                         kvpop_out_dtype o_dtype, float* lse, hipStream_t stream) {
+  AttnShape s;
+  kvpop_status st = check_dims(dims, &s);
+  if (st != KVPOP_OK) return st;
+  if (!q || !k_cache || !v_cache || !slot_pos || !o) return KVPOP_ERR_INVALID_ARGUMENT;
+  if (o_dtype != KVPOP_OUT_F32 && o_dtype != KVPOP_OUT_BF16) return KVPOP_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(slot_pos, 4) ||
+      !aligned(o, 4) || (lse && !aligned(lse, 4)))
+    return KVPOP_ERR_INVALID_ARGUMENT;
+  if (kvpop::plan_decode(s).workspace_floats * sizeof(float) > kvpop::decode_noalloc_capacity())
+    return KVPOP_ERR_WORKSPACE_TOO_SMALL;
+  return from_hip(kvpop::launch_decode_noalloc(s, q, k_cache, v_cache, slot_pos, o,
+                                               o_dtype == KVPOP_OUT_BF16 ? 1 : 0, lse, stream));
+}
+
 kvpop_status kvpop_score_mlp(int batch, int n_kv_heads, int n_tok, int head_dim, int hidden,
                              const void* keys, const float* w1, const float* b1, const float* w2,
                              const float* b2, float* scores, hipStream_t stream) {

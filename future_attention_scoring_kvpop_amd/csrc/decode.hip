@@ -2,8 +2,10 @@
 // split partial states, and the plan that sizes the split (device code in
 // decode_dev.h).
 #include <atomic>
+#include <mutex>
 
 #include "decode_dev.h"
+#include "kvpop.h"
 #include "launch.h"
 
 namespace kvpop {
@@ -50,6 +52,13 @@ __global__ void decode_merge_kernel(const float* __restrict__ ws, void* __restri
     if (f == 0 && lse_out) lse_out[bg] = L > 0.f ? (M + fast_log2(L)) * kLn2 : -INFINITY;
   }
 }
+
+// Split partials of the allocation-free entry point: a fixed array in device
+// memory (each device the library runs on holds its own copy until the
+// process ends).  Host code never passes this name to a kernel: the array's
+// device address is looked up once per device (noalloc_scratch) and that
+// address is what the kernels receive.
+static __device__ __align__(256) float scratch[KVPOP_DECODE_NOALLOC_SCRATCH_BYTES / sizeof(float)];
 
 }  // namespace
 
@@ -136,6 +145,45 @@ hipError_t launch_decode(const AttnShape& s, const void* q, const void* kc, cons
   hipLaunchKernelGGL(decode_merge_kernel, dim3(s.B * s.Hq), dim3(s.D), 0, st, workspace, o, o_bf16,
                      lse, s.Hq, s.Hkv, s.D, p.n_split);
   return hipGetLastError();
+}
+
+// Device address of this device's scratch array, looked up on the first
+// call on each device (with that device current) and kept per device.
+static hipError_t noalloc_scratch(float** out) {
+  static std::mutex mu;
+  static std::atomic<float*> addr[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  float* p = addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(mu);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      void* a = nullptr;
+      e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!a) return hipErrorInvalidSymbol;
+      p = static_cast<float*>(a);
+      addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+size_t decode_noalloc_capacity() { return sizeof(scratch); }
+
+hipError_t launch_decode_noalloc(const AttnShape& s, const void* q, const void* kc, const void* vc,
+                                 const int32_t* slot_pos, void* o, int o_bf16, float* lse,
+                                 hipStream_t st) {
+  float* ws = nullptr;
+  hipError_t e = noalloc_scratch(&ws);
+  if (e != hipSuccess) return e;
+  // every split writes all of its partial states before the merge reads
+  // them, so the array needs no clearing between calls
+  return launch_decode(s, q, kc, vc, slot_pos, o, o_bf16, lse, ws, st);
 }
 
 }  // namespace kvpop

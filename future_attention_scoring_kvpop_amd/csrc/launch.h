@@ -133,6 +133,14 @@ hipError_t launch_decode(const AttnShape& s, const void* q, const void* kc, cons
                          const int32_t* slot_pos, void* o, int o_bf16, float* lse,
                          float* workspace, hipStream_t st);
 
+// Decode attention with the split partials in the library's own fixed
+// device array (the allocation-free entry point); the caller checks first
+// that plan_decode's workspace fits decode_noalloc_capacity() bytes.
+size_t decode_noalloc_capacity();
+hipError_t launch_decode_noalloc(const AttnShape& s, const void* q, const void* kc, const void* vc,
+                                 const int32_t* slot_pos, void* o, int o_bf16, float* lse,
+                                 hipStream_t st);
+
 hipError_t launch_score_mlp(int B, int Hkv, int n_tok, int D, int hidden, const void* keys,
                             const float* w1, const float* b1, const float* w2, const float* b2,
                             float* scores, hipStream_t st);

@@ -222,6 +222,30 @@ kvpop_status kvpop_decode_attend(const kvpop_dims* dims, const void* q, const vo
                                  size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * kvpop_decode_attend_noalloc -- kvpop_decode_attend for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments, result (bit for
+ * bit) and errors as kvpop_decode_attend, without the workspace: when the
+ * launch splits the slots over several workgroups, their partial states go
+ * to a fixed array of KVPOP_DECODE_NOALLOC_SCRATCH_BYTES inside the library
+ * (one per device, held until the process ends; its address is looked up
+ * on the first call on each device).  The call itself allocates nothing.
+ *   Returns KVPOP_ERR_WORKSPACE_TOO_SMALL, before any launch, when the shape
+ *   needs more than that (kvpop_workspace_bytes(KVPOP_OP_DECODE, dims, 0) >
+ *   KVPOP_DECODE_NOALLOC_SCRATCH_BYTES; never for B * Hkv rows that fill
+ *   the device, which need no split).
+ * All calls on one device share the array and it keeps the last call's
+ * contents: calls that may overlap in time on one device (different
+ * streams, or several host threads) race and must be serialised by the
+ * caller; calls issued in order on one stream are safe.
+ */
+#define KVPOP_DECODE_NOALLOC_SCRATCH_BYTES (8u << 20)
+kvpop_status kvpop_decode_attend_noalloc(const kvpop_dims* dims, const void* q,
+                                         const void* k_cache, const void* v_cache,
+                                         const int32_t* slot_pos, void* o,
+                                         kvpop_out_dtype o_dtype, float* lse, hipStream_t stream);
+
+/*
  * kvpop_score_mlp -- stateless headwise MLP scorer (App. E.2), on keys:
  *   score = b2[h] + sum_j w2[h][j] * gelu(b1[h][j] + sum_c W1[h][j][c] k[c])
  *   gelu(x) = 0.5 x (1 + erf(x / sqrt 2))

@@ -112,6 +112,26 @@ def test_decode_validation(lib):
     assert call(nbytes=need - 1) == 3
 
 
+def test_decode_noalloc_validation(lib):
+    """The allocation-free decode entry point: the same argument checks as
+    kvpop_decode_attend, and a refusal (workspace too small) for shapes whose
+    split partials exceed the library's fixed array."""
+    d = kv.dims(1, 32, 8, 4096, 128)
+    assert 0 < kv.workspace_bytes(kv.OP_DECODE, d) <= kv.DECODE_NOALLOC_SCRATCH_BYTES
+
+    def call(dd=d, o_dtype=0, sp=GOOD, q=GOOD):
+        return lib.kvpop_decode_attend_noalloc(ctypes.byref(dd) if dd is not None else None, q,
+                                               GOOD, GOOD, sp, GOOD, o_dtype, None, None)
+
+    assert call(dd=None) == 1
+    assert call(o_dtype=2) == 1
+    assert call(sp=None) == 1
+    assert call(q=P(0x10008)) == 1  # misaligned
+    big = kv.dims(1, 128, 1, 200000, 128)
+    assert kv.workspace_bytes(kv.OP_DECODE, big) > kv.DECODE_NOALLOC_SCRATCH_BYTES
+    assert call(dd=big) == 3
+
+
 def test_mlp_and_cache_step_validation(lib):
     assert lib.kvpop_score_mlp(1, 8, 10, 128, 65, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, None) == 2
     assert lib.kvpop_score_mlp(1, 8, 10, 96, 64, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, None) == 2
