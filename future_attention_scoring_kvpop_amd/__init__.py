@@ -26,6 +26,7 @@ OP_FUTURE_TARGET = 0
 OP_DECODE = 1
 OP_FWD_LSE = 2
 OP_FWD_LSE_SPARSE = 3
+OP_FWD_ATTN = 4
 
 EXPORTS = ("kvpop_abi_version", "kvpop_status_string", "kvpop_workspace_bytes", "kvpop_fwd_lse",
            "kvpop_future_attn_target", "kvpop_evict_select", "kvpop_decode_attend",
@@ -71,13 +72,13 @@ def lib():
             "kvpop_abi_version": (I, []),
             "kvpop_status_string": (ctypes.c_char_p, [I]),
             "kvpop_workspace_bytes": (Z, [I, DP, I]),
-            "kvpop_fwd_lse": (I, [DP, P, P, P, P, Z, P]),
+            "kvpop_fwd_lse": (I, [DP, P, P, P, P, P, I, P, Z, P]),
             "kvpop_running_topk": (I, [I, I, I, I, I, I, P, P, P, P, P]),
             "kvpop_mlstm_step": (I, [I, I, I, I, I, I, I, P, P, P, P, ctypes.POINTER(MlstmWeights),
                                      P, P, P]),
             "kvpop_decode_step_mlstm": (I, [DP, I, I, I, P, P, ctypes.POINTER(MlstmWeights), P, P, P,
                                             P, P, P, P, I, P, P, Z, P]),
-            "kvpop_fwd_lse_sparse": (I, [DP, P, P, P, I, P, P, Z, P]),
+            "kvpop_fwd_lse_sparse": (I, [DP, P, P, P, P, I, P, P, I, P, Z, P]),
             "kvpop_future_attn_target": (I, [DP, P, P, P, I, I, I, I, P, P, P, Z, P]),
             "kvpop_evict_select": (I, [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P]),
             "kvpop_decode_attend": (I, [DP, P, P, P, P, P, I, P, P, Z, P]),
@@ -127,8 +128,27 @@ def workspace_bytes(op, d, window=0):
     return int(lib().kvpop_workspace_bytes(op, ctypes.byref(d), int(window)))
 
 
-def fwd_lse(q, k, scale=0.0, out=None, workspace=None):
-    """Dense causal log-normalizers LSE [B,Hq,S] fp32 (App. D.1, D.4)."""
+def _attn_out(q, v, k, out_o, out_dtype):
+    """The output buffer of the main pass, or None without v."""
+    if v is None:
+        if out_o is not None:
+            raise ValueError("out_o needs v")
+        return None
+    _need(v, torch.bfloat16, "v", 4)
+    if tuple(v.shape) != tuple(k.shape):
+        raise ValueError("v shape mismatch")
+    o = out_o if out_o is not None else torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    if o.dtype not in (torch.float32, torch.bfloat16) or tuple(o.shape) != tuple(q.shape):
+        raise ValueError("o: expected fp32 or bf16 of q's shape")
+    _need(o, o.dtype, "o")
+    return o
+
+
+def fwd_lse(q, k, scale=0.0, out=None, workspace=None, v=None, out_o=None,
+            out_dtype=torch.float32):
+    """Dense causal log-normalizers LSE [B,Hq,S] fp32 (App. D.1, D.4); with
+    v [B,Hkv,S,D] also the causal attention output O [B,Hq,S,D] (fp32 or
+    bf16 per out_dtype), returned as (lse, o)."""
     _need(q, torch.bfloat16, "q", 4)
     _need(k, torch.bfloat16, "k", 4)
     B, Hq, S, D = q.shape
@@ -137,14 +157,16 @@ def fwd_lse(q, k, scale=0.0, out=None, workspace=None):
         raise ValueError("k shape mismatch")
     lse = out if out is not None else torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
     _need(lse, torch.float32, "lse")
+    o = _attn_out(q, v, k, out_o, out_dtype)
     d = dims(B, Hq, Hkv, S, D, scale)
-    nbytes = workspace_bytes(OP_FWD_LSE, d)
+    nbytes = workspace_bytes(OP_FWD_ATTN if v is not None else OP_FWD_LSE, d)
     ws = workspace if workspace is not None else (
         torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None)
-    st = lib().kvpop_fwd_lse(ctypes.byref(d), _p(q), _p(k), _p(lse), _p(ws),
+    st = lib().kvpop_fwd_lse(ctypes.byref(d), _p(q), _p(k), _p(v), _p(lse), _p(o),
+                             1 if o is not None and o.dtype == torch.bfloat16 else 0, _p(ws),
                              0 if ws is None else ws.numel() * ws.element_size(), _stream())
     _check("kvpop_fwd_lse", st)
-    return lse
+    return lse if o is None else (lse, o)
 
 
 def running_topk(scores, n_sink, window, budget, log_decay=None, want_cutoff=True, out=None,
@@ -252,12 +274,15 @@ def decode_step_mlstm(q, k_cache, v_cache, slot_pos, slot_score, k_new, v_new, p
     return o, lse
 
 
-def fwd_lse_sparse(q, k, keep_until, budget=0, scale=0.0, out=None, workspace=None):
+def fwd_lse_sparse(q, k, keep_until, budget=0, scale=0.0, out=None, workspace=None, v=None,
+                   out_o=None, out_dtype=torch.float32):
     """Sparse causal log-normalizers LSE [B,Hq,S] fp32 over the running
     top-k mask (App. D.3, C.1): key t counts for row d while
     t <= d < keep_until[t].  ``budget`` is the budget keep_until was made
     with: each block of queries then attends over its listed keys only
-    (0: every causal key is read and tested)."""
+    (0: every causal key is read and tested).  With v, also the sparse
+    attention output O [B,Hq,S,D] (App. I), returned as (lse, o); every
+    causal key is then read and tested."""
     _need(q, torch.bfloat16, "q", 4)
     _need(k, torch.bfloat16, "k", 4)
     _need(keep_until, torch.int32, "keep_until", 3)
@@ -267,15 +292,19 @@ def fwd_lse_sparse(q, k, keep_until, budget=0, scale=0.0, out=None, workspace=No
         raise ValueError("k / keep_until shape mismatch")
     lse = out if out is not None else torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
     _need(lse, torch.float32, "lse")
+    o = _attn_out(q, v, k, out_o, out_dtype)
     d = dims(B, Hq, Hkv, S, D, scale)
-    nbytes = workspace_bytes(OP_FWD_LSE_SPARSE, d, budget)
+    nbytes = (workspace_bytes(OP_FWD_ATTN, d) if v is not None
+              else workspace_bytes(OP_FWD_LSE_SPARSE, d, budget))
     ws = workspace if workspace is not None else (
         torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None)
-    st = lib().kvpop_fwd_lse_sparse(ctypes.byref(d), _p(q), _p(k), _p(keep_until), int(budget),
-                                    _p(lse), _p(ws),
-                                    0 if ws is None else ws.numel() * ws.element_size(), _stream())
+    st = lib().kvpop_fwd_lse_sparse(ctypes.byref(d), _p(q), _p(k), _p(v), _p(keep_until),
+                                    int(budget), _p(lse), _p(o),
+                                    1 if o is not None and o.dtype == torch.bfloat16 else 0,
+                                    _p(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                    _stream())
     _check("kvpop_fwd_lse_sparse", st)
-    return lse
+    return lse if o is None else (lse, o)
 
 
 def future_attn_target(q, k, lse, window, lookahead=-1, agg="sum", count_normalize=False,

@@ -75,22 +75,42 @@ size_t kvpop_workspace_bytes(int op, const kvpop_dims* dims, int window) {
     if (window == 0) return kvpop::plan_fwd(s).partial_floats * sizeof(float);
     return kvpop::plan_fwd_sparse(s, window).workspace_bytes;
   }
+  if (op == KVPOP_OP_FWD_ATTN) return kvpop::fwd_out_workspace_bytes(s);
   return 0;
 }
 
-kvpop_status kvpop_fwd_lse(const kvpop_dims* dims, const void* q, const void* k, float* lse,
-                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+// Workspace check of the main pass: LSE-only calls need the plan's bytes
+// (none for many row blocks), calls with an attention output the V^T buffer.
+static kvpop_status check_fwd_workspace(size_t need, size_t align, const void* workspace,
+                                        size_t workspace_bytes) {
+  if (!need) return KVPOP_OK;
+  if (!workspace || !aligned(workspace, align)) return KVPOP_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < need) return KVPOP_ERR_WORKSPACE_TOO_SMALL;
+  return KVPOP_OK;
+}
+
+static kvpop_status check_fwd_output(const void* v, const void* o, kvpop_out_dtype o_dtype) {
+  if ((v == nullptr) != (o == nullptr)) return KVPOP_ERR_INVALID_ARGUMENT;
+  if (v && (!aligned(v, 16) || !aligned(o, 16))) return KVPOP_ERR_INVALID_ARGUMENT;
+  if (o_dtype != KVPOP_OUT_F32 && o_dtype != KVPOP_OUT_BF16) return KVPOP_ERR_INVALID_ARGUMENT;
+  return KVPOP_OK;
+}
+
+kvpop_status kvpop_fwd_lse(const kvpop_dims* dims, const void* q, const void* k, const void* v,
+                           float* lse, void* o, kvpop_out_dtype o_dtype, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
   AttnShape s;
   kvpop_status st = check_dims(dims, &s);
   if (st != KVPOP_OK) return st;
   if (!q || !k || !lse) return KVPOP_ERR_INVALID_ARGUMENT;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(lse, 4)) return KVPOP_ERR_INVALID_ARGUMENT;
-  const kvpop::FwdPlan p = kvpop::plan_fwd(s);
-  if (p.partial_floats) {
-    if (!workspace || !aligned(workspace, 16)) return KVPOP_ERR_INVALID_ARGUMENT;
-    if (workspace_bytes < p.partial_floats * sizeof(float)) return KVPOP_ERR_WORKSPACE_TOO_SMALL;
-  }
-  return from_hip(kvpop::launch_fwd_lse(s, q, k, nullptr, 0, lse, workspace, stream));
+  if ((st = check_fwd_output(v, o, o_dtype)) != KVPOP_OK) return st;
+  const size_t need = v ? kvpop::fwd_out_workspace_bytes(s)
+                        : kvpop::plan_fwd(s).partial_floats * sizeof(float);
+  if ((st = check_fwd_workspace(need, v ? 256 : 16, workspace, workspace_bytes)) != KVPOP_OK)
+    return st;
+  return from_hip(kvpop::launch_fwd_lse(s, q, k, nullptr, 0, lse, workspace, stream, v, o,
+                                        o_dtype == KVPOP_OUT_BF16 ? 1 : 0));
 }
 
 kvpop_status kvpop_mlstm_step(int batch, int n_kv_heads, int head_dim, int n_sink, int window,
@@ -176,22 +196,24 @@ kvpop_status kvpop_running_topk(int batch, int n_kv_heads, int seq_len, int n_si
 }
 
 kvpop_status kvpop_fwd_lse_sparse(const kvpop_dims* dims, const void* q, const void* k,
-                                  const int32_t* keep_until, int budget, float* lse,
-                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                                  const void* v, const int32_t* keep_until, int budget,
+                                  float* lse, void* o, kvpop_out_dtype o_dtype, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
   AttnShape s;
   kvpop_status st = check_dims(dims, &s);
   if (st != KVPOP_OK) return st;
   if (!q || !k || !keep_until || !lse || budget < 0) return KVPOP_ERR_INVALID_ARGUMENT;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(keep_until, 4) || !aligned(lse, 4))
     return KVPOP_ERR_INVALID_ARGUMENT;
-  const size_t need = budget > 0 ? kvpop::plan_fwd_sparse(s, budget).workspace_bytes
-                                 : kvpop::plan_fwd(s).partial_floats * sizeof(float);
-  if (need) {
-    if (!workspace || !aligned(workspace, budget > 0 ? 256 : 16)) return KVPOP_ERR_INVALID_ARGUMENT;
-    if (workspace_bytes < need) return KVPOP_ERR_WORKSPACE_TOO_SMALL;
-  }
-  return from_hip(
-      kvpop::launch_fwd_lse(s, q, k, (const int*)keep_until, budget, lse, workspace, stream));
+  if ((st = check_fwd_output(v, o, o_dtype)) != KVPOP_OK) return st;
+  const size_t need = v ? kvpop::fwd_out_workspace_bytes(s)
+                        : budget > 0 ? kvpop::plan_fwd_sparse(s, budget).workspace_bytes
+                                     : kvpop::plan_fwd(s).partial_floats * sizeof(float);
+  if ((st = check_fwd_workspace(need, (v || budget > 0) ? 256 : 16, workspace, workspace_bytes)) !=
+      KVPOP_OK)
+    return st;
+  return from_hip(kvpop::launch_fwd_lse(s, q, k, (const int*)keep_until, budget, lse, workspace,
+                                        stream, v, o, o_dtype == KVPOP_OUT_BF16 ? 1 : 0));
 }
 
 kvpop_status kvpop_future_attn_target(const kvpop_dims* dims, const void* q, const void* k,

@@ -41,6 +41,18 @@
 //       whole causal row through the same code with the list t = 0, 1, ...
 //     - Masked mode (no budget): every causal tile is read as in the dense
 //       pass and each score is tested against keep_until.
+//   * Attention output (App. D.4 first step and App. I: the main pass is the
+//     model's attention, dense or over the sparse mask): with V given, the
+//     same pass also forms O = softmax(Q K^T) V.  A first kernel stores V
+//     transposed (head-dim rows of keys) in the workspace, so each 64-key
+//     tile of V^T reaches LDS by the same DMA as K, one stage beside it.
+//     K rows are fed to the score MFMA in an order that leaves every lane
+//     holding 8 consecutive keys per 16-key slice, which is the B operand of
+//     the second MFMA (O^T[dim][query] += V^T[dim][key] P^T[key][query]),
+//     so the probabilities go from registers to the matrix core as bf16
+//     without an LDS round trip.  The two half-waves of a query column share
+//     one running maximum (one lane swap per tile), so their partial sums
+//     rescale together.  Rows are never split in this mode.
 #include <algorithm>
 #include <type_traits>
 
@@ -161,14 +173,54 @@ __global__ __launch_bounds__(256) void keylist_kernel(const int* __restrict__ ke
   if (tid == 0) hdr[blk] = fits ? make_int2(n_t, n_full / kKT) : make_int2(-1, 0);
 }
 
-template <int D, int MODE>
-__global__ __launch_bounds__(kThreads, KVPOP_FWD_MIN_BLOCKS) void fwd_lse_kernel(
+// Workgroups per CU the kernel is built for: the output mode holds a V^T
+// stage beside every K stage and 64 more accumulators per lane.
+constexpr int kOutBlocks = 2;
+
+// V [B*Hkv][S][D] -> V^T [B*Hkv][D][s_pad] (bf16, zero past S), one
+// workgroup per (b, KV head, 64-key tile); rows of V^T are 64-key aligned so
+// the output pass can DMA a tile of them like a tile of K.
+template <int D>
+__global__ __launch_bounds__(256) void transpose_v_kernel(const bf16_t* __restrict__ v,
+                                                          bf16_t* __restrict__ vt, int S,
+                                                          int s_pad) {
+  constexpr int CPR = D / 8;  // 16-byte chunks per V row
+  __shared__ uint16_t tile[kKT][D + 2];
+  const int n_t = s_pad / kKT;
+  const int bh = blockIdx.x / n_t, t0 = (blockIdx.x % n_t) * kKT;
+  const bf16_t* src = v + (size_t)bh * S * D;
+  for (int i = threadIdx.x; i < kKT * CPR; i += 256) {
+    const int r = i / CPR, ch = i % CPR;
+    const uint4 x = t0 + r < S ? ldg16(src + (size_t)(t0 + r) * D + ch * 8) : make_uint4(0, 0, 0, 0);
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      tile[r][ch * 8 + 2 * j] = (uint16_t)(w[j] & 0xffffu);
+      tile[r][ch * 8 + 2 * j + 1] = (uint16_t)(w[j] >> 16);
+    }
+  }
+  __syncthreads();
+  bf16_t* dst = vt + (size_t)bh * D * s_pad + t0;
+  for (int i = threadIdx.x; i < D * (kKT / 8); i += 256) {
+    const int d = i / (kKT / 8), kc = i % (kKT / 8);
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = (uint32_t)tile[kc * 8 + 2 * j][d] | ((uint32_t)tile[kc * 8 + 2 * j + 1][d] << 16);
+    stg16(dst + (size_t)d * s_pad + kc * 8, make_uint4(w[0], w[1], w[2], w[3]));
+  }
+}
+
+template <int D, int MODE, bool OUT>
+__global__ __launch_bounds__(kThreads, OUT ? kOutBlocks : KVPOP_FWD_MIN_BLOCKS) void fwd_lse_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const int* __restrict__ keep_until,
     const int2* __restrict__ hdr, const int* __restrict__ lists, int cap, float* __restrict__ lse,
     float2* __restrict__ part, int B, int Hq, int Hkv, int S, float c, float scale, int n_pb,
-    int kmax, int n_pieces, int n_items, int snake_cus) {
+    int kmax, int n_pieces, int n_items, int snake_cus, const bf16_t* __restrict__ vt, int s_pad,
+    void* __restrict__ o_out, int o_bf16) {
   constexpr bool SPARSE = MODE != kDense;
   static_assert(MODE != kListed || kStages == 2, "the listed mode pairs list slots with stages");
+  static_assert(!OUT || (MODE != kListed && kStages == 2), "the output mode: dense or masked, two stages");
   constexpr int NS = D / 16;           // MFMA k-slices
   constexpr int CPR = D / 8;           // 16-byte chunks per row
   constexpr int ROWB = D * 2;          // bytes per K row
@@ -198,7 +250,16 @@ __global__ __launch_bounds__(kThreads, KVPOP_FWD_MIN_BLOCKS) void fwd_lse_kernel
     constexpr int j = decltype(J)::value;
     return j == 0 ? lt0 : lt1;
   };
-  constexpr int DPS = LPW + (SPARSE ? 1 : 0) + (MODE == kListed ? 1 : 0);  // DMAs per wave per stage
+  // output mode: each stage's 64-key tile of V^T (D rows of 128 bytes, the
+  // 16-byte chunks of row d XOR-swizzled by d & 7)
+  __shared__ __attribute__((aligned(1024))) uint8_t vs0[OUT ? TILE : 16], vs1[OUT ? TILE : 16];
+  auto vst = [&](auto J) -> uint8_t* {
+    constexpr int j = decltype(J)::value;
+    return j == 0 ? vs0 : vs1;
+  };
+  constexpr int VPW = OUT ? D * kKT * 2 / 1024 / (kThreads / 64) : 0;  // V^T DMAs per wave
+  // DMAs per wave per stage
+  constexpr int DPS = LPW + (SPARSE ? 1 : 0) + (MODE == kListed ? 1 : 0) + VPW;
 
   const int G = Hq / Hkv;
   const int P = 128 / G;
@@ -258,6 +319,7 @@ __global__ __launch_bounds__(kThreads, KVPOP_FWD_MIN_BLOCKS) void fwd_lse_kernel
   const int g = h * G + gl;
 
   const bf16_t* kbase = k + ((size_t)b * Hkv + h) * (size_t)S * D;
+  const bf16_t* vtbase = OUT ? vt + ((size_t)b * Hkv + h) * (size_t)D * s_pad : nullptr;
   const int* kuntil = SPARSE ? keep_until + ((size_t)b * Hkv + h) * (size_t)S : nullptr;
   auto issue = [&](auto J, int kt) {
     uint8_t* dst = kst(J);
@@ -272,6 +334,16 @@ __global__ __launch_bounds__(kThreads, KVPOP_FWD_MIN_BLOCKS) void fwd_lse_kernel
     }
     if constexpr (SPARSE)
       dma4(kuntil + min(kt * kKT + lane, S - 1), ust(J) + wave * 64);
+    if constexpr (OUT) {
+      uint8_t* vdst = vst(J);
+#pragma unroll
+      for (int j = 0; j < VPW; ++j) {
+        const int I = wave * VPW + j;       // V^T rows 8 I .. 8 I + 7
+        const int row = I * 8 + (lane >> 3);
+        const int lc = (lane & 7) ^ (row & 7);
+        dma16(vtbase + (size_t)row * s_pad + kt * kKT + lc * 8, vdst + I * 1024);
+      }
+    }
   };
   // listed mode: K rows and keep_until values of the tile whose list is in
   // slot J, gathered into stage J
@@ -323,13 +395,39 @@ __global__ __launch_bounds__(kThreads, KVPOP_FWD_MIN_BLOCKS) void fwd_lse_kernel
   }
 
   float m = -INFINITY, l = 0.f;
-  const int sw = col & (CPR - 1);
+  // A-fragment row of this lane within a 32-key sub-tile.  The output mode
+  // swaps bits 2 and 3 of the row, so that result register r of half h holds
+  // key 16 (r / 8) + 8 h + r % 8 (eight consecutive keys per 16-key slice,
+  // the B operand layout of the P.V product) instead of 8 (r / 4) + 4 h + r % 4.
+  const int krow = OUT ? ((col & 19) | ((col & 4) << 1) | ((col & 8) >> 1)) : col;
+  const int sw = krow & (CPR - 1);
   // byte offset of this lane's A fragment of k-slice s within a 32-key
   // sub-tile: loop-invariant, so each read is one ds_read whose immediate
   // offset holds the stage and sub-tile base
   uint32_t foff[NS];
 #pragma unroll
-  for (int s2 = 0; s2 < NS; ++s2) foff[s2] = col * ROWB + (((2 * s2 + half) ^ sw) << 4);
+  for (int s2 = 0; s2 < NS; ++s2) foff[s2] = krow * ROWB + (((2 * s2 + half) ^ sw) << 4);
+  // key offset (within the 64-key tile) of result registers 4 r4 .. 4 r4 + 3
+  // of sub-tile sub: four consecutive keys either way
+  auto kb4 = [&](int sub, int r4) {
+    return OUT ? 32 * sub + 16 * (r4 >> 1) + 8 * half + 4 * (r4 & 1) : 32 * sub + 8 * r4 + 4 * half;
+  };
+  // output mode: O^T accumulators (dims 32 db + 8 (r/4) + 4 h + r%4 of this
+  // lane's query column) and the byte offsets of the V^T A fragments: rows
+  // 32 db + col, keys 32 sub + 16 j + 8 h .. + 7 (chunk 4 sub + 2 j + h)
+  constexpr int NDB = OUT ? D / 32 : 1;
+  f32x16 oacc[NDB];
+  uint32_t voff[2][2];
+  if constexpr (OUT) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) voff[sub][j] = col * 128 + (((4 * sub + 2 * j + half) ^ (col & 7)) << 4);
+  }
   auto step = [&](auto J, int i) {
     constexpr int j = decltype(J)::value;
     constexpr int jn = (j + kStages - 1) % kStages;
@@ -382,11 +480,11 @@ __global__ __launch_bounds__(kThreads, KVPOP_FWD_MIN_BLOCKS) void fwd_lse_kernel
         for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
-            const int4 u = *reinterpret_cast<const int4*>(ut + sub * 32 + 8 * r4 + 4 * half);
+            const int4 u = *reinterpret_cast<const int4*>(ut + kb4(sub, r4));
             const int uu[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const int t = t0 + sub * 32 + 8 * r4 + 4 * half + e;
+              const int t = t0 + kb4(sub, r4) + e;
               acc[sub][4 * r4 + e] =
                   ((t > dpos) | (t >= k_end) | (dpos >= uu[e])) ? -INFINITY : acc[sub][4 * r4 + e];
             }
@@ -396,7 +494,7 @@ __global__ __launch_bounds__(kThreads, KVPOP_FWD_MIN_BLOCKS) void fwd_lse_kernel
         for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
-            const int4 u = *reinterpret_cast<const int4*>(ut + sub * 32 + 8 * r4 + 4 * half);
+            const int4 u = *reinterpret_cast<const int4*>(ut + kb4(sub, r4));
             acc[sub][4 * r4 + 0] = dpos >= u.x ? -INFINITY : acc[sub][4 * r4 + 0];
             acc[sub][4 * r4 + 1] = dpos >= u.y ? -INFINITY : acc[sub][4 * r4 + 1];
             acc[sub][4 * r4 + 2] = dpos >= u.z ? -INFINITY : acc[sub][4 * r4 + 2];
@@ -408,24 +506,63 @@ __global__ __launch_bounds__(kThreads, KVPOP_FWD_MIN_BLOCKS) void fwd_lse_kernel
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int t = t0 + sub * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          const int t = t0 + kb4(sub, r >> 2) + (r & 3);
           acc[sub][r] = ((t > dpos) | (t >= k_end)) ? -INFINITY : acc[sub][r];
         }
     }
-    float mx = m;
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[sub][r]);
-    if (mx > -INFINITY) {
-      const float mc = mx * c;
-      float ts = 0.f;
+    if constexpr (OUT) {
+      // one running maximum per query column, shared by its two half-waves
+      float mx = -INFINITY;
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) ts += fast_exp2(fmaf(acc[sub][r], c, -mc));
-      l = l * fast_exp2(fmaf(m, c, -mc)) + ts;
-      m = mx;
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[sub][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mn = fmaxf(m, mx);
+      const float mc = mn > -INFINITY ? mn * c : 0.f;  // masked scores still give 0
+      const float alpha = fast_exp2(fmaf(m, c, -mc));   // 0 while nothing was kept
+      float ts = 0.f;
+      bf16x8 pb[2][2];
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(fmaf(acc[sub][r], c, -mc));
+          ts += p;
+          pb[sub][r >> 3][r & 7] = (__bf16)p;
+        }
+      l = l * alpha + ts;
+      m = mn;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      const uint8_t* vtile = vst(J);
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+            oacc[db] = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(vtile + db * 32 * 128 +
+                                                                         voff[sub][j])),
+                              pb[sub][j], oacc[db]);
+    } else {
+      float mx = m;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[sub][r]);
+      if (mx > -INFINITY) {
+        const float mc = mx * c;
+        float ts = 0.f;
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) ts += fast_exp2(fmaf(acc[sub][r], c, -mc));
+        l = l * fast_exp2(fmaf(m, c, -mc)) + ts;
+        m = mx;
+      }
     }
   };
   for (int i = 0; i < n_kt; i += kStages) {
@@ -435,6 +572,33 @@ __global__ __launch_bounds__(kThreads, KVPOP_FWD_MIN_BLOCKS) void fwd_lse_kernel
     if (kStages > 3 && i + 3 < n_kt) step(I3{}, i + 3);
   }
 
+  if constexpr (OUT) {
+    // both half-waves share m: their sums add; O = oacc / sum
+    const float lt = l + __shfl_xor(l, 32);
+    if (valid) {
+      const size_t row = ((size_t)b * Hq + g) * S + dpos;
+      if (half == 0) lse[row] = lt > 0.f ? m * scale + logf(lt) : -INFINITY;
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int dim = 32 * db + 8 * r4 + 4 * half;
+          const float o0 = oacc[db][4 * r4] * inv, o1 = oacc[db][4 * r4 + 1] * inv;
+          const float o2 = oacc[db][4 * r4 + 2] * inv, o3 = oacc[db][4 * r4 + 3] * inv;
+          if (o_bf16) {
+            uint2 w;
+            w.x = (uint32_t)f32_to_bf16_rne(o0) | ((uint32_t)f32_to_bf16_rne(o1) << 16);
+            w.y = (uint32_t)f32_to_bf16_rne(o2) | ((uint32_t)f32_to_bf16_rne(o3) << 16);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(o_out) + row * D + dim) = w;
+          } else {
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(o_out) + row * D + dim) =
+                make_float4(o0, o1, o2, o3);
+          }
+        }
+    }
+    return;
+  }
   // merge the two half-waves that share a query column
   const float mo = __shfl_xor(m, 32);
   const float lo = __shfl_xor(l, 32);
@@ -504,19 +668,41 @@ SparsePlan plan_fwd_sparse(const AttnShape& s, int budget) {
   return sp;
 }
 
+size_t fwd_out_workspace_bytes(const AttnShape& s) {
+  const size_t s_pad = (size_t)(s.S + kKT - 1) / kKT * kKT;
+  return (size_t)s.B * s.Hkv * s.D * s_pad * sizeof(bf16_t);
+}
+
 hipError_t launch_fwd_lse(const AttnShape& s, const void* q, const void* k, const int* keep_until,
-                          int budget, float* lse, void* workspace, hipStream_t st) {
-  const bool listed = keep_until && budget > 0;
+                          int budget, float* lse, void* workspace, hipStream_t st, const void* v,
+                          void* o, int o_bf16) {
+  const bool out = v != nullptr;
+  const bool listed = keep_until && budget > 0 && !out;
   FwdPlan p = plan_fwd(s);
-  if (listed) {  // whole rows: a listed block walks about budget + P keys
+  if (listed || out) {  // whole rows: a listed block walks about budget + P keys
     p.kmax = (s.S + kKT - 1) / kKT * kKT;
     p.n_pieces = 1;
   }
   const int n_items = s.B * s.Hkv * p.n_pb * p.n_pieces;
   const float c = s.scale * kLog2e;
-  // one resident round (four workgroups per CU): deal each XCD's blocks in a snake
+  // one resident round: deal each XCD's blocks in a snake
   const int cus = device_cu_count();
-  const int snake_cus = n_items <= cus * KVPOP_FWD_MIN_BLOCKS && cus % 8 == 0 ? cus / 8 : 0;
+  const int per_cu = out ? kOutBlocks : KVPOP_FWD_MIN_BLOCKS;
+  const int snake_cus = n_items <= cus * per_cu && cus % 8 == 0 ? cus / 8 : 0;
+  const int s_pad = (s.S + kKT - 1) / kKT * kKT;
+  bf16_t* vt = nullptr;
+  if (out) {  // V^T into the workspace
+    vt = reinterpret_cast<bf16_t*>(workspace);
+    const unsigned n_blk = (unsigned)(s.B * s.Hkv * (s_pad / kKT));
+    if (s.D == 128)
+      hipLaunchKernelGGL(transpose_v_kernel<128>, dim3(n_blk), dim3(256), 0, st, (const bf16_t*)v, vt,
+                         s.S, s_pad);
+    else
+      hipLaunchKernelGGL(transpose_v_kernel<64>, dim3(n_blk), dim3(256), 0, st, (const bf16_t*)v, vt,
+                         s.S, s_pad);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   dim3 grid(n_items), block(kThreads);
   float2* part = reinterpret_cast<float2*>(workspace);
   const int2* hdr = nullptr;
@@ -537,16 +723,21 @@ hipError_t launch_fwd_lse(const AttnShape& s, const void* q, const void* k, cons
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, block, 0, st, (const bf16_t*)q, (const bf16_t*)k, keep_until,
                        hdr, lists, cap, lse, part, s.B, s.Hq, s.Hkv, s.S, c, s.scale, p.n_pb,
-                       p.kmax, p.n_pieces, n_items, snake_cus);
+                       p.kmax, p.n_pieces, n_items, snake_cus, (const bf16_t*)vt, s_pad, o,
+                       o_bf16);
   };
   if (s.D == 128) {
-    if (listed) go(fwd_lse_kernel<128, kListed>);
-    else if (keep_until) go(fwd_lse_kernel<128, kMasked>);
-    else go(fwd_lse_kernel<128, kDense>);
+    if (out && keep_until) go(fwd_lse_kernel<128, kMasked, true>);
+    else if (out) go(fwd_lse_kernel<128, kDense, true>);
+    else if (listed) go(fwd_lse_kernel<128, kListed, false>);
+    else if (keep_until) go(fwd_lse_kernel<128, kMasked, false>);
+    else go(fwd_lse_kernel<128, kDense, false>);
   } else {
-    if (listed) go(fwd_lse_kernel<64, kListed>);
-    else if (keep_until) go(fwd_lse_kernel<64, kMasked>);
-    else go(fwd_lse_kernel<64, kDense>);
+    if (out && keep_until) go(fwd_lse_kernel<64, kMasked, true>);
+    else if (out) go(fwd_lse_kernel<64, kDense, true>);
+    else if (listed) go(fwd_lse_kernel<64, kListed, false>);
+    else if (keep_until) go(fwd_lse_kernel<64, kMasked, false>);
+    else go(fwd_lse_kernel<64, kDense, false>);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_pieces == 1) return e;

@@ -35,9 +35,14 @@ SparsePlan plan_fwd_sparse(const AttnShape& s, int budget);
 // keep_until: nullable [B][Hkv][S]; when given, key t counts for row d only
 // while t <= d < keep_until[t] (the sparse normalizer).  budget > 0 selects
 // the listed pass (workspace from plan_fwd_sparse), else every causal key
-// is tested (workspace from plan_fwd).
+// is tested (workspace from plan_fwd).  With v (and o) the pass also writes
+// the attention output; every causal key is then read (tested against
+// keep_until when given) and the workspace holds V^T
+// (fwd_out_workspace_bytes).
+size_t fwd_out_workspace_bytes(const AttnShape& s);
 hipError_t launch_fwd_lse(const AttnShape& s, const void* q, const void* k, const int* keep_until,
-                          int budget, float* lse, void* workspace, hipStream_t st);
+                          int budget, float* lse, void* workspace, hipStream_t st,
+                          const void* v = nullptr, void* o = nullptr, int o_bf16 = 0);
 
 // ---- delayed stateful mLSTM scorer (one decoding step) ----
 constexpr int kMlstmFeat = 32;   // projected features per Hedgehog half

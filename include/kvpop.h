@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define KVPOP_ABI_VERSION 2
+#define KVPOP_ABI_VERSION 3
 
 typedef enum {
     KVPOP_OK = 0,
@@ -70,25 +70,39 @@ typedef struct {
 #define KVPOP_OP_DECODE 1
 #define KVPOP_OP_FWD_LSE 2
 #define KVPOP_OP_FWD_LSE_SPARSE 3 /* third argument: the budget */
+#define KVPOP_OP_FWD_ATTN 4       /* kvpop_fwd_lse / _sparse with v and o */
 
 int kvpop_abi_version(void);
 const char* kvpop_status_string(kvpop_status s);
 
 /*
- * kvpop_fwd_lse -- main causal pass, log-normalizers only.
+ * kvpop_fwd_lse -- main causal attention pass: per-query log-normalizers,
+ * and optionally the attention output.
  * App. D.1 (dense target identity) and D.4, first step: the main attention
- * pass yields one log-normalizer per query.
+ * pass yields one log-normalizer per query, which the target reuses; the
+ * pass itself is the model's causal attention.
  *   LSE[b][g][d] = log sum_{t <= d} exp(scale * Q[b][g][d] . K[b][g/G][t])
+ *   O[b][g][d]   = sum_{t <= d} exp(scale * Q[b][g][d] . K[b][g/G][t] - LSE[b][g][d]) V[b][g/G][t]
  * (the diagonal t = d is included, so no row is empty).  No S x S matrix is
- * formed.  q, k: bf16 as laid out above; lse: fp32 [B][Hq][S], written in
- * full.  Accumulation is fp32.
- *   workspace: kvpop_workspace_bytes(KVPOP_OP_FWD_LSE, dims, 0) bytes (zero
- *   for shapes with many row blocks; then it may be NULL), 16-byte aligned,
- *   no initialisation needed.  It holds partial (max, sum) pairs when long
- *   causal rows are split to balance the launch.
+ * formed.  q, k, v: bf16 as laid out above; lse: fp32 [B][Hq][S], written
+ * in full.  Accumulation is fp32; the probabilities enter the product with V
+ * rounded to bf16.
+ *   v, o:      nullable together (NULL: log-normalizers only).  o is
+ *              [B][Hq][S][D], fp32 or bf16 (round to nearest even) per
+ *              o_dtype, 16-byte aligned, written in full.
+ *   workspace: kvpop_workspace_bytes(KVPOP_OP_FWD_LSE, dims, 0) bytes without
+ *              v (zero for shapes with many row blocks; then it may be NULL;
+ *              16-byte aligned; partial (max, sum) pairs when long causal rows
+ *              are split to balance the launch), or
+ *              kvpop_workspace_bytes(KVPOP_OP_FWD_ATTN, dims, 0) bytes with v
+ *              (256-byte aligned; V transposed, 64-key padded).  No
+ *              initialisation needed.
+ * Errors: INVALID_ARGUMENT for NULL q, k or lse, v without o (or the
+ * reverse), misaligned pointers, a bad o_dtype; WORKSPACE_TOO_SMALL.
  */
-kvpop_status kvpop_fwd_lse(const kvpop_dims* dims, const void* q, const void* k, float* lse,
-                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+kvpop_status kvpop_fwd_lse(const kvpop_dims* dims, const void* q, const void* k, const void* v,
+                           float* lse, void* o, kvpop_out_dtype o_dtype, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
 
 /*
  * kvpop_running_topk -- running top-k retention mask and its cutoffs.
@@ -121,32 +135,40 @@ kvpop_status kvpop_running_topk(int batch, int n_kv_heads, int seq_len, int n_si
                                 int32_t* keep_until, int32_t* cutoff, hipStream_t stream);
 
 /*
- * kvpop_fwd_lse_sparse -- main causal pass with the sparse normalizer.
+ * kvpop_fwd_lse_sparse -- main causal pass with the sparse normalizer (and
+ * optionally the sparse attention output).
  * App. D.3: the target may reuse the log-normalizer of the fixed-budget
- * sparse attention instead of the dense one; App. C.1 gives its mask:
- *   LSE[b][g][d] = log sum_{t <= d, d < keep_until[b][h][t]} exp(scale * q_d . k_t)
+ * sparse attention instead of the dense one; App. C.1 gives its mask; App. I
+ * has that sparse (student) attention supply both output and normalizers:
+ *   R_d          = { t <= d : d < keep_until[b][h][t] }
+ *   LSE[b][g][d] = log sum_{t in R_d} exp(scale * q_d . k_t)
+ *   O[b][g][d]   = sum_{t in R_d} exp(scale * q_d . k_t - LSE[b][g][d]) v_t
  * with keep_until from kvpop_running_topk (h = g / G); keep_until is int32
- * [B][Hkv][S], 4-byte aligned; q, k and lse as for kvpop_fwd_lse.
- *   budget:    the budget keep_until was made with (> 0), or 0.  With a
- *              budget the pass first lists, for every block of P = 128/G
- *              query positions, the keys still retained at its first query
- *              (at most budget + P for a running top-k mask) and attends
- *              over those only; a block whose list would exceed that bound
- *              (keep_until made otherwise) walks its whole causal row, so
- *              the result is the same for any keep_until.  With 0 every
- *              causal key is read and tested.
- *   workspace: kvpop_workspace_bytes(KVPOP_OP_FWD_LSE_SPARSE, dims, budget)
- *              bytes, 256-byte aligned with a budget (16 without), no
- *              initialisation needed; it may be NULL when that is zero.
- * A row whose retained set is empty gets -inf (the mask of
- * kvpop_running_topk always keeps token d itself when w >= 1).  The result
+ * [B][Hkv][S], 4-byte aligned; q, k, v, lse, o and o_dtype as for
+ * kvpop_fwd_lse.
+ *   budget:    the budget keep_until was made with (> 0), or 0.  Without v
+ *              and with a budget the pass first lists, for every block of
+ *              P = 128/G query positions, the keys still retained at its
+ *              first query (at most budget + P for a running top-k mask) and
+ *              attends over those only; a block whose list would exceed that
+ *              bound (keep_until made otherwise) walks its whole causal row,
+ *              so the result is the same for any keep_until.  With 0, or
+ *              with v, every causal key is read and tested.
+ *   workspace: with v: kvpop_workspace_bytes(KVPOP_OP_FWD_ATTN, dims, 0)
+ *              bytes; without: kvpop_workspace_bytes(KVPOP_OP_FWD_LSE_SPARSE,
+ *              dims, budget) bytes; 256-byte aligned with v or a budget (16
+ *              otherwise), no initialisation needed; it may be NULL when the
+ *              size is zero.
+ * A row whose retained set is empty gets LSE = -inf and O = 0 (the mask of
+ * kvpop_running_topk always keeps token d itself when w >= 1).  The LSE
  * feeds kvpop_future_attn_target unchanged.
  * Errors: as kvpop_fwd_lse; INVALID_ARGUMENT for a NULL keep_until or a
  * negative budget.
  */
 kvpop_status kvpop_fwd_lse_sparse(const kvpop_dims* dims, const void* q, const void* k,
-                                  const int32_t* keep_until, int budget, float* lse,
-                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+                                  const void* v, const int32_t* keep_until, int budget,
+                                  float* lse, void* o, kvpop_out_dtype o_dtype, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
 
 /*
  * kvpop_future_attn_target -- transposed future-attention pass.

@@ -35,16 +35,16 @@ def test_exports_match_header(lib):
     assert names == set(kv.EXPORTS), names ^ set(kv.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.kvpop_abi_version() == 2
+    assert lib.kvpop_abi_version() == 3
     for s in range(5):
         assert lib.kvpop_status_string(s)
 
 
 def test_dims_validation(lib):
     def fwd(d):
-        return lib.kvpop_fwd_lse(ctypes.byref(d), GOOD, GOOD, GOOD, None, 0, None)
+        return lib.kvpop_fwd_lse(ctypes.byref(d), GOOD, GOOD, None, GOOD, None, 0, None, 0, None)
 
-    assert lib.kvpop_fwd_lse(None, GOOD, GOOD, GOOD, None, 0, None) == 1
+    assert lib.kvpop_fwd_lse(None, GOOD, GOOD, None, GOOD, None, 0, None, 0, None) == 1
     assert fwd(kv.dims(0, 32, 8, 4096, 128)) == 1
     assert fwd(kv.dims(1, 32, 8, 0, 128)) == 1
     assert fwd(kv.dims(1, 30, 8, 4096, 128)) == 1   # Hq % Hkv
@@ -54,12 +54,31 @@ def test_dims_validation(lib):
     d = kv.dims(1, 2, 1, 4096, 128)
     need = kv.workspace_bytes(kv.OP_FWD_LSE, d)
     assert need > 0  # few row blocks: long causal rows are split
-    assert lib.kvpop_fwd_lse(ctypes.byref(d), None, GOOD, GOOD, GOOD, need, None) == 1
-    assert lib.kvpop_fwd_lse(ctypes.byref(d), P(0x10008), GOOD, GOOD, GOOD, need, None) == 1  # misaligned
-    assert lib.kvpop_fwd_lse(ctypes.byref(d), GOOD, GOOD, GOOD, None, need, None) == 1
-    assert lib.kvpop_fwd_lse(ctypes.byref(d), GOOD, GOOD, GOOD, GOOD, need - 8, None) == 3
+    assert lib.kvpop_fwd_lse(ctypes.byref(d), None, GOOD, None, GOOD, None, 0, GOOD, need, None) == 1
+    assert lib.kvpop_fwd_lse(ctypes.byref(d), P(0x10008), GOOD, None, GOOD, None, 0, GOOD, need, None) == 1  # misaligned
+    assert lib.kvpop_fwd_lse(ctypes.byref(d), GOOD, GOOD, None, GOOD, None, 0, None, need, None) == 1
+    assert lib.kvpop_fwd_lse(ctypes.byref(d), GOOD, GOOD, None, GOOD, None, 0, GOOD, need - 8, None) == 3
     for big in (kv.dims(1, 32, 8, 32768, 128), kv.dims(1, 32, 8, 4096, 128)):
         assert kv.workspace_bytes(kv.OP_FWD_LSE, big) == 0  # enough row blocks: no split
+    # the attention output: v and o together, 16-byte aligned, a valid type,
+    # and room for V^T (64-key padded rows)
+    d = kv.dims(1, 32, 8, 100, 128)
+    need = kv.workspace_bytes(kv.OP_FWD_ATTN, d)
+    assert need == 1 * 8 * 128 * 128 * 2
+
+    def att(v=GOOD, o=GOOD, o_dtype=0, ws=GOOD, nbytes=need):
+        return lib.kvpop_fwd_lse(ctypes.byref(d), GOOD, GOOD, v, GOOD, o, o_dtype, ws, nbytes, None)
+
+    assert att(v=None) == 1
+    assert att(o=None) == 1
+    assert att(o_dtype=2) == 1
+    assert att(o=P(0x10008)) == 1
+    assert att(ws=None) == 1
+    assert att(ws=P(0x10010)) == 1  # V^T workspace: 256-byte aligned
+    assert att(nbytes=need - 1) == 3
+    sp = lib.kvpop_fwd_lse_sparse
+    assert sp(ctypes.byref(d), GOOD, GOOD, GOOD, GOOD, 64, GOOD, None, 0, GOOD, need, None) == 1
+    assert sp(ctypes.byref(d), GOOD, GOOD, GOOD, GOOD, 64, GOOD, GOOD, 0, GOOD, need - 1, None) == 3
 
 
 def test_target_validation(lib):
@@ -191,25 +210,25 @@ def test_running_topk_and_sparse_lse_validation(lib):
     assert rt(1, 8, 65537, 4, 128, 1024, GOOD, None, GOOD, None, None) == 2     # longest row 65536
     sp = lib.kvpop_fwd_lse_sparse
     d = kv.dims(1, 32, 8, 4096, 128)
-    assert sp(ctypes.byref(d), GOOD, GOOD, None, 0, GOOD, None, 0, None) == 1     # no mask
-    assert sp(ctypes.byref(d), GOOD, GOOD, P(0x10002), 0, GOOD, None, 0, None) == 1
-    assert sp(ctypes.byref(d), GOOD, GOOD, GOOD, -1, GOOD, None, 0, None) == 1    # budget < 0
-    assert sp(None, GOOD, GOOD, GOOD, 0, GOOD, None, 0, None) == 1
+    assert sp(ctypes.byref(d), GOOD, GOOD, None, None, 0, GOOD, None, 0, None, 0, None) == 1     # no mask
+    assert sp(ctypes.byref(d), GOOD, GOOD, None, P(0x10002), 0, GOOD, None, 0, None, 0, None) == 1
+    assert sp(ctypes.byref(d), GOOD, GOOD, None, GOOD, -1, GOOD, None, 0, None, 0, None) == 1    # budget < 0
+    assert sp(None, GOOD, GOOD, None, GOOD, 0, GOOD, None, 0, None, 0, None) == 1
     d = kv.dims(1, 32, 8, 4096, 96)
-    assert sp(ctypes.byref(d), GOOD, GOOD, GOOD, 0, GOOD, None, 0, None) == 2      # D = 96
+    assert sp(ctypes.byref(d), GOOD, GOOD, None, GOOD, 0, GOOD, None, 0, None, 0, None) == 2      # D = 96
     d = kv.dims(1, 32, 8, 4096, 128)
     need = lib.kvpop_workspace_bytes(3, ctypes.byref(d), 0)
     assert need == lib.kvpop_workspace_bytes(2, ctypes.byref(d), 0)
     if need:
-        assert sp(ctypes.byref(d), GOOD, GOOD, GOOD, 0, GOOD, GOOD, need - 16, None) == 3
+        assert sp(ctypes.byref(d), GOOD, GOOD, None, GOOD, 0, GOOD, None, 0, GOOD, need - 16, None) == 3
     # with a budget: a header per block of 32 queries (8 heads x 128 blocks),
     # then 1024 + 32 listed keys per block
     need = lib.kvpop_workspace_bytes(3, ctypes.byref(d), 1024)
     assert need == 8 * 128 * 8 + 8 * 128 * 1088 * 4
     assert lib.kvpop_workspace_bytes(3, ctypes.byref(d), -1) == 0
-    assert sp(ctypes.byref(d), GOOD, GOOD, GOOD, 1024, GOOD, None, 0, None) == 1   # no workspace
-    assert sp(ctypes.byref(d), GOOD, GOOD, GOOD, 1024, GOOD, P(0x10010), need, None) == 1  # 256 B
-    assert sp(ctypes.byref(d), GOOD, GOOD, GOOD, 1024, GOOD, GOOD, need - 1, None) == 3
+    assert sp(ctypes.byref(d), GOOD, GOOD, None, GOOD, 1024, GOOD, None, 0, None, 0, None) == 1   # no workspace
+    assert sp(ctypes.byref(d), GOOD, GOOD, None, GOOD, 1024, GOOD, None, 0, P(0x10010), need, None) == 1  # 256 B
+    assert sp(ctypes.byref(d), GOOD, GOOD, None, GOOD, 1024, GOOD, None, 0, GOOD, need - 1, None) == 3
 
 
 def test_mlstm_step_validation(lib):

@@ -281,7 +281,7 @@ def test_sparse_abi_errors(kv):
     assert L.kvpop_running_topk(1, 1, 64, 4, 16, 30, None, None, pu, None, None) == 1
     assert L.kvpop_running_topk(0, 1, 64, 4, 16, 30, p, None, pu, None, None) == 1
     d = kv.dims(1, 2, 1, 64, 96)
-    assert L.kvpop_fwd_lse_sparse(ctypes.byref(d), p, p, pu, 0, p, None, 0, None) == 2  # D = 96
+    assert L.kvpop_fwd_lse_sparse(ctypes.byref(d), p, p, None, pu, 0, p, None, 0, None, 0, None) == 2  # D = 96
     d = kv.dims(1, 2, 1, 64, 64)
-    assert L.kvpop_fwd_lse_sparse(ctypes.byref(d), p, p, None, 0, p, None, 0, None) == 1
-    assert L.kvpop_fwd_lse_sparse(ctypes.byref(d), p, p, pu, 16, p, None, 0, None) == 1  # no workspace
+    assert L.kvpop_fwd_lse_sparse(ctypes.byref(d), p, p, None, None, 0, p, None, 0, None, 0, None) == 1
+    assert L.kvpop_fwd_lse_sparse(ctypes.byref(d), p, p, None, pu, 16, p, None, 0, None, 0, None) == 1  # no workspace
