@@ -1,20 +1,23 @@
 """Benchmark of the KVpop hot path on one MI355X.
 
-Timed step (the metric's first half): one pass of the whole hot path over the
-Qwen3-4B-shaped layer (B=1, 32 query / 8 KV heads, D=128, S=4096, RoPE,
-w=128, s=4, budget 1024): causal LSE pass -> transposed future-attention
-target (SUM over the group) -> retention + compaction of K/V -> one
-bounded-cache decode step (delayed MLP scoring) -> decode attention.
-value = KV-head keys scored per second = B*Hkv*S / step time.
+Timed step (the headline): one pass of the whole hot path over the
+Qwen3-8B-shaped 36-layer prefill (B=1, 32 query / 8 KV heads, D=128,
+S=32768, RoPE, w=256, s=4, budget 8192 per KV head), on every layer's own
+resident inputs: causal LSE pass -> transposed future-attention target (SUM
+over the group) -> retention + compaction of K/V to the budget -> one
+bounded-cache decode step over the fresh cache (delayed MLP scoring, then
+decode attention).  value = 36 * B * Hkv * S KV-head keys scored per second
+of step time.  roofline: the transposed pass (kvpop_future_attn_target),
+the dominant call, against the dense bf16 MFMA peak.
 
-Also reported: the bounded-cache decode workload (64 sequences, 36 layers,
-budget 4096 per KV head, 512 steps: per layer and step one cache step with
-the delayed MLP scorer and one GQA decode attention; the same steps through
-the single-call kvpop_decode_step are reported beside it) in steps/s with its
-HBM roofline, the roofline of the dominant kernel, and the CPU oracle timed
-on a bounded sample.
+Also reported, each under its own key: the same step on the Qwen3-4B layer,
+the target variants, retention and the sparse normalizer on that layer, the
+skewed 16k batch, the attention-output mode of the main pass, the sparse
+normalizer on one 32k layer, the bounded-cache decode workload (64
+sequences, 36 layers, budget 4096, 512 steps; steps/s with its HBM
+roofline) and the CPU oracle timed on bounded samples.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]   (defaults: K=20, W=50)
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]   (defaults: K=5, W=2)
 """
 import argparse
 import json
@@ -35,14 +38,13 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 FP32_VECTOR_PEAK_TFS = 157.3     # MI355X fp32 vector (counts packed FMA; one FMA per lane per cycle is half)
 
 # HBM bytes of one kvpop_future_attn_target call (transposed pass + merge) on
-# the Qwen3-4B layer workload, from two rocprofv3 --pmc runs (FETCH_SIZE, then
-# WRITE_SIZE, KiB per dispatch) each scaled by what the same counter reads for
-# a torch copy of known size (`bench.py --calibrate-copy`).  Valid only for
-# the kernel code it was taken on (sources_digest): bench reports null once
-# that changes.
+# one layer of the 36-layer prefill, from two rocprofv3 --pmc runs (FETCH_SIZE,
+# then WRITE_SIZE, KiB per dispatch) each scaled by what the same counter
+# reads for a torch copy of known size (`bench.py --calibrate-copy`).  Valid
+# only for the kernel code it was taken on (sources_digest): bench reports
+# null once that changes.
 TRAFFIC_SOURCES = ("future_target.hip", "common.h", "launch.h")
-TRAFFIC = {"sha256": "2680e749021cdc622038ebce49365a3827392d31c3e2d79cfdcd018d50410731",
-           "fetch_bytes": 2 * (23013.5 + 325.0) * 1024, "write_bytes": (577.6 + 128.0) * 1024}
+TRAFFIC = None
 METRIC = "future-attn target keys/s + MFMA util; bounded-cache decode steps/s + HBM util"
 
 
@@ -151,6 +153,110 @@ def bench_target(kv, steps, warmup):
     return st, ms, t_tr, brk, f_fwd, f_tr
 
 
+class PrefillStep:
+    """Buffers and one step of the hot path over every layer of a
+    multi-layer prefill workload (the layers' inputs resident in HBM)."""
+
+    def __init__(self, kv, w, seed_base=4000, hidden=64, delay=16):
+        dev = torch.device("cuda")
+        self.kv, self.w, self.delay = kv, w, delay
+        log(f"{w.name}: generating {w.layers} layers of inputs")
+        self.ins = [synth.attention_inputs(w, seed=seed_base + l, device=dev) for l in range(w.layers)]
+        d = kv.dims(w.B, w.Hq, w.Hkv, w.S, w.D)
+        self.lse = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device=dev)
+        self.mass = torch.empty((w.B, w.Hkv, w.S), dtype=torch.float32, device=dev)
+        self.tws = torch.empty(kv.workspace_bytes(kv.OP_FUTURE_TARGET, d, w.window),
+                               dtype=torch.uint8, device=dev)
+        self.fws = torch.empty(max(kv.workspace_bytes(kv.OP_FWD_LSE, d), 16), dtype=torch.uint8,
+                               device=dev)
+        self.sp = torch.empty((w.B, w.Hkv, w.budget), dtype=torch.int32, device=dev)
+        self.ss = torch.empty((w.B, w.Hkv, w.budget), dtype=torch.float32, device=dev)
+        self.kc = torch.empty((w.B, w.Hkv, w.budget, w.D), dtype=torch.bfloat16, device=dev)
+        self.vc = torch.empty_like(self.kc)
+        self.mlps = [[t.to(dev) for t in synth.mlp_weights(w.Hkv, w.D, hidden, seed=seed_base + l)]
+                     for l in range(w.layers)]
+        self.k_new = synth.bf16(synth.normal((w.B, w.Hkv, w.D), seed_base + 101, dev, w.std))
+        self.v_new = synth.bf16(synth.normal((w.B, w.Hkv, w.D), seed_base + 102, dev, w.std))
+        self.q_new = synth.bf16(synth.normal((w.B, w.Hq, w.D), seed_base + 103, dev, w.std))
+        self.o = torch.empty((w.B, w.Hq, w.D), dtype=torch.bfloat16, device=dev)
+        dd = kv.dims(w.B, w.Hq, w.Hkv, w.budget, w.D)
+        self.dws = torch.empty(max(kv.workspace_bytes(kv.OP_DECODE, dd), 16), dtype=torch.uint8,
+                               device=dev)
+
+    def layer(self, i, ev=None):
+        """One layer of the step; ev: five events around its four passes."""
+        kv, w = self.kv, self.w
+        q, k, v = self.ins[i]
+        if ev:
+            ev[0].record()
+        kv.fwd_lse(q, k, out=self.lse, workspace=self.fws)
+        if ev:
+            ev[1].record()
+        kv.future_attn_target(q, k, self.lse, w.window, agg="sum", out=self.mass, workspace=self.tws)
+        if ev:
+            ev[2].record()
+        kv.evict_select(self.mass, w.n_sink, w.window, w.budget, k, v, out_pos=self.sp,
+                        out_score=self.ss, out_k=self.kc, out_v=self.vc)
+        if ev:
+            ev[3].record()
+        kv.decode_step(self.q_new, self.kc, self.vc, self.sp, self.ss, self.k_new, self.v_new, w.S,
+                       w.n_sink, w.window, self.delay, mlp=self.mlps[i], out_dtype=torch.bfloat16,
+                       want_lse=False, out=self.o, workspace=self.dws)
+        if ev:
+            ev[4].record()
+
+    def run(self, evs=None):
+        for i in range(self.w.layers):
+            self.layer(i, evs[i] if evs else None)
+
+
+def bench_prefill_step(kv, w, steps, warmup):
+    """The headline: `steps` timed steps (after `warmup`) of PrefillStep,
+    between two events; events around every pass of every layer give the
+    per-pass means (at ~9 ms per layer their cost is negligible).  The
+    roofline of the transposed pass is its flops per call over the mean of
+    its calls' event durations in the timed steps."""
+    st = PrefillStep(kv, w)
+    for i in range(warmup):
+        st.run()
+        log(f"{w.name}: warm-up step {i + 1}/{warmup} issued")
+    torch.cuda.synchronize()
+    E = lambda: torch.cuda.Event(enable_timing=True)
+    evs = [[[E() for _ in range(5)] for _ in range(w.layers)] for _ in range(steps)]
+    a, b = E(), E()
+    a.record()
+    for i in range(steps):
+        st.run(evs[i])
+        log(f"{w.name}: timed step {i + 1}/{steps} issued")
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    n = steps * w.layers
+    flat = [e for step in evs for e in step]
+    per = [sum(e[j].elapsed_time(e[j + 1]) for e in flat) / n for j in range(4)]
+    t_fwd, t_tr, t_sel, t_dec = per
+    f_fwd, f_tr = target_flops(w)
+    rows = w.B * w.Hkv
+    sg_bytes = rows * (4 * w.S + 8 * w.budget) + rows * 2 * (2 * w.budget * w.D * 2)
+    tf = lambda f, ms_: f / (ms_ / 1e3) / 1e12
+    out = {"ms_per_step": ms, "keys_per_s": w.layers * w.B * w.Hkv * w.S / (ms / 1e3),
+           "t_target_ms": t_tr, "f_target": f_tr,
+           "per_layer_ms": {"fwd_lse": t_fwd, "future_attn_target": t_tr, "select_gather": t_sel,
+                            "decode_step": t_dec},
+           "fwd_lse": {"flops": f_fwd, "tflops": tf(f_fwd, t_fwd),
+                       "frac": tf(f_fwd, t_fwd) / MFMA_BF16_PEAK_TFLOPS},
+           "future_attn_target": {"flops": f_tr, "tflops": tf(f_tr, t_tr),
+                                  "frac": tf(f_tr, t_tr) / MFMA_BF16_PEAK_TFLOPS},
+           "select_gather": {"bytes": sg_bytes, "achieved": sg_bytes / (t_sel / 1e3) / 1e9,
+                             "unit": "GB/s",
+                             "frac": sg_bytes / (t_sel / 1e3) / 1e9 / HBM_PEAK_GBS},
+           "decode_step": {"ms": t_dec, "sequences": w.B, "slots": w.budget,
+                           "entry_point": "kvpop_decode_step"}}
+    del st
+    torch.cuda.empty_cache()
+    return out
+
+
 def target_flops_lookahead(w, lookahead):
     """Algorithmic flops of the transposed pass with a finite lookahead L:
     key t counts queries t+w .. min(S-1, t+w+L), so 2*D*sum_j min(L+1, j)
@@ -227,6 +333,46 @@ def bench_retention(kv, st, reps=50):
                               "achieved": gbs(sel_bytes + gat_bytes, t_both), "unit": "GB/s",
                               "frac": gbs(sel_bytes + gat_bytes, t_both) / HBM_PEAK_GBS},
             "note": "8 rows of 4096 scores: launch- and latency-bound, not bandwidth-bound"}
+
+
+def bench_attention_output(kv, w, reps=5, seed=6000):
+    """The main pass with its attention output (App. D.4 first step, App. I)
+    on one layer of a workload: kvpop_fwd_lse with v and a bf16 o, beside
+    the LSE-only call on the same inputs.  Algorithmic flops of the output
+    mode: 4 D per causal (query, key) pair -- the score product and the
+    P.V product -- i.e. twice those of the LSE-only pass."""
+    dev = torch.device("cuda")
+    q, k, v = synth.attention_inputs(w, seed=seed, device=dev)
+    d = kv.dims(w.B, w.Hq, w.Hkv, w.S, w.D)
+    lse = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device=dev)
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    aws = torch.empty(kv.workspace_bytes(kv.OP_FWD_ATTN, d), dtype=torch.uint8, device=dev)
+    fws = torch.empty(max(kv.workspace_bytes(kv.OP_FWD_LSE, d), 16), dtype=torch.uint8, device=dev)
+
+    def t_ms(fn):
+        fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    t_out = t_ms(lambda: kv.fwd_lse(q, k, v=v, out=lse, out_o=o, workspace=aws))
+    t_lse = t_ms(lambda: kv.fwd_lse(q, k, out=lse, workspace=fws))
+    f_lse, _ = target_flops(w)
+    tf = lambda f, ms: f / (ms / 1e3) / 1e12
+    out = {"workload": w.name, "o_dtype": "bf16", "entry_point": "kvpop_fwd_lse (v, o given)",
+           "ms": t_out, "flops": 2 * f_lse, "tflops": tf(2 * f_lse, t_out),
+           "frac": tf(2 * f_lse, t_out) / MFMA_BF16_PEAK_TFLOPS,
+           "lse_only": {"ms": t_lse, "flops": f_lse, "frac": tf(f_lse, t_lse) / MFMA_BF16_PEAK_TFLOPS},
+           "note": "output-mode time includes the V transpose into the workspace"}
+    del q, k, v, o, aws
+    torch.cuda.empty_cache()
+    return out
 
 
 def live_pairs(until, S):
@@ -657,22 +803,98 @@ def bench_decode(kv, steps, layers, seed=5):
     }
 
 
-def cpu_baseline(min_seconds=10.0):
-    """The oracle (plain C, double, all host threads) on the target work of
-    the layer workload -- LSE of all 32 query heads, the future mass of all
-    8 x 4096 keys, then the oracle's selection -- repeated until at least
-    `min_seconds` have passed; plus the oracle's decode step (cache step with
-    given scores + decode attention) on a few (sequence, layer) units of the
-    bounded-decode workload, scaled to whole steps."""
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_target_sample(w, threads, min_seconds, seed):
+    """The oracle's target work on a bounded, labelled sample of one layer
+    of workload w, scaled to the whole workload.  Rounds of randomly drawn
+    normalizer rows (LSE of row d costs d + 1 dot products) and key columns
+    (the future mass of key t costs G * (S - t - w) dot products, fed seeded
+    stand-in normalizers: the oracle's cost does not depend on their values)
+    run until `min_seconds` have passed; each half is scaled by its share of
+    the layer's dot products.  Selection is timed on every row of the layer.
+    Returns KV-head keys per second over the whole workload (every layer
+    costs the same)."""
     import numpy as np
 
     import oracle
 
+    q, k, _ = synth.attention_inputs(w, seed=seed)
+    qf = np.ascontiguousarray(q.float().numpy())
+    kf = np.ascontiguousarray(k.float().numpy())
+    del q, k
+    G = w.Hq // w.Hkv
+    r = np.random.default_rng(seed)
+    t_rows = t_keys = 0.0
+    dots_rows = dots_keys = 0
+    n_rows = n_keys = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < min_seconds:
+        bh = int(r.integers(w.B * w.Hkv))
+        b, h = divmod(bh, w.Hkv)
+        qs = np.ascontiguousarray(qf[b:b + 1, h * G:(h + 1) * G])
+        ks = np.ascontiguousarray(kf[b:b + 1, h:h + 1])
+        rows = r.integers(0, G * w.S, 64).astype(np.int64)
+        a = time.perf_counter()
+        oracle.lse(qs, ks, rows=rows, nthreads=threads)
+        t_rows += time.perf_counter() - a
+        dots_rows += int((rows % w.S + 1).sum())
+        n_rows += rows.size
+        cols = r.integers(0, w.S, 64).astype(np.int64)
+        lse_stand_in = synth.normalizers(1, G, w.S, seed=seed + n_keys).double().numpy()
+        a = time.perf_counter()
+        oracle.future_mass(qs, ks, lse_stand_in, w.window, cols=cols, nthreads=threads)
+        t_keys += time.perf_counter() - a
+        dots_keys += int((G * np.clip(w.S - cols - w.window, 0, None)).sum())
+        n_keys += cols.size
+    # dot products of one layer: LSE rows sum_d (d + 1) per query head;
+    # mass sum_t max(0, S - t - w) per query head
+    n = max(w.S - w.window, 0)
+    layer_rows = w.B * w.Hq * w.S * (w.S + 1) // 2
+    layer_keys = w.B * w.Hq * n * (n + 1) // 2
+    sc = synth.scores((w.B, w.Hkv, w.S), seed=seed).numpy()
+    a = time.perf_counter()
+    oracle.select(sc, w.n_sink, w.window, w.budget)
+    t_sel = time.perf_counter() - a
+    t_layer = t_rows * layer_rows / dots_rows + t_keys * layer_keys / dots_keys + t_sel
+    return {"value": w.B * w.Hkv * w.S / t_layer, "unit": "keys/s", "cores": threads,
+            "kind": "oracle", "workload": w.name,
+            "sample": f"{n_rows} LSE rows and {n_keys} key columns of one {w.name} layer "
+                      f"({t_rows + t_keys:.1f} s), each scaled by its share of the layer's dot "
+                      f"products, plus selection of all {w.B * w.Hkv} rows ({t_sel:.2f} s)"
+                      + ("; every layer costs the same" if w.layers > 1 else ""),
+            "scaled_s_per_layer": t_layer}
+
+
+def cpu_baseline(min_seconds=10.0):
+    """The oracle (plain C, double, all host threads) on bounded samples:
+    the 36-layer prefill (the headline workload, scaled from sampled rows
+    and keys), the skewed 16k batch (the same way), the Qwen3-4B layer's
+    whole target work (LSE of all 32 query heads, the future mass of all
+    8 x 4096 keys, then selection), and the decode step on a few (sequence,
+    layer) units of the bounded-decode workload, scaled to whole steps."""
+    import numpy as np
+
+    import oracle
+
+    threads = len(os.sched_getaffinity(0))
+    out = cpu_target_sample(synth.QWEN8B, threads, min_seconds, seed=4000)
+    out["cpu_model"] = cpu_model()
+    out["skewed_long"] = cpu_target_sample(synth.SKEWED, threads, min_seconds / 2, seed=3000)
     w = synth.QWEN4B
     q, k, _ = synth.attention_inputs(w, seed=7)
     qf = np.ascontiguousarray(q.float().numpy())
     kf = np.ascontiguousarray(k.float().numpy())
-    threads = len(os.sched_getaffinity(0))
     reps = 0
     t0 = time.perf_counter()
     while True:
@@ -681,12 +903,13 @@ def cpu_baseline(min_seconds=10.0):
         oracle.select(m.astype(np.float32), w.n_sink, w.window, w.budget)
         reps += 1
         dt = time.perf_counter() - t0
-        if dt >= min_seconds:
+        if dt >= min_seconds / 2:
             break
     keys = w.B * w.Hkv * w.S
-    out = {"value": keys * reps / dt, "unit": "keys/s", "cores": threads, "kind": "oracle",
-           "sample": f"{reps} full {w.name} steps' target work (LSE of {w.Hq} query heads, future "
-                     f"mass of {keys} keys, selection), no decode step; {dt:.1f} s"}
+    out["layer_step"] = {"value": keys * reps / dt, "unit": "keys/s", "cores": threads,
+                         "kind": "oracle", "workload": w.name,
+                         "sample": f"{reps} full {w.name} target computations (LSE of {w.Hq} query "
+                                   f"heads, future mass of {keys} keys, selection); {dt:.1f} s"}
     out["decode"] = cpu_decode_baseline(threads)
     return out
 
@@ -779,17 +1002,26 @@ def calibrate_copy(mib):
     print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}), flush=True)
 
 
+LEGS = ("prefill", "layer", "variants", "retention", "sparse", "skewed", "attn_out",
+        "sparse_long", "decode", "cpu")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=5, help="timed steps of the 36-layer prefill")
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--prefill-layers", type=int, default=36,
+                    help="layers of the headline step (fewer only for profiling runs)")
+    ap.add_argument("--layer-steps", type=int, default=20)
+    ap.add_argument("--layer-warmup", type=int, default=50)
     ap.add_argument("--decode-steps", type=int, default=512)
     ap.add_argument("--decode-layers", type=int, default=36)
+    ap.add_argument("--only", default="", help="comma-separated legs to run: " + ",".join(LEGS))
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-long", action="store_true",
-                    help="skip the skewed 16k and the 36-layer 32k prefill workloads")
+                    help="skip the skewed 16k batch and the 32k sparse-normalizer layer")
     ap.add_argument("--calibrate-copy", type=int, metavar="MIB", default=0,
                     help="only run a plain copy of MIB MiB (counter calibration)")
     a = ap.parse_args()
@@ -801,6 +1033,18 @@ def main():
     if a.calibrate_copy:
         calibrate_copy(a.calibrate_copy)
         return
+    legs = set(a.only.split(",")) if a.only else set(LEGS)
+    bad = legs - set(LEGS)
+    if bad:
+        ap.error(f"unknown legs {sorted(bad)}")
+    if a.no_decode:
+        legs.discard("decode")
+    if a.no_cpu:
+        legs.discard("cpu")
+    if a.no_long:
+        legs -= {"skewed", "sparse_long"}
+
+    import dataclasses
 
     import future_attention_scoring_kvpop_amd as kv
 
@@ -809,55 +1053,78 @@ def main():
         __graft_entry__.build()
     torch.cuda.set_device(0)
 
-    log(f"target step: {a.warmup} warmup + {a.steps} timed")
-    st, ms, t_tr, brk, f_fwd, f_tr = bench_target(kv, a.steps, a.warmup)
-    w = st.w
-    keys = w.B * w.Hkv * w.S
-    value = keys / (ms / 1e3)
-    t_fwd = brk["fwd_lse"]
-    log(f"target step {ms:.4f} ms (future target {t_tr:.4f}; instrumented: fwd_lse {t_fwd:.4f}, "
-        f"select+gather+decode {brk['select_gather_decode']:.4f})")
-    achieved_tr = f_tr / (t_tr / 1e3) / 1e12
-    achieved_fwd = f_fwd / (t_fwd / 1e3) / 1e12
-    out = {
-        "metric": METRIC, "value": value, "unit": "keys/s", "n_gpus": 1, "steps": a.steps,
-        "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
-                   "head_dim": w.D, "seq_len": w.S, "window": w.window, "sinks": w.n_sink,
-                   "budget": w.budget, "aggregation": "sum", "rope_theta": synth.ROPE_THETA,
-                   "step": "fwd_lse + future_attn_target + evict_select(+gather) + cache_step + "
-                           "decode_attend"},
-        "roofline": {"bound": "mfma", "kernel": "kvpop_future_attn_target (transposed pass + merge)",
-                     "achieved": achieved_tr, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved_tr / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic_bytes(),
-                     "flops_per_launch": f_tr, "ms_per_launch": t_tr},
-        "kernels": {"fwd_lse": {"ms": t_fwd, "tflops": achieved_fwd,
-                                "frac": achieved_fwd / MFMA_BF16_PEAK_TFLOPS},
-                    "future_attn_target": {"ms": t_tr, "tflops": achieved_tr,
-                                           "frac": achieved_tr / MFMA_BF16_PEAK_TFLOPS},
-                    "select_gather_decode": {"ms": brk["select_gather_decode"]},
-                    "instrumented_ms_per_step": brk["ms_per_step"],
-                    "note": "fwd_lse and select_gather_decode from a second loop with events "
-                            "around every pass; future_attn_target from the timed steps"},
-    }
-    out["target_variants"] = bench_target_variants(kv, st)
-    out["retention"] = bench_retention(kv, st)
-    log("sparse normalizer: running top-k mask, sparse causal pass, transposed pass")
-    out["sparse_normalizer"] = bench_sparse(kv, st)
-    if not a.no_long:
+    w = synth.QWEN8B
+    if a.prefill_layers != w.layers:
+        w = dataclasses.replace(w, layers=a.prefill_layers)
+    out = {"metric": METRIC, "value": None, "unit": "keys/s", "n_gpus": 1, "steps": a.steps,
+           "warmup": a.warmup, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": w.name, "layers": w.layers, "batch": w.B, "q_heads": w.Hq,
+                      "kv_heads": w.Hkv, "head_dim": w.D, "seq_len": w.S, "window": w.window,
+                      "sinks": w.n_sink, "budget": w.budget, "aggregation": "sum",
+                      "rope_theta": synth.ROPE_THETA,
+                      "step": "per layer: fwd_lse + future_attn_target + evict_select(+gather) + "
+                              "decode_step (cache step with delayed MLP score + decode attention)"}}
+    if "prefill" in legs:
+        log(f"{w.name}: {a.warmup} warm-up + {a.steps} timed steps of {w.layers} layers")
+        pre = bench_prefill_step(kv, w, a.steps, a.warmup)
+        achieved = pre["f_target"] / (pre["t_target_ms"] / 1e3) / 1e12
+        out["value"] = pre["keys_per_s"]
+        out["ms_per_step"] = pre["ms_per_step"]
+        out["roofline"] = {"bound": "mfma",
+                           "kernel": "kvpop_future_attn_target (transposed pass + merge)",
+                           "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic_bytes(),
+                           "flops_per_launch": pre["f_target"], "ms_per_launch": pre["t_target_ms"]}
+        out["prefill_36_layers"] = {k_: v_ for k_, v_ in pre.items()
+                                    if k_ not in ("t_target_ms", "f_target")}
+        if w.layers != 36:
+            out["reduced"] = True
+        log(f"{w.name}: {pre['ms_per_step']:.2f} ms per step, {out['value']:.4g} keys/s, "
+            f"target {achieved / MFMA_BF16_PEAK_TFLOPS:.3f} of peak")
+    if legs & {"layer", "variants", "retention", "sparse"}:
+        log(f"layer step: {a.layer_warmup} warmup + {a.layer_steps} timed")
+        st, ms, t_tr, brk, f_fwd, f_tr = bench_target(kv, a.layer_steps, a.layer_warmup)
+        wl = st.w
+        tf = lambda f, t: f / (t / 1e3) / 1e12
+        out["layer_step"] = {
+            "workload": wl.name, "ms_per_step": ms, "keys_per_s": wl.B * wl.Hkv * wl.S / (ms / 1e3),
+            "step": "fwd_lse + future_attn_target + evict_select(+gather) + cache_step + "
+                    "decode_attend",
+            "fwd_lse": {"ms": brk["fwd_lse"], "tflops": tf(f_fwd, brk["fwd_lse"]),
+                        "frac": tf(f_fwd, brk["fwd_lse"]) / MFMA_BF16_PEAK_TFLOPS},
+            "future_attn_target": {"ms": t_tr, "tflops": tf(f_tr, t_tr),
+                                   "frac": tf(f_tr, t_tr) / MFMA_BF16_PEAK_TFLOPS},
+            "select_gather_decode": {"ms": brk["select_gather_decode"]},
+            "instrumented_ms_per_step": brk["ms_per_step"],
+            "note": "fwd_lse and select_gather_decode from a second loop with events around every "
+                    "pass; future_attn_target from the timed steps"}
+        if "variants" in legs:
+            out["layer_step"]["target_variants"] = bench_target_variants(kv, st)
+        if "retention" in legs:
+            out["layer_step"]["retention"] = bench_retention(kv, st)
+        if "sparse" in legs:
+            log("sparse normalizer: running top-k mask, sparse causal pass, transposed pass")
+            out["sparse_normalizer"] = bench_sparse(kv, st)
+        del st
+        torch.cuda.empty_cache()
+    if "attn_out" in legs:
+        log("attention output of the main pass: 4k layer and one 32k layer")
+        out["attention_output"] = {"qwen3-4b-layer": bench_attention_output(kv, synth.QWEN4B, reps=20),
+                                   "qwen3-8b-prefill-layer": bench_attention_output(kv, synth.QWEN8B)}
+    if "skewed" in legs:
         log("skewed-long: 4 x 16384, 3 warm-up and 4 timed passes")
         out["skewed_long"] = bench_prefill(kv, synth.SKEWED, reps=4, warm=3)
-        log("qwen3-8b-prefill: 36 layers x 32768, 1 timed pass")
-        out["prefill_36_layers"] = bench_prefill(kv, synth.QWEN8B, reps=1)
-        out["prefill_36_layers"]["sparse_one_layer"] = bench_sparse_long(kv, synth.QWEN8B)
-    if not a.no_decode:
+    if "sparse_long" in legs:
+        log("sparse normalizer on one 32k-prefill layer")
+        out["sparse_normalizer_32k_layer"] = bench_sparse_long(kv, synth.QWEN8B)
+    if "decode" in legs:
         log(f"decode: {a.decode_steps} steps x {a.decode_layers} layers")
         out["decode"] = bench_decode(kv, a.decode_steps, a.decode_layers)
         if a.decode_layers != 36 or a.decode_steps != 512:
             out["decode"]["reduced"] = True
-    if not a.no_cpu:
-        log("cpu baseline: oracle on a bounded sample")
+    if "cpu" in legs:
+        log("cpu baseline: oracle on bounded samples")
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)
 
