@@ -79,6 +79,13 @@ size_t kvpop_workspace_bytes(int op, const kvpop_dims* dims, int window) {
   return 0;
 }
 
+// Keys, keep_until and V^T of one KV head are addressed by 32-bit byte
+// offsets (buffer ranges below 2 GiB).
+static bool fwd_ranges_ok(const AttnShape& s) {
+  const double s_pad = (double)((s.S + 63) / 64 * 64);
+  return (double)s.S * s.D * 2 < 2147483648.0 && s_pad * s.D * 2 < 2147483648.0;
+}
+
 // Workspace check of the main pass: LSE-only calls need the plan's bytes
 // (none for many row blocks), calls with an attention output the V^T buffer.
 static kvpop_status check_fwd_workspace(size_t need, size_t align, const void* workspace,
@@ -105,6 +112,7 @@ kvpop_status kvpop_fwd_lse(const kvpop_dims* dims, const void* q, const void* k,
   if (!q || !k || !lse) return KVPOP_ERR_INVALID_ARGUMENT;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(lse, 4)) return KVPOP_ERR_INVALID_ARGUMENT;
   if ((st = check_fwd_output(v, o, o_dtype)) != KVPOP_OK) return st;
+  if (!fwd_ranges_ok(s)) return KVPOP_ERR_UNSUPPORTED;
   const size_t need = v ? kvpop::fwd_out_workspace_bytes(s)
                         : kvpop::plan_fwd(s).partial_floats * sizeof(float);
   if ((st = check_fwd_workspace(need, v ? 256 : 16, workspace, workspace_bytes)) != KVPOP_OK)
@@ -206,6 +214,7 @@ kvpop_status kvpop_fwd_lse_sparse(const kvpop_dims* dims, const void* q, const v
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(keep_until, 4) || !aligned(lse, 4))
     return KVPOP_ERR_INVALID_ARGUMENT;
   if ((st = check_fwd_output(v, o, o_dtype)) != KVPOP_OK) return st;
+  if (!fwd_ranges_ok(s)) return KVPOP_ERR_UNSUPPORTED;
   const size_t need = v ? kvpop::fwd_out_workspace_bytes(s)
                         : budget > 0 ? kvpop::plan_fwd_sparse(s, budget).workspace_bytes
                                      : kvpop::plan_fwd(s).partial_floats * sizeof(float);
@@ -232,6 +241,10 @@ kvpop_status kvpop_future_attn_target(const kvpop_dims* dims, const void* q, con
       !aligned(workspace, 256) || (mass_per_qhead && !aligned(mass_per_qhead, 4)))
     return KVPOP_ERR_INVALID_ARGUMENT;
   if ((double)s.S + window + 512.0 > 2.0e9) return KVPOP_ERR_UNSUPPORTED;
+  // query rows and normalizers are addressed by 32-bit byte offsets within
+  // one head's Q and one group's LSE
+  if ((double)s.S * s.D * 2 >= 2147483648.0 || (double)s.S * (s.Hq / s.Hkv) * 4 >= 2147483648.0)
+    return KVPOP_ERR_UNSUPPORTED;
   if (workspace_bytes < kvpop::plan_target(s, window).workspace_bytes)
     return KVPOP_ERR_WORKSPACE_TOO_SMALL;
   const int la = (lookahead < 0 || lookahead >= s.S) ? -1 : lookahead;  // >= S-1 has no effect

@@ -61,6 +61,39 @@ __device__ __forceinline__ void dma4(const void* g, void* lds_base) {
                                    (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
 }
 
+// Raw buffer resource (gfx9 layout: 48-bit base, stride 0, num_records bytes,
+// 32-bit data format) for a wave-uniform range; loads past num_records
+// return zero without touching memory.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+  r.z = __builtin_amdgcn_readfirstlane((int)bytes);
+  r.w = 0x00020000;
+  return r;
+}
+
+}  // namespace kvpop
+extern "C" __device__ void kvpop_raw_buffer_load_lds(kvpop::i32x4 rsrc,
+                                                     __attribute__((address_space(3))) void* lds,
+                                                     int size, int voffset, int soffset, int offset,
+                                                     int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+namespace kvpop {
+
+// Direct buffer -> LDS loads: lane i writes its bytes (zero past the
+// range) at lds_base + size * i; lds_base must be wave-uniform; voff is the
+// lane's byte offset in the range.
+__device__ __forceinline__ void bdma16(i32x4 rsrc, uint32_t voff, void* lds_base) {
+  kvpop_raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_base, 16, (int)voff,
+                            0, 0, 0);
+}
+__device__ __forceinline__ void bdma4(i32x4 rsrc, uint32_t voff, void* lds_base) {
+  kvpop_raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_base, 4, (int)voff,
+                            0, 0, 0);
+}
+
 // Wait until at most N vector memory operations of this wave are in flight
 // (gfx9 s_waitcnt encoding: vmcnt bits [3:0] and [15:14]; expcnt and
 // lgkmcnt left at their "no wait" maxima).

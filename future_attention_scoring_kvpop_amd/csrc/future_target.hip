@@ -23,10 +23,14 @@
 //     registers per wave keep four waves per SIMD resident, so the MFMA
 //     phase of one wave overlaps the exp2/accumulate phase of the others.
 //   * All waves of a workgroup (8 for D = 128) share each stage of two
-//     query tiles.  Stages reach LDS by direct global->LDS DMA into a ring,
-//     each wave issuing a fixed share (and its own copy of the tiles'
+//     query tiles.  Stages reach LDS by direct buffer->LDS loads into a
+//     ring, each wave issuing a fixed share (and its own copy of the tiles'
 //     normalizers); each stage is its own LDS object so the compiler never
-//     drains in-flight prefetches before a read.  Rows are stored unpadded
+//     drains in-flight prefetches before a read.  A load's address is the
+//     head's buffer range plus a 32-bit offset (a scalar row base plus a
+//     per-lane constant), and rows past S read as zero, so issuing a stage
+//     costs one vector add per load (5-7% off the pass against 64-bit
+//     per-lane addresses with clamped rows).  Rows are stored unpadded
 //     with their 16-byte chunks XOR-swizzled by row, which keeps the
 //     fragment reads bank-conflict free.  A bare s_barrier plus explicit
 //     vmcnt/lgkmcnt waits orders the ring; B fragments are read in groups of
@@ -207,6 +211,16 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KVPO
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
+  // byte offset of this lane's 16-byte chunk within its query-row DMAs'
+  // tile (row and swizzled chunk depend only on the lane and the wave)
+  uint32_t qoff[QPW];
+#pragma unroll
+  for (int j = 0; j < QPW; ++j) {
+    const int I = wave * QPW + j;
+    const int row = (I % NQI) * ROWS_PER_LOAD + lane / CPR;
+    qoff[j] = (uint32_t)(row * ROWB + (((lane % CPR) ^ (row & (CPR - 1))) << 4));
+  }
+  const uint32_t col4 = (uint32_t)col * 4u;
 
   for (bool first = true;; first = false) {
   const int nq = n_qtiles(geo, ch, kb);
@@ -218,6 +232,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KVPO
   const int run = (bh * geo.n_chunks + ch) * geo.n_kb + kb;
   const int run0 = run * (PER_HEAD ? G : 1);
   const size_t head0 = (size_t)b * Hq + (size_t)h * G;  // first query head of the group
+  const i32x4 rl = buffer_rsrc(lse + head0 * S, (uint32_t)(G * S) * 4u);
   if (!geo.item_mode && off == 0 && tid == 0) run_start[run] = x;
   if (!first) {
     wait_lgkmcnt0();  // every wave is done reading the previous block's stages
@@ -245,19 +260,21 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KVPO
     }
     // each lane fetches one 16-byte chunk of a query row; chunks are
     // XOR-swizzled by row in LDS, so the lane holds logical chunk pc ^ row
+    // Buffer loads: a query row DMA is the head's range plus this lane's
+    // byte offset (the tile's first row, a scalar, plus the lane's fixed
+    // offset); rows past S read as zero.  The normalizers of the stage's
+    // tiles (lanes 32 h .. 32 h + 31: tile h) come from the group's range.
 #pragma unroll
     for (int j = 0; j < QPW; ++j) {
       const int I = wave * QPW + j;
       const int tt = I / NQI;
-      const int row = (I % NQI) * ROWS_PER_LOAD + lane / CPR;
-      const int lc = (lane % CPR) ^ (row & (CPR - 1));
-      const int d = min(dt0 + tq[tt] * kQT + row, S - 1);
-      const bf16_t* qb = q + (head0 + tg[tt]) * S * D;
-      dma16(qb + (size_t)d * D + lc * 8, qst(J) + I * 1024);
+      const i32x4 rq = buffer_rsrc(q + (head0 + tg[tt]) * S * D, (uint32_t)S * ROWB);
+      bdma16(rq, (uint32_t)((dt0 + tq[tt] * kQT) * ROWB) + qoff[j], qst(J) + I * 1024);
     }
     {
-      const int tt = TPS == 2 ? half : 0;
-      dma4(lse + (head0 + tg[tt]) * S + min(dt0 + tq[tt] * kQT + col, S - 1), lst(J) + wave * 64);
+      const uint32_t l0 = (uint32_t)(tg[0] * S + dt0 + tq[0] * kQT) * 4u;
+      const uint32_t l1 = TPS == 2 ? (uint32_t)(tg[1] * S + dt0 + tq[1] * kQT) * 4u : l0;
+      bdma4(rl, (half ? l1 : l0) + col4, lst(J) + wave * 64);
     }
 #pragma unroll
     for (int t = 0; t < TPS; ++t)
@@ -354,14 +371,16 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KVPO
         }
         if constexpr (KVPOP_TGT_SETPRIO == 1) __builtin_amdgcn_s_setprio(0);
         if constexpr (KVPOP_TGT_SETPRIO == 2) __builtin_amdgcn_s_setprio(1);
-        // queries past the sequence end get L = +inf, so their terms vanish
-        const float L2 = d0 + col < S ? lraw * kLog2e : __builtin_inff();
-        const bool full = d0 >= ts + 31 + window &&
+        // squares inside the allowed region and the sequence need no test
+        const bool full = d0 >= ts + 31 + window && d0 + kQT <= S &&
                           (lookahead < 0 || d0 + kQT - 1 <= ts + window + lookahead);
         if (full) {
+          const float nl2 = lraw * -kLog2e;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) macc[r] += fast_exp2(fmaf(acc[r], c, -L2));
+          for (int r = 0; r < 16; ++r) macc[r] += fast_exp2(fmaf(acc[r], c, nl2));
         } else {
+          // queries past the sequence end get L = +inf, so their terms vanish
+          const float L2 = d0 + col < S ? lraw * kLog2e : __builtin_inff();
           // key row of register r is ts + 4*half + 8*(r/4) + r%4: the pair is
           // allowed when base - (8*(r/4) + r%4) lies in [0, lookahead]
           const int base = d0 + col - ts - window - 4 * half;

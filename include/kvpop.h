@@ -98,7 +98,9 @@ const char* kvpop_status_string(kvpop_status s);
  *              (256-byte aligned; V transposed, 64-key padded).  No
  *              initialisation needed.
  * Errors: INVALID_ARGUMENT for NULL q, k or lse, v without o (or the
- * reverse), misaligned pointers, a bad o_dtype; WORKSPACE_TOO_SMALL.
+ * reverse), misaligned pointers, a bad o_dtype; UNSUPPORTED when one KV
+ * head's K or V (S * D * 2 bytes, S rounded up to 64) reaches 2 GiB;
+ * WORKSPACE_TOO_SMALL.
  */
 kvpop_status kvpop_fwd_lse(const kvpop_dims* dims, const void* q, const void* k, const void* v,
                            float* lse, void* o, kvpop_out_dtype o_dtype, void* workspace,
@@ -192,6 +194,10 @@ kvpop_status kvpop_fwd_lse_sparse(const kvpop_dims* dims, const void* q, const v
  * The result is deterministic on a given device: partial sums are reduced
  * in a fixed order, and how the work is cut depends only on the shape and
  * the device's count of resident workgroups.
+ * Errors: INVALID_ARGUMENT for NULL q, k, lse, mass or workspace, w < 0, a
+ * bad agg, misaligned pointers; UNSUPPORTED when one head's Q (S * D * 2
+ * bytes) or one group's LSE (S * G * 4 bytes) reaches 2 GiB;
+ * WORKSPACE_TOO_SMALL.
  */
 kvpop_status kvpop_future_attn_target(const kvpop_dims* dims, const void* q, const void* k,
                                       const float* lse, int window, int lookahead, kvpop_agg agg,
