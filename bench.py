@@ -44,7 +44,32 @@ FP32_VECTOR_PEAK_TFS = 157.3     # MI355X fp32 vector (counts packed FMA; one FM
 # only for the kernel code it was taken on (sources_digest): bench reports
 # null once that changes.
 TRAFFIC_SOURCES = ("future_target.hip", "common.h", "launch.h")
-TRAFFIC = None
+TRAFFIC = {"sha256": "1837fdadea88300da01de41560d4db6eab29c9108453348a290d14fcae9f8e74",
+           "fetch_bytes": 2 * (410471.9 + 4321.1) * 1024, "write_bytes": (8576.0 + 1024.0) * 1024}
+# HBM bytes per dispatch of the HBM-bound kernels the bench reports, from the
+# same pair of counter runs with the same scaling (FETCH_SIZE x 2, WRITE_SIZE
+# x 1), each valid only for the sources it was taken on.
+COUNTERS = {
+    "decode_step": {"sources": ("decode_step.hip", "decode_dev.h", "cache_step_dev.h", "mlstm_dev.h",
+                                "common.h", "launch.h"),
+                    "fetch_kib": 536891.5, "write_kib": 825.4,
+                    "per": "decode_step_kernel<128, 4> launch: one layer-step of 64 sequences x 8 KV "
+                           "heads over budget 4096"},
+    "select_prefill": {"sources": ("select.hip", "common.h", "launch.h"),
+                       "fetch_kib": 704.9, "write_kib": 512.0,
+                       "per": "select_kernel<32> launch: 8 rows of 32768 scores, budget 8192"},
+    "gather_prefill": {"sources": ("select.hip", "common.h", "launch.h"),
+                       "fetch_kib": 16666.5, "write_kib": 32768.0,
+                       "per": "gather_kernel launch: 8 rows x 8192 slots of K and V"},
+    "select_decode_prefix": {"sources": ("select.hip", "common.h", "launch.h"),
+                             "fetch_kib": 52782.1, "write_kib": 17124.2,
+                             "per": "select_kernel<32> launch: 512 rows of 32768 scores, budget 4096"},
+    "gather_decode_prefix": {"sources": ("select.hip", "common.h", "launch.h"),
+                             "fetch_kib": 532516.2, "write_kib": 1048576.1,
+                             "per": "gather_kernel launch: 512 rows x 4096 slots of K and V"},
+}
+COUNTER_SHA = {"decode": "95e66b3167c19803ca5bc2e0454642ac23c1d242e0701da31d75f1e3e2ae4434",
+               "select": "30233bdd2724acefe38b73eb57ab34a6aecb96d9353e2cb0f2f59df6ca869551"}
 METRIC = "future-attn target keys/s + MFMA util; bounded-cache decode steps/s + HBM util"
 
 
@@ -249,7 +274,9 @@ def bench_prefill_step(kv, w, steps, warmup):
                                   "frac": tf(f_tr, t_tr) / MFMA_BF16_PEAK_TFLOPS},
            "select_gather": {"bytes": sg_bytes, "achieved": sg_bytes / (t_sel / 1e3) / 1e9,
                              "unit": "GB/s",
-                             "frac": sg_bytes / (t_sel / 1e3) / 1e9 / HBM_PEAK_GBS},
+                             "frac": sg_bytes / (t_sel / 1e3) / 1e9 / HBM_PEAK_GBS,
+                             "counters": _pair_counters("select_prefill", "gather_prefill", t_sel),
+                             "note": "8 rows: bound by the latency of one workgroup per row"},
            "decode_step": {"ms": t_dec, "sequences": w.B, "slots": w.budget,
                            "entry_point": "kvpop_decode_step"}}
     del st
@@ -605,6 +632,15 @@ def decode_bytes_per_step(w, layers):
     return cache + append + exit_copy + qo
 
 
+def _pair_counters(a, b, ms):
+    """Counter bytes of two kernels launched together once per `ms`."""
+    ba, bb = counter_bytes(a), counter_bytes(b)
+    if ba is None or bb is None:
+        return None
+    gbs = (ba + bb) / (ms / 1e3) / 1e9
+    return {"bytes": ba + bb, "achieved": gbs, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS}
+
+
 def time_prefix_retention(kv, w, kp, vp, mlp, reps=3):
     """One-shot retention of one layer's prefix (64 x 8 rows of 32768 tokens
     down to the budget): the MLP scorer over every prefix key (one FMA per
@@ -645,10 +681,13 @@ def time_prefix_retention(kv, w, kp, vp, mlp, reps=3):
                       "frac": tfl / FP32_VECTOR_PEAK_TFS},
             "score_select_gather_ms": t_score + t_both,
             "select": {"ms": t_sel, "bytes": sel_bytes, "achieved": gbs(sel_bytes, t_sel),
-                       "unit": "GB/s", "frac": gbs(sel_bytes, t_sel) / HBM_PEAK_GBS},
+                       "unit": "GB/s", "frac": gbs(sel_bytes, t_sel) / HBM_PEAK_GBS,
+                       "counters": counter_hbm("select_decode_prefix", 1e3 / t_sel)},
             "select_gather": {"ms": t_both, "bytes": sel_bytes + gat_bytes,
                               "achieved": gbs(sel_bytes + gat_bytes, t_both), "unit": "GB/s",
-                              "frac": gbs(sel_bytes + gat_bytes, t_both) / HBM_PEAK_GBS}}
+                              "frac": gbs(sel_bytes + gat_bytes, t_both) / HBM_PEAK_GBS,
+                              "counters": _pair_counters("select_decode_prefix",
+                                                         "gather_decode_prefix", t_both)}}
 
 
 def bench_decode(kv, steps, layers, seed=5):
@@ -781,7 +820,8 @@ def bench_decode(kv, steps, layers, seed=5):
         "prefix": S, "delay": delay, "value": sps, "unit": "steps/s", "ms_per_step": ms / steps,
         "wall_s": wall, "bytes_per_step": by,
         "hbm": {"achieved": by * sps / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": by * sps / 1e9 / HBM_PEAK_GBS},
+                "frac": by * sps / 1e9 / HBM_PEAK_GBS,
+                "counters": counter_hbm("decode_step", sps * layers)},
         "prefix_retention": prefix_retention,
         "entry_point": "kvpop_decode_step",
         "two_calls": {"entry_points": "kvpop_cache_step + kvpop_decode_attend",
@@ -964,14 +1004,14 @@ def cpu_decode_baseline(threads, units=4, steps=16):
                       f"by 64 x 36 units per step"}
 
 
-def sources_digest():
-    """SHA-256 of the target kernel's sources with comments and blank lines
-    removed, so that only a change of code invalidates recorded counters."""
+def sources_digest(names=TRAFFIC_SOURCES):
+    """SHA-256 of kernel sources with comments and blank lines removed, so
+    that only a change of code invalidates recorded counters."""
     import hashlib
     import re
 
     h = hashlib.sha256()
-    for name in TRAFFIC_SOURCES:
+    for name in names:
         with open(os.path.join(ROOT, "future_attention_scoring_kvpop_amd", "csrc", name)) as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -987,6 +1027,27 @@ def traffic_bytes():
     if TRAFFIC is None or sources_digest() != TRAFFIC["sha256"]:
         return None
     return TRAFFIC["fetch_bytes"] + TRAFFIC["write_bytes"]
+
+
+def counter_bytes(name):
+    """HBM bytes per dispatch recorded for one of COUNTERS, or None when the
+    kernel's sources differ from those the counters were taken on."""
+    c = COUNTERS[name]
+    sha = COUNTER_SHA["decode" if name == "decode_step" else "select"]
+    if sources_digest(c["sources"]) != sha:
+        return None
+    return 2.0 * c["fetch_kib"] * 1024 + c["write_kib"] * 1024
+
+
+def counter_hbm(name, dispatches_per_s):
+    """{bytes, achieved GB/s, frac} from the recorded counters at a measured
+    dispatch rate (None when the counters are stale)."""
+    by = counter_bytes(name)
+    if by is None:
+        return None
+    gbs = by * dispatches_per_s / 1e9
+    return {"bytes_per_dispatch": by, "achieved": gbs, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+            "per": COUNTERS[name]["per"]}
 
 
 def calibrate_copy(mib):
