@@ -44,7 +44,7 @@ FP32_VECTOR_PEAK_TFS = 157.3     # MI355X fp32 vector (counts packed FMA; one FM
 # only for the kernel code it was taken on (sources_digest): bench reports
 # null once that changes.
 TRAFFIC_SOURCES = ("future_target.hip", "common.h", "launch.h")
-TRAFFIC = {"sha256": "1837fdadea88300da01de41560d4db6eab29c9108453348a290d14fcae9f8e74",
+TRAFFIC = {"sha256": "e957b9e624bc934e8b45883971ccf2f4f899428b5be40a12f5009e44883a6bdd",
            "fetch_bytes": 2 * (410471.9 + 4321.1) * 1024, "write_bytes": (8576.0 + 1024.0) * 1024}
 # HBM bytes per dispatch of the HBM-bound kernels the bench reports, from the
 # same pair of counter runs with the same scaling (FETCH_SIZE x 2, WRITE_SIZE

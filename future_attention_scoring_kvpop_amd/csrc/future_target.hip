@@ -79,7 +79,6 @@ namespace {
 #ifndef KVPOP_TGT_STAGES
 #define KVPOP_TGT_STAGES 3
 #endif
-// B * Hkv * S at or below which the 4-wave (128-key) workgroups are used
 // 32-query tiles per LDS ring stage: each barrier, DMA issue and wait then
 // covers this many tiles
 #ifndef KVPOP_TGT_TPS
@@ -93,9 +92,6 @@ namespace {
 // 512 / n registers per lane)
 #ifndef KVPOP_TGT_WPE
 #define KVPOP_TGT_WPE 4
-#endif
-#ifndef KVPOP_TGT_SMALL_KEYS
-#define KVPOP_TGT_SMALL_KEYS 0
 #endif
 // wave priority raised around a tile's MFMA burst (1; ~2% faster than 0:
 // the arbiter then feeds the matrix core first while other waves of the
@@ -572,12 +568,9 @@ static int target_slots(int D, int waves) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, 64 * waves, 0) == hipSuccess && nb > 0)
       per_cu = std::min(per_cu == 16 / waves ? nb : per_cu, nb);
   };
-  if (D == 128 && waves == 8) {
+  if (D == 128) {
     occ((const void*)future_target_kernel<128, false, 8>);
     occ((const void*)future_target_kernel<128, true, 8>);
-  } else if (D == 128) {
-    occ((const void*)future_target_kernel<128, false, 4>);
-    occ((const void*)future_target_kernel<128, true, 4>);
   } else {
     occ((const void*)future_target_kernel<64, false, 4>);
     occ((const void*)future_target_kernel<64, true, 4>);
@@ -589,8 +582,10 @@ static int target_slots(int D, int waves) {
 
 TargetPlan plan_target(const AttnShape& s, int window) {
   TargetPlan p;
-  // a 32-query tile of D = 64 is four 1 KB loads: one per wave of four
-  p.waves = s.D == 64 || (long)s.B * s.Hkv * s.S <= KVPOP_TGT_SMALL_KEYS ? 4 : 8;
+  // a 32-query tile is D / 16 1 KB loads: one per wave of eight (D = 128)
+  // or of four (D = 64); four-wave workgroups at D = 128 (128-key blocks)
+  // measured 16% slower on the 4k layer
+  p.waves = s.D == 64 ? 4 : 8;
   p.key_block = 32 * p.waves;
   p.n_kb = (s.S + p.key_block - 1) / p.key_block;
   const int G = s.Hq / s.Hkv;
@@ -632,15 +627,11 @@ hipError_t launch_future_target(const AttnShape& s, const void* q, const void* k
 #define KVPOP_TARGET_LAUNCH(DD, PH, WW)                                                            \
   hipLaunchKernelGGL((future_target_kernel<DD, PH, WW>), grid, block, 0, st, qq, kk, lse,          \
                      workspace, run_start, s.Hq, s.Hkv, s.S, window, lookahead, c, geo)
-#define KVPOP_TARGET_WAVES(DD, PH)                  \
-  if (p.waves == 4) KVPOP_TARGET_LAUNCH(DD, PH, 4); \
-  else KVPOP_TARGET_LAUNCH(DD, PH, 8)
     if (s.D == 128) {
-      if (per_head) { KVPOP_TARGET_WAVES(128, true); } else { KVPOP_TARGET_WAVES(128, false); }
+      if (per_head) { KVPOP_TARGET_LAUNCH(128, true, 8); } else { KVPOP_TARGET_LAUNCH(128, false, 8); }
     } else {
       if (per_head) { KVPOP_TARGET_LAUNCH(64, true, 4); } else { KVPOP_TARGET_LAUNCH(64, false, 4); }
     }
-#undef KVPOP_TARGET_WAVES
 #undef KVPOP_TARGET_LAUNCH
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
