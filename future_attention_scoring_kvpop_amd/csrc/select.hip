@@ -20,7 +20,14 @@
 //     equal keys fill up in position order, one scan of the waves' packed
 //     (equal, above) counts plus ballots within each wave give every kept
 //     token its output slot, so the long-range slots come out in ascending
-//     position with no sort.  Longer rows are streamed from memory, with two
+//     position with no sort.  The slots are staged in LDS (the histograms
+//     are free by then) and written by consecutive threads, and the kept
+//     scores come from registers, not from a second read of the row.
+//   * Histogram rows are padded to 260 words: with 256 every copy of one
+//     bin sits in one LDS bank, and the first pass's clustered keys then
+//     serialise on bank conflicts despite the copies (the first pass of a
+//     32K row took 7.8 us of atomics; 12% off the 32k layer's selection and
+//     15% off the 512-row decode prefix with the staging above).  Longer rows are streamed from memory, with two
 //     block scans per 8K-position chunk.
 //   * The gather is a separate, fully coalesced 16-byte-per-lane copy.
 #include <algorithm>
@@ -30,6 +37,12 @@
 
 namespace kvpop {
 namespace {
+
+// lanes holding at least this many keys count the first radix pass into
+// kSelCopies histograms per wave
+#ifndef KVPOP_SEL_COPIES_VPT
+#define KVPOP_SEL_COPIES_VPT 16
+#endif
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
@@ -69,12 +82,16 @@ __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t* t
 // use one histogram per wave.
 constexpr int kSelCopies = 8;
 constexpr int kSelHists = kSelWaves * kSelCopies;
+// Row stride of the histograms in LDS: 256 bins plus 4 words, so that the
+// copies of one bin fall in different banks (with a 256-word stride every
+// copy of a bin shares one bank and the copies' atomics conflict anyway).
+constexpr int kHistStride = 260;
 
 // Every thread: sums the kSelHists copies of each bin into the first
 // kSelThreads / 256 rows of part (4 partial sums per bin), then folds them
 // into row 0..kSelWaves-1 form for radix_pick: row g < 4 holds partial g,
 // rows 4..kSelWaves-1 are zeroed.
-__device__ __forceinline__ void fold_copies(uint32_t (*hist)[256]) {
+__device__ __forceinline__ void fold_copies(uint32_t (*hist)[kHistStride]) {
   const int tid = threadIdx.x, bin = tid & 255, grp = tid >> 8;
   uint32_t c = 0;
   for (int k = grp; k < kSelHists; k += kSelThreads / 256) c += hist[k][bin];
@@ -86,7 +103,7 @@ __device__ __forceinline__ void fold_copies(uint32_t (*hist)[256]) {
 // Wave 0 turns the per-wave digit histograms of one radix pass into the
 // digit of the rem-th largest key (higher digits first) and the rank of
 // that key among the keys with this digit.
-__device__ __forceinline__ void radix_pick(const uint32_t (*hist)[256], uint32_t rem,
+__device__ __forceinline__ void radix_pick(const uint32_t (*hist)[kHistStride], uint32_t rem,
                                            uint32_t* sh_digit, uint32_t* sh_rem) {
   const int lane = threadIdx.x & 63;
   uint32_t cnt[4], tot = 0;
@@ -125,7 +142,7 @@ template <int VPT>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const float* __restrict__ scores, int32_t* __restrict__ slot_pos,
     float* __restrict__ slot_score, int S, int n_sink, int window, int budget) {
-  __shared__ uint32_t hist[kSelHists][256];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kSelHists][kHistStride];
   __shared__ uint32_t wsum[2 * kSelWaves];
   __shared__ uint32_t sh_digit, sh_rem;
 
@@ -178,16 +195,17 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     // Slots past the row get key 0 (the key of NaN): they rank with the
     // lowest tokens and come after every real position, so with kk < n_e
     // none of them is ever kept and the counts stay consistent.
+    // the scores stay in registers beside their keys: the kept ones are
+    // written from there (their own bits: keys merge -0/+0 and NaNs)
     uint32_t kv[VPT];
+    float raw[VPT];
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int p = p0 + 64 * i;
-      const uint32_t key = rank_key(sc[min(p, e_hi - 1)]);
-      kv[i] = p < e_hi ? key : 0u;
-    }
+    for (int i = 0; i < VPT; ++i) raw[i] = sc[min(p0 + 64 * i, e_hi - 1)];
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) kv[i] = p0 + 64 * i < e_hi ? rank_key(raw[i]) : 0u;
     // first-pass histogram copies pay off once a lane holds many keys
-    constexpr int NC = VPT >= 16 ? kSelCopies : 1;
-    for (int i = tid; i < kSelWaves * NC * 64; i += kSelThreads)
+    constexpr int NC = VPT >= KVPOP_SEL_COPIES_VPT ? kSelCopies : 1;
+    for (int i = tid; i < kSelWaves * NC * kHistStride / 4; i += kSelThreads)
       reinterpret_cast<uint4*>(&hist[0][0])[i] = make_uint4(0, 0, 0, 0);
 
     // ---- radix select of the kk-th largest key ----
@@ -195,7 +213,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     for (int pass = 0; pass < 4; ++pass) {
       const int shift = 24 - 8 * pass;
       if (pass > 0)
-        for (int i = tid; i < kSelWaves * 256; i += kSelThreads) (&hist[0][0])[i] = 0u;
+        for (int i = tid; i < kSelWaves * kHistStride; i += kSelThreads) (&hist[0][0])[i] = 0u;
       __syncthreads();
       uint32_t* h = hist[pass == 0 ? wave * NC + lane % NC : wave];
 #pragma unroll
@@ -233,7 +251,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     uint32_t pre = 0;
     for (int w = 0; w < wave; ++w) pre += wsum[w];
     uint32_t eq_run = pre >> 16;
-    uint32_t out = n_sink + (pre & 0xffffu) + min(eq_run, need_eq);
+    uint32_t out = (pre & 0xffffu) + min(eq_run, need_eq);  // slot past the sinks
+    // the kept positions and scores are staged in LDS (the histograms are
+    // free now) and then written with consecutive threads on consecutive
+    // slots, instead of one scattered store per kept token
+    const bool staged = (size_t)kk * 8 <= sizeof(hist);
+    int* stg_p = reinterpret_cast<int*>(&hist[0][0]);
+    float* stg_s = reinterpret_cast<float*>(stg_p + kk);
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int p = p0 + 64 * i;
@@ -242,19 +266,31 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       const bool keep = kv[i] > T || (eq && eq_run + __popcll(em & below) < need_eq);
       const unsigned long long km = __ballot(keep);
       const uint32_t o = out + __popcll(km & below);
-      if (keep && o < (uint32_t)(n_sink + kk)) {
-        sp[o] = p;
-        if (ss) ss[o] = sc[p];  // the score's own bits (keys merge -0/+0 and NaNs)
+      if (keep && o < (uint32_t)kk) {
+        if (staged) {
+          stg_p[o] = p;
+          stg_s[o] = raw[i];
+        } else {
+          sp[n_sink + o] = p;
+          if (ss) ss[n_sink + o] = raw[i];
+        }
       }
       out += __popcll(km);
       eq_run += __popcll(em);
+    }
+    if (staged) {
+      __syncthreads();
+      for (int j = tid; j < kk; j += kSelThreads) {
+        sp[n_sink + j] = stg_p[j];
+        if (ss) ss[n_sink + j] = stg_s[j];
+      }
     }
   } else {
     // ---- radix select of the kk-th largest key, re-reading the scores ----
     uint32_t prefix = 0, pmask = 0, rem = (uint32_t)kk;
     for (int pass = 0; pass < 4; ++pass) {
       const int shift = 24 - 8 * pass;
-      for (int i = tid; i < kSelWaves * 256; i += kSelThreads) (&hist[0][0])[i] = 0u;
+      for (int i = tid; i < kSelWaves * kHistStride; i += kSelThreads) (&hist[0][0])[i] = 0u;
       __syncthreads();
       for (int p = e_lo + tid; p < e_hi; p += kSelThreads) {
         const uint32_t key = rank_key(sc[p]);
