@@ -192,17 +192,20 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     // holds position e_lo + 64*(VPT*w + i) + l in slot i (coalesced loads)
     const int lane = tid & 63;
     const int p0 = e_lo + 64 * VPT * wave + lane;
-    // Slots past the row get key 0 (the key of NaN): they rank with the
+    // Slots past the row hold a NaN, whose key is 0: they rank with the
     // lowest tokens and come after every real position, so with kk < n_e
     // none of them is ever kept and the counts stay consistent.
-    // the scores stay in registers beside their keys: the kept ones are
-    // written from there (their own bits: keys merge -0/+0 and NaNs)
-    uint32_t kv[VPT];
+    // Only the scores stay in registers and the keys are recomputed where
+    // they are used (a few ALU operations): keys, scores and positions side
+    // by side at 32 per lane overflow the 128 registers of a 1024-thread
+    // workgroup and spill.  The kept scores are written from the registers
+    // with their own bits (keys merge -0/+0 and NaNs).
     float raw[VPT];
 #pragma unroll
     for (int i = 0; i < VPT; ++i) raw[i] = sc[min(p0 + 64 * i, e_hi - 1)];
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) kv[i] = p0 + 64 * i < e_hi ? rank_key(raw[i]) : 0u;
+    for (int i = 0; i < VPT; ++i)
+      if (p0 + 64 * i >= e_hi) raw[i] = __uint_as_float(0x7fc00000u);
     // first-pass histogram copies pay off once a lane holds many keys
     constexpr int NC = VPT >= KVPOP_SEL_COPIES_VPT ? kSelCopies : 1;
     for (int i = tid; i < kSelWaves * NC * kHistStride / 4; i += kSelThreads)
@@ -217,8 +220,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       __syncthreads();
       uint32_t* h = hist[pass == 0 ? wave * NC + lane % NC : wave];
 #pragma unroll
-      for (int i = 0; i < VPT; ++i)
-        if ((kv[i] & pmask) == prefix) atomicAdd(&h[(kv[i] >> shift) & 255u], 1u);
+      for (int i = 0; i < VPT; ++i) {
+        const uint32_t key = rank_key(raw[i]);
+        if ((key & pmask) == prefix) atomicAdd(&h[(key >> shift) & 255u], 1u);
+      }
       __syncthreads();
       if (NC > 1 && pass == 0) {
         fold_copies(hist);
@@ -243,8 +248,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     uint32_t w_gt = 0, w_eq = 0;
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      w_gt += __popcll(__ballot(kv[i] > T));
-      w_eq += __popcll(__ballot(kv[i] == T));
+      const uint32_t key = rank_key(raw[i]);
+      w_gt += __popcll(__ballot(key > T));
+      w_eq += __popcll(__ballot(key == T));
     }
     if (lane == 0) wsum[wave] = (w_eq << 16) | w_gt;
     __syncthreads();
@@ -252,6 +258,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     for (int w = 0; w < wave; ++w) pre += wsum[w];
     uint32_t eq_run = pre >> 16;
     uint32_t out = (pre & 0xffffu) + min(eq_run, need_eq);  // slot past the sinks
+    // the positions are recomputed here from a copy of p0 the compiler
+    // cannot see through; otherwise it keeps all VPT of them live from the
+    // loads on
+    int q0 = p0;
+    asm volatile("" : "+v"(q0));
     // the kept positions and scores are staged in LDS (the histograms are
     // free now) and then written with consecutive threads on consecutive
     // slots, instead of one scattered store per kept token
@@ -260,10 +271,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     float* stg_s = reinterpret_cast<float*>(stg_p + kk);
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      const int p = p0 + 64 * i;
-      const bool eq = kv[i] == T;
+      const int p = q0 + 64 * i;
+      const uint32_t key = rank_key(raw[i]);
+      const bool eq = key == T;
       const unsigned long long em = __ballot(eq);
-      const bool keep = kv[i] > T || (eq && eq_run + __popcll(em & below) < need_eq);
+      const bool keep = key > T || (eq && eq_run + __popcll(em & below) < need_eq);
       const unsigned long long km = __ballot(keep);
       const uint32_t o = out + __popcll(km & below);
       if (keep && o < (uint32_t)kk) {
