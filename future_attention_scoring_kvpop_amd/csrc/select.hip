@@ -80,12 +80,29 @@ __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t* t
 // where scores cluster, and lanes of one atomic that hit one LDS address
 // serialise.  Later passes see only the keys under the chosen prefix and
 // use one histogram per wave.
-constexpr int kSelCopies = 8;
+#ifndef KVPOP_SEL_COPIES
+#define KVPOP_SEL_COPIES 8
+#endif
+constexpr int kSelCopies = KVPOP_SEL_COPIES;
 constexpr int kSelHists = kSelWaves * kSelCopies;
 // Row stride of the histograms in LDS: 256 bins plus 4 words, so that the
 // copies of one bin fall in different banks (with a 256-word stride every
 // copy of a bin shares one bank and the copies' atomics conflict anyway).
 constexpr int kHistStride = 260;
+// The LDS array holds the histograms during the radix passes and the kept
+// slots of the long-range region (8 bytes per slot) after them: at least
+// enough for rows of 16 scores per lane, so those are always staged.
+constexpr int kSelLdsWords = kSelHists * kHistStride > 2 * 16 * kSelThreads
+                                 ? kSelHists * kHistStride
+                                 : 2 * 16 * kSelThreads;
+constexpr size_t kSelLdsBytes = sizeof(uint32_t) * kSelLdsWords;
+
+// Lanes below this one whose bit is set in m (the rank of this lane among
+// the set lanes), plus base.
+__device__ __forceinline__ uint32_t lanes_below(unsigned long long m, uint32_t base) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)m, base));
+}
 
 // Every thread: sums the kSelHists copies of each bin into the first
 // kSelThreads / 256 rows of part (4 partial sums per bin), then folds them
@@ -136,13 +153,16 @@ __device__ __forceinline__ void radix_pick(const uint32_t (*hist)[kHistStride], 
 }
 
 // VPT > 0: rows of at most VPT * kSelThreads eligible tokens, held in
-// registers (VPT keys per lane) for the radix passes and the compaction.
+// registers (VPT scores per lane) for the radix passes and the compaction;
+// STAGE: the kept slots are staged in LDS (the launcher sets it only when
+// 8 * kk bytes fit the histogram array).
 // VPT == 0: longer rows, streamed from memory in chunks.
-template <int VPT>
+template <int VPT, bool STAGE>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const float* __restrict__ scores, int32_t* __restrict__ slot_pos,
     float* __restrict__ slot_score, int S, int n_sink, int window, int budget) {
-  __shared__ __attribute__((aligned(16))) uint32_t hist[kSelHists][kHistStride];
+  __shared__ __attribute__((aligned(16))) uint32_t lds[kSelLdsWords];
+  uint32_t(*hist)[kHistStride] = reinterpret_cast<uint32_t(*)[kHistStride]>(lds);
   __shared__ uint32_t wsum[2 * kSelWaves];
   __shared__ uint32_t sh_digit, sh_rem;
 
@@ -244,7 +264,6 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     // the waves' packed (equal, above) totals; within a wave, ballots order
     // the lanes; before any position, min(equal so far, need_eq) of the
     // equal tokens were kept. ----
-    const unsigned long long below = (1ull << lane) - 1ull;
     uint32_t w_gt = 0, w_eq = 0;
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
@@ -256,41 +275,40 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     __syncthreads();
     uint32_t pre = 0;
     for (int w = 0; w < wave; ++w) pre += wsum[w];
-    uint32_t eq_run = pre >> 16;
-    uint32_t out = (pre & 0xffffu) + min(eq_run, need_eq);  // slot past the sinks
+    // wave-uniform from here on: kept in scalar registers
+    uint32_t eq_run = __builtin_amdgcn_readfirstlane(pre >> 16);
+    uint32_t out = __builtin_amdgcn_readfirstlane((pre & 0xffffu) + min(pre >> 16, need_eq));
     // the positions are recomputed here from a copy of p0 the compiler
     // cannot see through; otherwise it keeps all VPT of them live from the
     // loads on
     int q0 = p0;
     asm volatile("" : "+v"(q0));
-    // the kept positions and scores are staged in LDS (the histograms are
-    // free now) and then written with consecutive threads on consecutive
-    // slots, instead of one scattered store per kept token
-    const bool staged = (size_t)kk * 8 <= sizeof(hist);
-    int* stg_p = reinterpret_cast<int*>(&hist[0][0]);
+    // STAGE: the kept positions and scores are staged in LDS (the
+    // histograms are free now) and then written with consecutive threads on
+    // consecutive slots, instead of one scattered store per kept token
+    int* stg_p = reinterpret_cast<int*>(lds);
     float* stg_s = reinterpret_cast<float*>(stg_p + kk);
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      const int p = q0 + 64 * i;
       const uint32_t key = rank_key(raw[i]);
       const bool eq = key == T;
       const unsigned long long em = __ballot(eq);
-      const bool keep = key > T || (eq && eq_run + __popcll(em & below) < need_eq);
+      const bool keep = key > T || (eq && lanes_below(em, eq_run) < need_eq);
       const unsigned long long km = __ballot(keep);
-      const uint32_t o = out + __popcll(km & below);
+      const uint32_t o = lanes_below(km, out);
       if (keep && o < (uint32_t)kk) {
-        if (staged) {
-          stg_p[o] = p;
+        if constexpr (STAGE) {
+          stg_p[o] = q0 + 64 * i;
           stg_s[o] = raw[i];
         } else {
-          sp[n_sink + o] = p;
+          sp[n_sink + o] = q0 + 64 * i;
           if (ss) ss[n_sink + o] = raw[i];
         }
       }
-      out += __popcll(km);
-      eq_run += __popcll(em);
+      out += (uint32_t)__popcll(km);
+      eq_run += (uint32_t)__popcll(em);
     }
-    if (staged) {
+    if constexpr (STAGE) {
       __syncthreads();
       for (int j = tid; j < kk; j += kSelThreads) {
         sp[n_sink + j] = stg_p[j];
@@ -389,19 +407,25 @@ hipError_t launch_select(int B, int Hkv, int S, int n_sink, int window, int budg
                          const float* scores, int32_t* slot_pos, float* slot_score,
                          hipStream_t st) {
   const int n_e = std::max(S - window, n_sink) - n_sink;
-#define KVPOP_SEL(V)                                                                            \
-  hipLaunchKernelGGL(select_kernel<V>, dim3(B * Hkv), dim3(kSelThreads), 0, st, scores, slot_pos, \
-                     slot_score, S, n_sink, window, budget)
+  // staging holds 8 bytes per long-range slot; with n_e <= 16 * kSelThreads
+  // the slots kept (fewer than n_e) always fit (kSelLdsWords)
+  const size_t kk = (size_t)std::max(budget - n_sink - window, 0);
+  const bool stage = kk * 8 <= kSelLdsBytes;
+#define KVPOP_SEL(V, ST)                                                                      \
+  hipLaunchKernelGGL((select_kernel<V, ST>), dim3(B * Hkv), dim3(kSelThreads), 0, st, scores, \
+                     slot_pos, slot_score, S, n_sink, window, budget)
   if (n_e <= 4 * kSelThreads)
-    KVPOP_SEL(4);
+    KVPOP_SEL(4, true);
   else if (n_e <= 8 * kSelThreads)
-    KVPOP_SEL(8);
+    KVPOP_SEL(8, true);
   else if (n_e <= 16 * kSelThreads)
-    KVPOP_SEL(16);
+    KVPOP_SEL(16, true);
+  else if (n_e <= 32 * kSelThreads && stage)
+    KVPOP_SEL(32, true);
   else if (n_e <= 32 * kSelThreads)
-    KVPOP_SEL(32);
+    KVPOP_SEL(32, false);
   else
-    KVPOP_SEL(0);
+    KVPOP_SEL(0, false);
 #undef KVPOP_SEL
   return hipGetLastError();
 }
