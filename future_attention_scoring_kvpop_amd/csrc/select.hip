@@ -9,13 +9,17 @@
 // gfx950 mapping
 //   * One 1024-thread workgroup per (b, h) row.  Scores are mapped to
 //     order-preserving uint32 keys (NaN lowest, -0 == +0) and the k-th
-//     largest key is found by a 4-pass MSD radix select (8-bit digits,
-//     per-wave LDS histograms -- eight per wave in the first pass of rows
-//     of 16K+ tokens, where clustered keys would serialise the atomics --
-//     and one wave-parallel suffix scan per pass).
+//     largest key is found by an MSD radix select.
 //   * Rows of up to 32K eligible tokens are read once, coalesced: each
-//     wave keeps the keys of a contiguous run of 64 x (4..32) positions in
-//     registers (slots past the row hold key 0, which is never kept).
+//     wave keeps the scores of a contiguous run of 64 x (4..32) positions
+//     in registers (slots past the row hold a NaN, whose key is never
+//     kept).  Three passes of 12, 10 and 10 bits count into histograms
+//     shared by the workgroup, in a few copies (lane l into copy l % copies)
+//     whose rows are padded by 4 words, so that lanes of one atomic rarely
+//     hit one address or one bank although keys cluster; each pass picks
+//     its digit with one block scan.  (Four passes of 8 bits with per-wave
+//     histograms took 15% longer on a 32K row: the first byte, sign and
+//     exponent, barely splits clustered scores.)
 //     Ties at the threshold key go to the lowest positions; since the kept
 //     equal keys fill up in position order, one scan of the waves' packed
 //     (equal, above) counts plus ballots within each wave give every kept
@@ -23,12 +27,8 @@
 //     position with no sort.  The slots are staged in LDS (the histograms
 //     are free by then) and written by consecutive threads, and the kept
 //     scores come from registers, not from a second read of the row.
-//   * Histogram rows are padded to 260 words: with 256 every copy of one
-//     bin sits in one LDS bank, and the first pass's clustered keys then
-//     serialise on bank conflicts despite the copies (the first pass of a
-//     32K row took 7.8 us of atomics; 12% off the 32k layer's selection and
-//     15% off the 512-row decode prefix with the staging above).  Longer rows are streamed from memory, with two
-//     block scans per 8K-position chunk.
+//   * Longer rows are streamed from memory: four 8-bit passes with per-wave
+//     histograms, then two block scans per 8K-position chunk.
 //   * The gather is a separate, fully coalesced 16-byte-per-lane copy.
 #include <algorithm>
 
@@ -37,12 +37,6 @@
 
 namespace kvpop {
 namespace {
-
-// lanes holding at least this many keys count the first radix pass into
-// kSelCopies histograms per wave
-#ifndef KVPOP_SEL_COPIES_VPT
-#define KVPOP_SEL_COPIES_VPT 16
-#endif
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
@@ -75,26 +69,30 @@ __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t* t
   return before + x - v;
 }
 
-// The first radix pass counts into kSelCopies histograms per wave (lane l
-// into copy l % kSelCopies): its digit is a float key's sign and exponent,
-// where scores cluster, and lanes of one atomic that hit one LDS address
-// serialise.  Later passes see only the keys under the chosen prefix and
-// use one histogram per wave.
+// Streamed path: 8-bit digits, one 256-bin histogram per wave; the row
+// stride is padded by 4 words so that one bin of different waves' rows
+// falls in different banks.
+constexpr int kHistStride = 260;
+
+// Register path: digits of 12, 10 and 10 bits (three passes).  Its
+// histograms are shared by the workgroup in kSelCopies copies, lane l
+// counting into copy l % kSelCopies: keys cluster (scores share a few
+// exponents, and ties), and lanes of one atomic that hit one LDS address
+// serialise.  The copies' rows are padded by 4 words so that one bin of
+// different copies falls in different banks.
 #ifndef KVPOP_SEL_COPIES
-#define KVPOP_SEL_COPIES 8
+#define KVPOP_SEL_COPIES 4
 #endif
 constexpr int kSelCopies = KVPOP_SEL_COPIES;
-constexpr int kSelHists = kSelWaves * kSelCopies;
-// Row stride of the histograms in LDS: 256 bins plus 4 words, so that the
-// copies of one bin fall in different banks (with a 256-word stride every
-// copy of a bin shares one bank and the copies' atomics conflict anyway).
-constexpr int kHistStride = 260;
+constexpr int kRegBins0 = 4096, kRegStride0 = kRegBins0 + 4;  // bits 31..20
+constexpr int kRegBins = 1024, kRegStride = kRegBins + 4;     // bits 19..10, 9..0
+static_assert(kRegBins % kSelThreads == 0 && kRegBins0 % kSelThreads == 0, "bins per thread");
+
 // The LDS array holds the histograms during the radix passes and the kept
 // slots of the long-range region (8 bytes per slot) after them: at least
 // enough for rows of 16 scores per lane, so those are always staged.
-constexpr int kSelLdsWords = kSelHists * kHistStride > 2 * 16 * kSelThreads
-                                 ? kSelHists * kHistStride
-                                 : 2 * 16 * kSelThreads;
+constexpr int kSelLdsWords = std::max({kSelWaves * kHistStride, kSelCopies * kRegStride0,
+                                       2 * 16 * kSelThreads});
 constexpr size_t kSelLdsBytes = sizeof(uint32_t) * kSelLdsWords;
 
 // Lanes below this one whose bit is set in m (the rank of this lane among
@@ -102,19 +100,6 @@ constexpr size_t kSelLdsBytes = sizeof(uint32_t) * kSelLdsWords;
 __device__ __forceinline__ uint32_t lanes_below(unsigned long long m, uint32_t base) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)m, base));
-}
-
-// Every thread: sums the kSelHists copies of each bin into the first
-// kSelThreads / 256 rows of part (4 partial sums per bin), then folds them
-// into row 0..kSelWaves-1 form for radix_pick: row g < 4 holds partial g,
-// rows 4..kSelWaves-1 are zeroed.
-__device__ __forceinline__ void fold_copies(uint32_t (*hist)[kHistStride]) {
-  const int tid = threadIdx.x, bin = tid & 255, grp = tid >> 8;
-  uint32_t c = 0;
-  for (int k = grp; k < kSelHists; k += kSelThreads / 256) c += hist[k][bin];
-  __syncthreads();
-  hist[grp][bin] = c;
-  for (int k = kSelThreads / 256 + grp; k < kSelWaves; k += kSelThreads / 256) hist[k][bin] = 0u;
 }
 
 // Wave 0 turns the per-wave digit histograms of one radix pass into the
@@ -152,6 +137,44 @@ __device__ __forceinline__ void radix_pick(const uint32_t (*hist)[kHistStride], 
   }
 }
 
+// The whole workgroup turns a histogram of NB bins (kSelCopies copies at
+// stride cs; higher digits rank first) into the digit of the rem-th largest
+// key and the rank of that key among the keys with this digit.  Thread t
+// owns the NB / kSelThreads bins below NB - t * NB / kSelThreads, so one
+// exclusive scan over the threads counts the keys in higher bins.  Needs
+// 1 <= rem <= the number of keys counted; the results are valid after the
+// caller's next barrier.
+template <int NB>
+__device__ __forceinline__ void block_pick(const uint32_t* h, int cs, uint32_t rem, uint32_t* wsum,
+                                           uint32_t* sh_digit, uint32_t* sh_rem) {
+  constexpr int BPT = NB / kSelThreads;
+  const int b0 = NB - BPT * ((int)threadIdx.x + 1);
+  uint32_t cnt[BPT], tot = 0;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int k = 0; k < kSelCopies; ++k) c += h[k * cs + b0 + j];
+    cnt[j] = c;
+    tot += c;
+  }
+  uint32_t total;
+  const uint32_t above = block_exclusive_scan(tot, wsum, &total);
+  if (above < rem && rem <= above + tot) {
+    uint32_t cum = above;
+    bool found = false;
+#pragma unroll
+    for (int j = BPT - 1; j >= 0; --j) {
+      if (!found && cum + cnt[j] >= rem) {
+        *sh_digit = (uint32_t)(b0 + j);
+        *sh_rem = rem - cum;
+        found = true;
+      }
+      cum += cnt[j];
+    }
+  }
+}
+
 // VPT > 0: rows of at most VPT * kSelThreads eligible tokens, held in
 // registers (VPT scores per lane) for the radix passes and the compaction;
 // STAGE: the kept slots are staged in LDS (the launcher sets it only when
@@ -162,7 +185,6 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const float* __restrict__ scores, int32_t* __restrict__ slot_pos,
     float* __restrict__ slot_score, int S, int n_sink, int window, int budget) {
   __shared__ __attribute__((aligned(16))) uint32_t lds[kSelLdsWords];
-  uint32_t(*hist)[kHistStride] = reinterpret_cast<uint32_t(*)[kHistStride]>(lds);
   __shared__ uint32_t wsum[2 * kSelWaves];
   __shared__ uint32_t sh_digit, sh_rem;
 
@@ -221,40 +243,43 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     // workgroup and spill.  The kept scores are written from the registers
     // with their own bits (keys merge -0/+0 and NaNs).
     float raw[VPT];
+    if (e_lo + 64 * VPT * (wave + 1) <= e_hi) {  // the whole run is in the row
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) raw[i] = sc[min(p0 + 64 * i, e_hi - 1)];
+      for (int i = 0; i < VPT; ++i) raw[i] = sc[p0 + 64 * i];
+    } else {
 #pragma unroll
-    for (int i = 0; i < VPT; ++i)
-      if (p0 + 64 * i >= e_hi) raw[i] = __uint_as_float(0x7fc00000u);
-    // first-pass histogram copies pay off once a lane holds many keys
-    constexpr int NC = VPT >= KVPOP_SEL_COPIES_VPT ? kSelCopies : 1;
-    for (int i = tid; i < kSelWaves * NC * kHistStride / 4; i += kSelThreads)
-      reinterpret_cast<uint4*>(&hist[0][0])[i] = make_uint4(0, 0, 0, 0);
-
-    // ---- radix select of the kk-th largest key ----
-    uint32_t prefix = 0, pmask = 0, rem = (uint32_t)kk;
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      if (pass > 0)
-        for (int i = tid; i < kSelWaves * kHistStride; i += kSelThreads) (&hist[0][0])[i] = 0u;
+      for (int i = 0; i < VPT; ++i) raw[i] = sc[min(p0 + 64 * i, e_hi - 1)];
+#pragma unroll
+      for (int i = 0; i < VPT; ++i)
+        if (p0 + 64 * i >= e_hi) raw[i] = __uint_as_float(0x7fc00000u);
+    }
+    // ---- radix select of the kk-th largest key: bits 31..20, then
+    // 19..10 and 9..0 of the keys under the prefix chosen so far ----
+    uint32_t prefix = 0, rem = (uint32_t)kk;
+    const int copy = lane % kSelCopies;
+    for (int pass = 0; pass < 3; ++pass) {
+      const int stride = pass == 0 ? kRegStride0 : kRegStride;
+      const int shift = pass == 0 ? 20 : 20 - 10 * pass;
+      const uint32_t pmask = pass == 0 ? 0u : ~0u << (shift + 10);
+      const uint32_t dmask = pass == 0 ? kRegBins0 - 1 : kRegBins - 1;
+      // block_pick's reads of the previous histogram precede its barriers
+      for (int i = tid; i < kSelCopies * stride / 4; i += kSelThreads)
+        reinterpret_cast<uint4*>(lds)[i] = make_uint4(0, 0, 0, 0);
       __syncthreads();
-      uint32_t* h = hist[pass == 0 ? wave * NC + lane % NC : wave];
+      uint32_t* h = lds + copy * stride;
 #pragma unroll
       for (int i = 0; i < VPT; ++i) {
         const uint32_t key = rank_key(raw[i]);
-        if ((key & pmask) == prefix) atomicAdd(&h[(key >> shift) & 255u], 1u);
+        if ((key & pmask) == prefix) atomicAdd(&h[(key >> shift) & dmask], 1u);
       }
       __syncthreads();
-      if (NC > 1 && pass == 0) {
-        fold_copies(hist);
-        __syncthreads();
-      }
-      if (wave == 0) radix_pick(hist, rem, &sh_digit, &sh_rem);
+      if (pass == 0)
+        block_pick<kRegBins0>(lds, kRegStride0, rem, wsum, &sh_digit, &sh_rem);
+      else
+        block_pick<kRegBins>(lds, kRegStride, rem, wsum, &sh_digit, &sh_rem);
       __syncthreads();
       prefix |= sh_digit << shift;
-      pmask |= 255u << shift;
       rem = sh_rem;
-      __syncthreads();
     }
     const uint32_t T = prefix;     // key of the kk-th best token
     const uint32_t need_eq = rem;  // tokens with key == T to keep (lowest positions)
@@ -288,25 +313,42 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     // consecutive slots, instead of one scattered store per kept token
     int* stg_p = reinterpret_cast<int*>(lds);
     float* stg_s = reinterpret_cast<float*>(stg_p + kk);
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const uint32_t key = rank_key(raw[i]);
-      const bool eq = key == T;
-      const unsigned long long em = __ballot(eq);
-      const bool keep = key > T || (eq && lanes_below(em, eq_run) < need_eq);
-      const unsigned long long km = __ballot(keep);
-      const uint32_t o = lanes_below(km, out);
-      if (keep && o < (uint32_t)kk) {
-        if constexpr (STAGE) {
-          stg_p[o] = q0 + 64 * i;
-          stg_s[o] = raw[i];
-        } else {
-          sp[n_sink + o] = q0 + 64 * i;
-          if (ss) ss[n_sink + o] = raw[i];
-        }
+    auto put = [&](int i, uint32_t o) {
+      if constexpr (STAGE) {
+        stg_p[o] = q0 + 64 * i;
+        stg_s[o] = raw[i];
+      } else {
+        sp[n_sink + o] = q0 + 64 * i;
+        if (ss) ss[n_sink + o] = raw[i];
       }
-      out += (uint32_t)__popcll(km);
-      eq_run += (uint32_t)__popcll(em);
+    };
+    // A wave before the tie cut keeps all its keys equal to T, a wave after
+    // it none: only the wave the cut falls in ranks its equal keys.
+    const uint32_t w_eq_u = __builtin_amdgcn_readfirstlane(w_eq);
+    if (eq_run + w_eq_u <= need_eq || eq_run >= need_eq) {
+      const bool with_eq = eq_run + w_eq_u <= need_eq;
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        const uint32_t key = rank_key(raw[i]);
+        const bool keep = key > T || (with_eq && key == T);
+        const unsigned long long km = __ballot(keep);
+        const uint32_t o = lanes_below(km, out);
+        if (keep && o < (uint32_t)kk) put(i, o);
+        out += (uint32_t)__popcll(km);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        const uint32_t key = rank_key(raw[i]);
+        const bool eq = key == T;
+        const unsigned long long em = __ballot(eq);
+        const bool keep = key > T || (eq && lanes_below(em, eq_run) < need_eq);
+        const unsigned long long km = __ballot(keep);
+        const uint32_t o = lanes_below(km, out);
+        if (keep && o < (uint32_t)kk) put(i, o);
+        out += (uint32_t)__popcll(km);
+        eq_run += (uint32_t)__popcll(em);
+      }
     }
     if constexpr (STAGE) {
       __syncthreads();
@@ -317,6 +359,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     }
   } else {
     // ---- radix select of the kk-th largest key, re-reading the scores ----
+    uint32_t(*hist)[kHistStride] = reinterpret_cast<uint32_t(*)[kHistStride]>(lds);
     uint32_t prefix = 0, pmask = 0, rem = (uint32_t)kk;
     for (int pass = 0; pass < 4; ++pass) {
       const int shift = 24 - 8 * pass;
