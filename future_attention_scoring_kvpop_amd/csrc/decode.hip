@@ -24,32 +24,87 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
                             o_out, o_bf16, lse_out, Hq, Hkv, n_slots, n_split, sps, c);
 }
 
-__global__ void decode_merge_kernel(const float* __restrict__ ws, void* __restrict__ o_out,
-                                    int o_bf16, float* __restrict__ lse_out, int Hq, int Hkv,
-                                    int D, int n_split) {
+// One workgroup per (b, query head) merges the split partial states
+// (max, sum, D features each).  The splits' maxima and scales are reduced
+// across the workgroup, so a thread issues its loads for many splits at once
+// instead of walking every split twice in sequence: with 32 splits a
+// one-thread-per-feature walk was a chain of L2 round trips, most of the
+// merge's time.  Thread t sums feature t % D over the splits s with
+// s % (kMergeThreads / D) == t / D; the groups are added in LDS.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeChunk = 1024;  // splits whose scales are held in LDS at a time
+
+__device__ __forceinline__ float block_max_merge(float v, float* red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < kMergeThreads / 64; ++w) r = fmaxf(r, red[w]);
+  return r;
+}
+
+__device__ __forceinline__ float block_sum_merge(float v, float* red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < kMergeThreads / 64; ++w) r += red[w];
+  return r;
+}
+
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
+    const float* __restrict__ ws, void* __restrict__ o_out, int o_bf16,
+    float* __restrict__ lse_out, int Hq, int Hkv, int D, int n_split) {
+  __shared__ float scl[kMergeChunk];
+  __shared__ float red[kMergeThreads / 64];
+  __shared__ float part[kMergeThreads];
   const int bg = blockIdx.x;  // b * Hq + g
   const int b = bg / Hq, g = bg % Hq;
   const int G = Hq / Hkv;
   const int h = g / G, gl = g % G;
   const size_t bh = (size_t)b * Hkv + h;
-  for (int f = threadIdx.x; f < D; f += blockDim.x) {
-    float M = -INFINITY;
-    for (int sp = 0; sp < n_split; ++sp) M = fmaxf(M, ws[((bh * n_split + sp) * G + gl) * (D + 2)]);
-    float L = 0.f, O = 0.f;
-    if (M > -INFINITY) {
-      for (int sp = 0; sp < n_split; ++sp) {
-        const float* pw = ws + ((bh * n_split + sp) * G + gl) * (D + 2);
-        if (pw[0] == -INFINITY) continue;
-        const float sc = fast_exp2(pw[0] - M);
+  const size_t stride = (size_t)G * (D + 2);  // floats from one split's state to the next
+  const float* base = ws + (bh * n_split * G + gl) * (D + 2);
+  const int tid = threadIdx.x;
+  const int ng = kMergeThreads / D, grp = tid / D, f = tid % D;
+
+  float m = -INFINITY;
+  for (int sp = tid; sp < n_split; sp += kMergeThreads) m = fmaxf(m, base[sp * stride]);
+  const float M = block_max_merge(m, red);
+  float L = 0.f, O = 0.f;
+  if (M > -INFINITY) {
+    for (int c0 = 0; c0 < n_split; c0 += kMergeChunk) {
+      const int nc = min(kMergeChunk, n_split - c0);
+      __syncthreads();  // the previous chunk's scales are consumed
+      for (int j = tid; j < nc; j += kMergeThreads) {
+        const float* pw = base + (c0 + j) * stride;
+        const float mw = pw[0];
+        const float sc = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
+        scl[j] = sc;
         L = fmaf(pw[1], sc, L);
-        O = fmaf(pw[2 + f], sc, O);
       }
+      __syncthreads();
+      if (grp < ng)
+        for (int j = grp; j < nc; j += ng) O = fmaf(base[(c0 + j) * stride + 2 + f], scl[j], O);
     }
-    const size_t oi = (size_t)bg * D + f;
-    const float val = L > 0.f ? O / L : 0.f;
+  }
+  L = block_sum_merge(L, red);
+  part[tid] = O;
+  __syncthreads();
+  if (tid < D) {
+    float acc = part[tid];
+    for (int k = 1; k < ng; ++k) acc += part[tid + k * D];
+    const size_t oi = (size_t)bg * D + tid;
+    const float val = L > 0.f ? acc / L : 0.f;
     if (o_bf16) reinterpret_cast<uint16_t*>(o_out)[oi] = f32_to_bf16_rne(val);
     else reinterpret_cast<float*>(o_out)[oi] = val;
-    if (f == 0 && lse_out) lse_out[bg] = L > 0.f ? (M + fast_log2(L)) * kLn2 : -INFINITY;
+    if (tid == 0 && lse_out) lse_out[bg] = L > 0.f ? (M + fast_log2(L)) * kLn2 : -INFINITY;
   }
 }
 
@@ -65,6 +120,11 @@ static __device__ __align__(256) float scratch[KVPOP_DECODE_NOALLOC_SCRATCH_BYTE
 // rounds of resident workgroups a decode launch is split into
 #ifndef KVPOP_DEC_ROUNDS
 #define KVPOP_DEC_ROUNDS 1
+#endif
+
+// fewest slots a split of the decode attention covers
+#ifndef KVPOP_DEC_MIN_SPLIT
+#define KVPOP_DEC_MIN_SPLIT 256
 #endif
 
 // Resident decode workgroups on the current device for the group size used.
@@ -98,7 +158,7 @@ DecodePlan plan_decode(const AttnShape& s) {
   const int units = s.B * s.Hkv;
   const int wgs = KVPOP_DEC_ROUNDS * decode_slots(s.D, s.Hq / s.Hkv);
   int want = (wgs + units - 1) / units;
-  const int max_split = (s.S + 255) / 256;
+  const int max_split = (s.S + KVPOP_DEC_MIN_SPLIT - 1) / KVPOP_DEC_MIN_SPLIT;
   p.n_split = want < 1 ? 1 : (want > max_split ? max_split : want);
   if (p.n_split < 1) p.n_split = 1;
   int sps = (s.S + p.n_split - 1) / p.n_split;
@@ -142,8 +202,9 @@ hipError_t launch_decode(const AttnShape& s, const void* q, const void* kc, cons
 #undef KVPOP_DEC
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_split == 1) return e;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(s.B * s.Hq), dim3(s.D), 0, st, workspace, o, o_bf16,
-                     lse, s.Hq, s.Hkv, s.D, p.n_split);
+  static_assert(kMergeThreads % 128 == 0, "feature groups for D = 64 and 128");
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(s.B * s.Hq), dim3(kMergeThreads), 0, st, workspace,
+                     o, o_bf16, lse, s.Hq, s.Hkv, s.D, p.n_split);
   return hipGetLastError();
 }
 
