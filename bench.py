@@ -56,20 +56,20 @@ COUNTERS = {
                     "per": "decode_step_kernel<128, 4> launch: one layer-step of 64 sequences x 8 KV "
                            "heads over budget 4096"},
     "select_prefill": {"sources": ("select.hip", "common.h", "launch.h"),
-                       "fetch_kib": 704.9, "write_kib": 512.0,
-                       "per": "select_kernel<32> launch: 8 rows of 32768 scores, budget 8192"},
+                       "fetch_kib": 661.4, "write_kib": 512.0,
+                       "per": "select_kernel<32, true> launch: 8 rows of 32768 scores, budget 8192"},
     "gather_prefill": {"sources": ("select.hip", "common.h", "launch.h"),
-                       "fetch_kib": 16666.5, "write_kib": 32768.0,
+                       "fetch_kib": 16659.6, "write_kib": 32768.0,
                        "per": "gather_kernel launch: 8 rows x 8192 slots of K and V"},
     "select_decode_prefix": {"sources": ("select.hip", "common.h", "launch.h"),
-                             "fetch_kib": 52782.1, "write_kib": 17124.2,
-                             "per": "select_kernel<32> launch: 512 rows of 32768 scores, budget 4096"},
+                             "fetch_kib": 32918.0, "write_kib": 16416.0,
+                             "per": "select_kernel<32, true> launch: 512 rows of 32768 scores, budget 4096"},
     "gather_decode_prefix": {"sources": ("select.hip", "common.h", "launch.h"),
-                             "fetch_kib": 532516.2, "write_kib": 1048576.1,
+                             "fetch_kib": 532510.4, "write_kib": 1048576.0,
                              "per": "gather_kernel launch: 512 rows x 4096 slots of K and V"},
 }
 COUNTER_SHA = {"decode": "95e66b3167c19803ca5bc2e0454642ac23c1d242e0701da31d75f1e3e2ae4434",
-               "select": "30233bdd2724acefe38b73eb57ab34a6aecb96d9353e2cb0f2f59df6ca869551"}
+               "select": "6d37a8f69e6991588cc2e0d7e53997806efc2dc28d72af9e8731aefffff6f48b"}
 METRIC = "future-attn target keys/s + MFMA util; bounded-cache decode steps/s + HBM util"
 
 
