@@ -21,7 +21,8 @@
 // gfx950 mapping
 //   * A workgroup owns 64 consecutive tokens (one per lane) of one row; its
 //     NSEG waves split the scanned positions [s, S) into NSEG segments of at
-//     most 64 chunks of 64 positions.  Each wave ranks the 64 positions of a
+//     most 64 chunks of 64 positions (128 chunks for rows past 65536).
+//     Each wave ranks the 64 positions of a
 //     chunk (one per lane), stores their keys in its own 256 bytes of LDS
 //     and reads them back four at a time with broadcast ds_read_b128, so a
 //     comparison of one position against the wave's 64 tokens costs one
@@ -42,7 +43,10 @@
 namespace kvpop {
 namespace {
 
-constexpr int kRtChunksPerSeg = 64;  // chunks of 64 positions per wave at most
+// chunks of 64 positions per wave at most: 64, or 128 for rows past 65536
+// positions (sixteen waves; the chunk counts then take 128 KB of LDS)
+constexpr int kRtChunksPerSeg = 64;
+constexpr int kRtChunksPerSegLong = 128;
 
 __device__ __forceinline__ uint32_t priority_key(float sigma, float lam, int t) {
   // pi = sigma + lambda * t, each operation rounded to fp32: contraction
@@ -57,13 +61,13 @@ __device__ __forceinline__ uint32_t order_key(const float* __restrict__ sc, floa
   return priority_key(sc[t], lam, t);
 }
 
-template <int NSEG>
+template <int NSEG, int CPS>
 __global__ __launch_bounds__(64 * NSEG) void running_topk_kernel(
     const float* __restrict__ scores, const float* __restrict__ log_decay,
     int* __restrict__ keep_until, int* __restrict__ cutoff, int Hkv, int S, int n_sink,
     int window, int k, int blocks_per_row, int seg_chunks) {
   __shared__ __attribute__((aligned(16))) uint32_t keys[NSEG][64];
-  __shared__ uint8_t ccount[NSEG][kRtChunksPerSeg][64];
+  __shared__ uint8_t ccount[NSEG][CPS][64];
   __shared__ int segtot[NSEG][64];
   __shared__ int found[2][64];  // positions of the (k-1)-th and k-th better token
 
@@ -189,7 +193,7 @@ __global__ __launch_bounds__(64 * NSEG) void running_topk_kernel(
 
 }  // namespace
 
-int running_topk_max_len() { return 16 * kRtChunksPerSeg * 64; }
+int running_topk_max_len() { return 16 * kRtChunksPerSegLong * 64; }
 
 hipError_t launch_running_topk(int B, int Hkv, int S, int n_sink, int window, int budget,
                                const float* scores, const float* log_decay, int* keep_until,
@@ -210,9 +214,10 @@ hipError_t launch_running_topk(int B, int Hkv, int S, int n_sink, int window, in
   int nseg = n_chunks <= 4 * kRtChunksPerSeg ? 4 : n_chunks <= 8 * kRtChunksPerSeg ? 8 : 16;
   const long waves_cap = 4L * 4 * device_cu_count();
   while (nseg < 16 && grid * nseg * 2 <= waves_cap && n_chunks >= nseg * 4) nseg *= 2;
-  if (nseg == 4) go(running_topk_kernel<4>, 4);
-  else if (nseg == 8) go(running_topk_kernel<8>, 8);
-  else go(running_topk_kernel<16>, 16);
+  if (n_chunks > 16 * kRtChunksPerSeg) go(running_topk_kernel<16, kRtChunksPerSegLong>, 16);
+  else if (nseg == 4) go(running_topk_kernel<4, kRtChunksPerSeg>, 4);
+  else if (nseg == 8) go(running_topk_kernel<8, kRtChunksPerSeg>, 8);
+  else go(running_topk_kernel<16, kRtChunksPerSeg>, 16);
   return hipGetLastError();
 }
 

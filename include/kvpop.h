@@ -129,7 +129,7 @@ kvpop_status kvpop_fwd_lse(const kvpop_dims* dims, const void* q, const void* k,
  *               when k = 0.
  * Errors: INVALID_ARGUMENT for non-positive sizes, s < 0, w < 0,
  * budget < s + w, a NULL scores or keep_until, misaligned pointers;
- * UNSUPPORTED for seq_len > 65536.
+ * UNSUPPORTED for seq_len > 131072.
  * The result is exact (integer outputs, no rounding-order dependence).
  */
 kvpop_status kvpop_running_topk(int batch, int n_kv_heads, int seq_len, int n_sink, int window,

@@ -207,7 +207,7 @@ def test_running_topk_and_sparse_lse_validation(lib):
     assert rt(1, 8, 4096, 4, 128, 1024, GOOD, None, None, None, None) == 1
     assert rt(1, 8, 4096, 4, 128, 1024, P(0x10002), None, GOOD, None, None) == 1  # misaligned
     assert rt(1, 8, 4096, 4, 128, 1024, GOOD, P(0x10001), GOOD, None, None) == 1
-    assert rt(1, 8, 65537, 4, 128, 1024, GOOD, None, GOOD, None, None) == 2     # longest row 65536
+    assert rt(1, 8, 131073, 4, 128, 1024, GOOD, None, GOOD, None, None) == 2    # longest row 131072
     sp = lib.kvpop_fwd_lse_sparse
     d = kv.dims(1, 32, 8, 4096, 128)
     assert sp(ctypes.byref(d), GOOD, GOOD, None, None, 0, GOOD, None, 0, None, 0, None) == 1     # no mask

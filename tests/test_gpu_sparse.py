@@ -87,11 +87,13 @@ def test_running_topk_full_size(kv, S, budget, w):
 
 
 @pytest.mark.parametrize("S,budget,w,s", [(40000, 5000, 256, 4), (65536, 6000, 128, 70),
-                                          (33000, 300, 16, 0)])
+                                          (33000, 300, 16, 0), (65600, 4000, 64, 4),
+                                          (100000, 9000, 256, 4), (131072, 8192, 256, 130)])
 def test_running_topk_longest_rows(kv, S, budget, w, s):
-    """Rows past 32768 positions take 16 segment waves per token block (the
-    longest rows the kernel takes are 65536); a small budget makes most
-    tokens leave early, a large one keeps many to the end."""
+    """Rows past 32768 positions take 16 segment waves per token block, rows
+    past 65536 segments of 128 chunks (the longest rows the kernel takes are
+    131072); a small budget makes most tokens leave early, a large one keeps
+    many to the end."""
     sc = synth.scores((1, 2, S), seed=S + budget, kind="ties" if S == 33000 else "normal")
     u, c, ou, oc = _topk(kv, sc, s, w, budget, [0.0, 2e-5])
     assert np.array_equal(u, ou)
@@ -99,7 +101,7 @@ def test_running_topk_longest_rows(kv, S, budget, w, s):
 
 
 def test_running_topk_rejects_rows_past_its_limit(kv):
-    sc = torch.zeros((1, 1, 65537), dtype=torch.float32, device="cuda")
+    sc = torch.zeros((1, 1, 131073), dtype=torch.float32, device="cuda")
     with pytest.raises(kv.KvpopError):
         kv.running_topk(sc, 4, 16, 64)
 
