@@ -242,8 +242,9 @@ kvpop_status kvpop_future_attn_target(const kvpop_dims* dims, const void* q, con
     return KVPOP_ERR_INVALID_ARGUMENT;
   if ((double)s.S + window + 512.0 > 2.0e9) return KVPOP_ERR_UNSUPPORTED;
   // query rows and normalizers are addressed by 32-bit byte offsets within
-  // one head's Q and one group's LSE
-  if ((double)s.S * s.D * 2 >= 2147483648.0 || (double)s.S * (s.Hq / s.Hkv) * 4 >= 2147483648.0)
+  // one group's Q and one group's LSE
+  if ((double)s.S * s.D * 2 * (s.Hq / s.Hkv) >= 2147483648.0 ||
+      (double)s.S * (s.Hq / s.Hkv) * 4 >= 2147483648.0)
     return KVPOP_ERR_UNSUPPORTED;
   if (workspace_bytes < kvpop::plan_target(s, window).workspace_bytes)
     return KVPOP_ERR_WORKSPACE_TOO_SMALL;

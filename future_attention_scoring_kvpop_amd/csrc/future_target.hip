@@ -27,9 +27,9 @@
 //     ring, each wave issuing a fixed share (and its own copy of the tiles'
 //     normalizers); each stage is its own LDS object so the compiler never
 //     drains in-flight prefetches before a read.  A load's address is the
-//     head's buffer range plus a 32-bit offset (a scalar row base plus a
-//     per-lane constant), and rows past S read as zero, so issuing a stage
-//     costs one vector add per load (5-7% off the pass against 64-bit
+//     group's buffer range plus a 32-bit offset (a scalar row base plus a
+//     per-lane constant); rows past S are masked by L = +inf.  Issuing a
+//     stage costs one vector add per load (5-7% off the pass against 64-bit
 //     per-lane addresses with clamped rows).  Rows are stored unpadded
 //     with their 16-byte chunks XOR-swizzled by row, which keeps the
 //     fragment reads bank-conflict free.  A bare s_barrier plus explicit
@@ -229,6 +229,9 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KVPO
   const int run0 = run * (PER_HEAD ? G : 1);
   const size_t head0 = (size_t)b * Hq + (size_t)h * G;  // first query head of the group
   const i32x4 rl = buffer_rsrc(lse + head0 * S, (uint32_t)(G * S) * 4u);
+  // the group's query rows: one range for its G heads, a head's rows at
+  // offset (head * S + row) * ROWB
+  const i32x4 rqg = buffer_rsrc(q + head0 * S * D, (uint32_t)(G * S) * ROWB);
   if (!geo.item_mode && off == 0 && tid == 0) run_start[run] = x;
   if (!first) {
     wait_lgkmcnt0();  // every wave is done reading the previous block's stages
@@ -256,16 +259,18 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KVPO
     }
     // each lane fetches one 16-byte chunk of a query row; chunks are
     // XOR-swizzled by row in LDS, so the lane holds logical chunk pc ^ row
-    // Buffer loads: a query row DMA is the head's range plus this lane's
+    // Buffer loads: a query row DMA is the group's range plus this lane's
     // byte offset (the tile's first row, a scalar, plus the lane's fixed
-    // offset); rows past S read as zero.  The normalizers of the stage's
-    // tiles (lanes 32 h .. 32 h + 31: tile h) come from the group's range.
+    // offset); rows past S read the next head's first rows (zero past the
+    // last head), which the non-full path masks with L = +inf.  The
+    // normalizers of the stage's tiles (lanes 32 h .. 32 h + 31: tile h)
+    // come from the group's range the same way.
 #pragma unroll
     for (int j = 0; j < QPW; ++j) {
       const int I = wave * QPW + j;
       const int tt = I / NQI;
-      const i32x4 rq = buffer_rsrc(q + (head0 + tg[tt]) * S * D, (uint32_t)S * ROWB);
-      bdma16(rq, (uint32_t)((dt0 + tq[tt] * kQT) * ROWB) + qoff[j], qst(J) + I * 1024);
+      bdma16(rqg, (uint32_t)((tg[tt] * S + dt0 + tq[tt] * kQT) * ROWB) + qoff[j],
+             qst(J) + I * 1024);
     }
     {
       const uint32_t l0 = (uint32_t)(tg[0] * S + dt0 + tq[0] * kQT) * 4u;

@@ -195,8 +195,8 @@ kvpop_status kvpop_fwd_lse_sparse(const kvpop_dims* dims, const void* q, const v
  * in a fixed order, and how the work is cut depends only on the shape and
  * the device's count of resident workgroups.
  * Errors: INVALID_ARGUMENT for NULL q, k, lse, mass or workspace, w < 0, a
- * bad agg, misaligned pointers; UNSUPPORTED when one head's Q (S * D * 2
- * bytes) or one group's LSE (S * G * 4 bytes) reaches 2 GiB;
+ * bad agg, misaligned pointers; UNSUPPORTED when one group's Q (G * S * D
+ * * 2 bytes) or one group's LSE (S * G * 4 bytes) reaches 2 GiB;
  * WORKSPACE_TOO_SMALL.
  */
 kvpop_status kvpop_future_attn_target(const kvpop_dims* dims, const void* q, const void* k,

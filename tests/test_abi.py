@@ -96,6 +96,10 @@ def test_target_validation(lib):
     assert call(ws=None) == 1
     assert call(ws=P(0x10010)) == 1           # workspace must be 256-byte aligned
     assert call(nbytes=need - 4) == 3
+    # one group's Q rows are addressed by 32-bit offsets: G * S * D * 2 < 2 GiB
+    big = kv.dims(1, 64, 8, 1 << 20, 128)
+    assert lib.kvpop_future_attn_target(ctypes.byref(big), GOOD, GOOD, GOOD, 128, -1, 0, 0,
+                                        GOOD, None, GOOD, 1 << 40, None) == 2
 
 
 def test_select_validation(lib):
