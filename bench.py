@@ -44,15 +44,15 @@ FP32_VECTOR_PEAK_TFS = 157.3     # MI355X fp32 vector (counts packed FMA; one FM
 # only for the kernel code it was taken on (sources_digest): bench reports
 # null once that changes.
 TRAFFIC_SOURCES = ("future_target.hip", "common.h", "launch.h")
-TRAFFIC = {"sha256": "e957b9e624bc934e8b45883971ccf2f4f899428b5be40a12f5009e44883a6bdd",
-           "fetch_bytes": 2 * (410471.9 + 4321.1) * 1024, "write_bytes": (8576.0 + 1024.0) * 1024}
+TRAFFIC = {"sha256": "4542a3bf544551a30468d807beb3b381cb2c8800097f79c1c5808cde80b73395",
+           "fetch_bytes": 2 * (412533.8 + 4319.0) * 1024, "write_bytes": (8576.0 + 1024.0) * 1024}
 # HBM bytes per dispatch of the HBM-bound kernels the bench reports, from the
 # same pair of counter runs with the same scaling (FETCH_SIZE x 2, WRITE_SIZE
 # x 1), each valid only for the sources it was taken on.
 COUNTERS = {
     "decode_step": {"sources": ("decode_step.hip", "decode_dev.h", "cache_step_dev.h", "mlstm_dev.h",
                                 "common.h", "launch.h"),
-                    "fetch_kib": 536891.5, "write_kib": 825.4,
+                    "fetch_kib": 536897.4, "write_kib": 825.4,
                     "per": "decode_step_kernel<128, 4> launch: one layer-step of 64 sequences x 8 KV "
                            "heads over budget 4096"},
     "select_prefill": {"sources": ("select.hip", "common.h", "launch.h"),
@@ -62,10 +62,10 @@ COUNTERS = {
                        "fetch_kib": 16659.6, "write_kib": 32768.0,
                        "per": "gather_kernel launch: 8 rows x 8192 slots of K and V"},
     "select_decode_prefix": {"sources": ("select.hip", "common.h", "launch.h"),
-                             "fetch_kib": 32918.0, "write_kib": 16416.0,
+                             "fetch_kib": 32917.9, "write_kib": 16416.0,
                              "per": "select_kernel<32, true> launch: 512 rows of 32768 scores, budget 4096"},
     "gather_decode_prefix": {"sources": ("select.hip", "common.h", "launch.h"),
-                             "fetch_kib": 532510.4, "write_kib": 1048576.0,
+                             "fetch_kib": 532510.7, "write_kib": 1048576.0,
                              "per": "gather_kernel launch: 512 rows x 4096 slots of K and V"},
 }
 COUNTER_SHA = {"decode": "95e66b3167c19803ca5bc2e0454642ac23c1d242e0701da31d75f1e3e2ae4434",
