@@ -950,6 +950,9 @@ def cpu_baseline(min_seconds=10.0):
                          "kind": "oracle", "workload": w.name,
                          "sample": f"{reps} full {w.name} target computations (LSE of {w.Hq} query "
                                    f"heads, future mass of {keys} keys, selection); {dt:.1f} s"}
+    # the same layer on one host thread, from a sampled bound (the full
+    # layer takes about half a minute on one thread)
+    out["layer_step"]["one_thread"] = cpu_target_sample(w, 1, min_seconds / 4, seed=4100)
     out["decode"] = cpu_decode_baseline(threads)
     return out
 
