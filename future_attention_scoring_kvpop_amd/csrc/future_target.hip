@@ -41,7 +41,10 @@
 //   * Squares fully inside the allowed region take a mask-free path (one
 //     FMA, one exp2, one add per pair); fully masked squares are skipped;
 //     diagonal squares compare each register's key row with a per-lane
-//     threshold; queries past S are masked by L = +inf.
+//     threshold; queries past S are masked by L = +inf.  Which of the three
+//     a tile takes depends only on its first query position, so each wave
+//     derives two position ranges once per run and a tile costs two scalar
+//     range tests; the fetch and compute positions advance by additions.
 //   * Each run writes one partial sum per key and workgroup, into piece
 //     run + wg (even split; runs and workgroups both advance along the list,
 //     so no two pairs share a piece) or run (one run per workgroup); the
@@ -84,7 +87,7 @@ namespace {
 #ifndef KVPOP_TGT_TPS
 #define KVPOP_TGT_TPS 2
 #endif
-// B fragments read from LDS per wait (8: all at once; 4: two groups)
+// B fragments read from LDS per wait (8: all at once; 4: two groups; 2: four)
 #ifndef KVPOP_TGT_FRAG_GROUP
 #define KVPOP_TGT_FRAG_GROUP 4
 #endif
@@ -92,6 +95,18 @@ namespace {
 // 512 / n registers per lane)
 #ifndef KVPOP_TGT_WPE
 #define KVPOP_TGT_WPE 4
+#endif
+// D = 128: 32-key sub-tiles per wave (1: 32 keys per wave; 2: 64 keys, so
+// each query fragment read from LDS feeds two MFMAs) and waves per workgroup
+#ifndef KVPOP_TGT_KSUB
+#define KVPOP_TGT_KSUB 1
+#endif
+#ifndef KVPOP_TGT_WAVES128
+#define KVPOP_TGT_WAVES128 8
+#endif
+// waves per SIMD of the two-sub-tile kernel (its keys take 64 registers)
+#ifndef KVPOP_TGT_WPE_KS2
+#define KVPOP_TGT_WPE_KS2 3
 #endif
 // wave priority raised around a tile's MFMA burst (1; ~2% faster than 0:
 // the arbiter then feeds the matrix core first while other waves of the
@@ -117,12 +132,14 @@ __device__ __forceinline__ void xreduce_step(float* v, int lane) {
   }
 }
 
-template <int D, bool PER_HEAD, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KVPOP_TGT_WPE, KVPOP_TGT_WPE))) void future_target_kernel(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const float* __restrict__ lse,
-    float* __restrict__ partial, int* __restrict__ run_start, int Hq, int Hkv, int S,
-    int window, int lookahead, float c, TargetGeom geo) {
-  constexpr int KB = 32 * WAVES;            // keys per key block
+template <int D, bool PER_HEAD, int WAVES, int KS>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(
+    KS == 1 ? KVPOP_TGT_WPE : KVPOP_TGT_WPE_KS2, KS == 1 ? KVPOP_TGT_WPE : KVPOP_TGT_WPE_KS2))) void
+future_target_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                     const float* __restrict__ lse, float* __restrict__ partial,
+                     int* __restrict__ run_start, int Hq, int Hkv, int S, int window,
+                     int lookahead, float c, TargetGeom geo) {
+  constexpr int KB = 32 * WAVES * KS;       // keys per key block
   constexpr int NS = D / 16;                // MFMA k-slices
   constexpr int CPR = D / 8;                // 16-byte chunks per row
   constexpr int ROWB = D * 2;               // bytes per query row
@@ -224,7 +241,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KVPO
   const int b = bh / Hkv, h = bh - (bh / Hkv) * Hkv;
   const int t0 = kb * KB;
   const int dt0 = 32 * max(ch * geo.ct, kb * geo.kbt + geo.w_t);  // the run's first query tile
-  const int ts = t0 + 32 * wave;  // this wave's 32 keys
+  const int ts = t0 + 32 * KS * wave;  // this wave's first key (32 KS keys)
   const int run = (bh * geo.n_chunks + ch) * geo.n_kb + kb;
   const int run0 = run * (PER_HEAD ? G : 1);
   const size_t head0 = (size_t)b * Hq + (size_t)h * G;  // first query head of the group
@@ -238,25 +255,41 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KVPO
     bare_barrier();
   }
 
-  // tile counters (query head of the group, tile in the run) of the next
-  // tile to fetch and of the tile being computed
+  // Fetch state: the group row (head * S + query position) of the next tile
+  // to fetch, and its head and tile in the run; a head's tiles end hstep
+  // rows before the next head's first tile.
   int ig = off / nq;
   int iq = off - ig * nq;
-  int cg = ig, cq = iq;
+  const int hstep = S - kQT * nq;
+  int frow = ig * S + dt0 + iq * kQT;
+  // Compute state: first query position d0 of the tile being computed and
+  // its head (cg); a head's tiles end at d_end.
+  const int d_end = dt0 + kQT * nq;
+  int d0 = dt0 + iq * kQT, cg = ig;
+  // This wave's tiles by d0 (wave-uniform): a tile has allowed pairs when
+  // d0 - skip_lo lies in [0, span] (none when the wave's keys start past S)
+  // and needs no mask when d0 - full_lo lies in [0, fspan].
+  constexpr int kFar = 1 << 29;
+  int skip_lo = ts + window - (kQT - 1), span = lookahead < 0 ? kFar : 32 * KS + 30 + lookahead;
+  if (ts >= S) {
+    skip_lo = kFar;
+    span = 0;
+  }
+  int full_lo = ts + 32 * KS - 1 + window;
+  int fspan = min(S - kQT, lookahead < 0 ? kFar : ts + window + lookahead - (kQT - 1)) - full_lo;
+  if (fspan < 0) {
+    full_lo = kFar;
+    fspan = 0;
+  }
 
-  // DMA of the stage's tiles (ig, iq) and the next one into stage J, then
-  // advance past them.  Query-row DMA I fetches tile I / NQI; past the last
-  // tile of the segment the final tile is fetched again (never computed).
+  // DMA of the stage's tiles (the next to fetch and the one after) into
+  // stage J, then advance past them.  Query-row DMA I fetches tile I / NQI;
+  // past the last tile of the group the stage's first tile is fetched again
+  // (never computed).
   auto issue = [&](auto J) {
-    int tg[2], tq[2];
-    tg[0] = ig;
-    tq[0] = iq;
-    tg[1] = iq + 1 == nq ? ig + 1 : ig;
-    tq[1] = iq + 1 == nq ? 0 : iq + 1;
-    if (TPS == 2 && tg[1] >= G) {
-      tg[1] = tg[0];
-      tq[1] = tq[0];
-    }
+    int rows[2];
+    rows[0] = frow;
+    rows[1] = iq + 1 < nq ? frow + kQT : ig + 1 < G ? frow + kQT + hstep : frow;
     // each lane fetches one 16-byte chunk of a query row; chunks are
     // XOR-swizzled by row in LDS, so the lane holds logical chunk pc ^ row
     // Buffer loads: a query row DMA is the group's range plus this lane's
@@ -269,49 +302,59 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KVPO
     for (int j = 0; j < QPW; ++j) {
       const int I = wave * QPW + j;
       const int tt = I / NQI;
-      bdma16(rqg, (uint32_t)((tg[tt] * S + dt0 + tq[tt] * kQT) * ROWB) + qoff[j],
-             qst(J) + I * 1024);
+      bdma16(rqg, (uint32_t)rows[tt] * ROWB + qoff[j], qst(J) + I * 1024);
     }
     {
-      const uint32_t l0 = (uint32_t)(tg[0] * S + dt0 + tq[0] * kQT) * 4u;
-      const uint32_t l1 = TPS == 2 ? (uint32_t)(tg[1] * S + dt0 + tq[1] * kQT) * 4u : l0;
+      const uint32_t l0 = (uint32_t)rows[0] * 4u;
+      const uint32_t l1 = TPS == 2 ? (uint32_t)rows[1] * 4u : l0;
       bdma4(rl, (half ? l1 : l0) + col4, lst(J) + wave * 64);
     }
 #pragma unroll
-    for (int t = 0; t < TPS; ++t)
+    for (int t = 0; t < TPS; ++t) {
+      frow += kQT;
       if (++iq == nq) {
         iq = 0;
         ++ig;
+        frow += hstep;
       }
+    }
   };
 
-  bf16x8 ka[NS];
-  {
-    const int t = ts + col;
+  // key sub-tile j of the wave: keys ts + 32 j .. ts + 32 j + 31
+  bf16x8 ka[KS][NS];
+#pragma unroll
+  for (int j = 0; j < KS; ++j) {
+    const int t = ts + 32 * j + col;
     const bf16_t* krow = k + (((size_t)b * Hkv + h) * S + (t < S ? t : 0)) * D + 8 * half;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) ka[s] = as_bf16x8(t < S ? ldg16(krow + 16 * s) : make_uint4(0, 0, 0, 0));
+    for (int s = 0; s < NS; ++s)
+      ka[j][s] = as_bf16x8(t < S ? ldg16(krow + 16 * s) : make_uint4(0, 0, 0, 0));
   }
-  float macc[16];
+  float macc[KS][16];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) macc[r] = 0.f;
+  for (int j = 0; j < KS; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) macc[j][r] = 0.f;
 
   // Sum each key's per-lane partials over the 32 lanes sharing its row and
-  // write one float per key of this wave's tile.
+  // write one float per key of this wave's sub-tiles.
   auto flush = [&](int gout) {
-    float v[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) v[r] = macc[r];
-    xreduce_step<8>(v, lane);
-    xreduce_step<4>(v, lane);
-    xreduce_step<2>(v, lane);
-    xreduce_step<1>(v, lane);
-    v[0] += __shfl_xor(v[0], 16);  // lane col now holds row register col & 15
-    const int r = col & 15;
-    const int t = ts + 8 * (r >> 2) + 4 * half + (r & 3);
-    if (col < 16 && t < S) {
-      const int piece = run0 + (PER_HEAD ? gout : 0) + (geo.item_mode ? 0 : wg);
-      partial[(size_t)piece * KB + (t - t0)] = v[0];
+    for (int j = 0; j < KS; ++j) {
+      float v[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) v[r] = macc[j][r];
+      xreduce_step<8>(v, lane);
+      xreduce_step<4>(v, lane);
+      xreduce_step<2>(v, lane);
+      xreduce_step<1>(v, lane);
+      v[0] += __shfl_xor(v[0], 16);  // lane col now holds row register col & 15
+      const int r = col & 15;
+      const int t = ts + 32 * j + 8 * (r >> 2) + 4 * half + (r & 3);
+      if (col < 16 && t < S) {
+        const int piece = run0 + (PER_HEAD ? gout : 0) + (geo.item_mode ? 0 : wg);
+        partial[(size_t)piece * KB + (t - t0)] = v[0];
+      }
     }
   };
 
@@ -338,15 +381,14 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KVPO
     for (int tt = 0; tt < TPS; ++tt) {
       const int it = si * TPS + tt;
       if (it >= n_iter) break;
-      const int d0 = dt0 + cq * kQT;
-      const bool skip = ts >= S || d0 + kQT - 1 < ts + window ||
-                        (lookahead >= 0 && d0 > ts + 31 + window + lookahead);
-      if (!skip) {
+      if ((uint32_t)(d0 - skip_lo) <= (uint32_t)span) {
         const uint8_t* tile = qst(J) + tt * TILE;
         float lraw = lst(J)[wave * 64 + (TPS == 2 ? tt * 32 + col : lane)];
-        f32x16 acc;
+        f32x16 acc[KS];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+        for (int j = 0; j < KS; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
         // fragment reads in groups of FG, each group issued before one wait
         // (the next group's reads overlap this group's MFMAs)
         constexpr int FG = KVPOP_TGT_FRAG_GROUP;
@@ -361,53 +403,63 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KVPO
           if constexpr (FG == 8)
             asm volatile("" ::"v"(bu[0]), "v"(bu[1]), "v"(bu[2]), "v"(bu[3]), "v"(bu[4]), "v"(bu[5]),
                          "v"(bu[6]), "v"(bu[7]), "v"(lraw));
-          else
+          else if constexpr (FG == 4)
             asm volatile("" ::"v"(bu[0]), "v"(bu[1]), "v"(bu[2]), "v"(bu[3]), "v"(lraw));
+          else
+            asm volatile("" ::"v"(bu[0]), "v"(bu[1]), "v"(lraw));
 #pragma unroll
           for (int s = 0; s < FG; ++s) {
             bf16x8 bq;
             __builtin_memcpy(&bq, &bu[s], 16);
-            acc = mfma32(ka[s0 + s], bq, acc);
+#pragma unroll
+            for (int j = 0; j < KS; ++j) acc[j] = mfma32(ka[j][s0 + s], bq, acc[j]);
           }
         }
         if constexpr (KVPOP_TGT_SETPRIO == 1) __builtin_amdgcn_s_setprio(0);
         if constexpr (KVPOP_TGT_SETPRIO == 2) __builtin_amdgcn_s_setprio(1);
         // squares inside the allowed region and the sequence need no test
-        const bool full = d0 >= ts + 31 + window && d0 + kQT <= S &&
-                          (lookahead < 0 || d0 + kQT - 1 <= ts + window + lookahead);
-        if (full) {
+        if ((uint32_t)(d0 - full_lo) <= (uint32_t)fspan) {
           const float nl2 = lraw * -kLog2e;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) macc[r] += fast_exp2(fmaf(acc[r], c, nl2));
+          for (int j = 0; j < KS; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) macc[j][r] += fast_exp2(fmaf(acc[j][r], c, nl2));
         } else {
           // queries past the sequence end get L = +inf, so their terms vanish
           const float L2 = d0 + col < S ? lraw * kLog2e : __builtin_inff();
-          // key row of register r is ts + 4*half + 8*(r/4) + r%4: the pair is
-          // allowed when base - (8*(r/4) + r%4) lies in [0, lookahead]
+          // key row of register r of sub-tile j is ts + 32 j + 4*half +
+          // 8*(r/4) + r%4: the pair is allowed when base - 32 j - (8*(r/4) +
+          // r%4) lies in [0, lookahead]
           const int base = d0 + col - ts - window - 4 * half;
-          if (lookahead < 0) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const float p = fast_exp2(fmaf(acc[r], c, -L2));
-              macc[r] += base >= 8 * (r >> 2) + (r & 3) ? p : 0.f;
-            }
-          } else {
+          for (int j = 0; j < KS; ++j) {
+            if (lookahead < 0) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int diff = base - (8 * (r >> 2) + (r & 3));
-              const float p = fast_exp2(fmaf(acc[r], c, -L2));
-              macc[r] += (unsigned)diff <= (unsigned)lookahead ? p : 0.f;
+              for (int r = 0; r < 16; ++r) {
+                const float p = fast_exp2(fmaf(acc[j][r], c, -L2));
+                macc[j][r] += base - 32 * j >= 8 * (r >> 2) + (r & 3) ? p : 0.f;
+              }
+            } else {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int diff = base - 32 * j - (8 * (r >> 2) + (r & 3));
+                const float p = fast_exp2(fmaf(acc[j][r], c, -L2));
+                macc[j][r] += (unsigned)diff <= (unsigned)lookahead ? p : 0.f;
+              }
             }
           }
         }
       }
-      if (PER_HEAD && (cq == nq - 1 || it == n_iter - 1)) {
+      if (PER_HEAD && (d0 + kQT == d_end || it == n_iter - 1)) {
         flush(cg);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) macc[r] = 0.f;
+        for (int j = 0; j < KS; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) macc[j][r] = 0.f;
       }
-      if (++cq == nq) {
-        cq = 0;
+      d0 += kQT;
+      if (d0 == d_end) {
+        d0 = dt0;
         ++cg;
       }
     }
@@ -560,26 +612,29 @@ static TargetGeom make_geometry(const AttnShape& s, const TargetPlan& p, int win
 // Resident workgroups of the transposed pass on the whole device (all its
 // variants for this head dim and wave count; the fewest, so a round of
 // shares never exceeds what runs at once).
+constexpr int kW128 = KVPOP_TGT_WAVES128, kKS128 = KVPOP_TGT_KSUB;
+
 static int target_slots(int D, int waves) {
-  static std::atomic<int> cached[64][2][2];
+  static std::atomic<int> cached[64][2];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  std::atomic<int>& slot = cached[dev][D == 128][waves == 8];
+  std::atomic<int>& slot = cached[dev][D == 128];
   int n = slot.load(std::memory_order_relaxed);
   if (n > 0) return n;
-  int per_cu = 16 / waves;  // fallback: four waves per SIMD
+  int per_cu = 0;
   auto occ = [&](const void* fn) {
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, 64 * waves, 0) == hipSuccess && nb > 0)
-      per_cu = std::min(per_cu == 16 / waves ? nb : per_cu, nb);
+      per_cu = per_cu == 0 ? nb : std::min(per_cu, nb);
   };
   if (D == 128) {
-    occ((const void*)future_target_kernel<128, false, 8>);
-    occ((const void*)future_target_kernel<128, true, 8>);
+    occ((const void*)future_target_kernel<128, false, kW128, kKS128>);
+    occ((const void*)future_target_kernel<128, true, kW128, kKS128>);
   } else {
-    occ((const void*)future_target_kernel<64, false, 4>);
-    occ((const void*)future_target_kernel<64, true, 4>);
+    occ((const void*)future_target_kernel<64, false, 4, 1>);
+    occ((const void*)future_target_kernel<64, true, 4, 1>);
   }
+  if (per_cu == 0) per_cu = std::max(1, 16 / waves);  // fallback: four waves per SIMD
   n = device_cu_count() * per_cu;
   slot.store(n, std::memory_order_relaxed);
   return n;
@@ -589,9 +644,11 @@ TargetPlan plan_target(const AttnShape& s, int window) {
   TargetPlan p;
   // a 32-query tile is D / 16 1 KB loads: one per wave of eight (D = 128)
   // or of four (D = 64); four-wave workgroups at D = 128 (128-key blocks)
-  // measured 16% slower on the 4k layer
-  p.waves = s.D == 64 ? 4 : 8;
-  p.key_block = 32 * p.waves;
+  // measured 16% slower on the 4k layer, and 64 keys per wave (two
+  // sub-tiles, four waves) 10% slower there and within 3% on a 32k layer
+  p.waves = s.D == 64 ? 4 : kW128;
+  p.ksub = s.D == 64 ? 1 : kKS128;
+  p.key_block = 32 * p.waves * p.ksub;
   p.n_kb = (s.S + p.key_block - 1) / p.key_block;
   const int G = s.Hq / s.Hkv;
   long long C = (long long)KVPOP_TGT_CHUNK_BYTES / ((long long)G * s.D * 2);
@@ -629,13 +686,14 @@ hipError_t launch_future_target(const AttnShape& s, const void* q, const void* k
   auto* kk = (const bf16_t*)k;
   if (geo.n_wg > 0) {
     dim3 grid(geo.n_wg), block(64 * p.waves);
-#define KVPOP_TARGET_LAUNCH(DD, PH, WW)                                                            \
-  hipLaunchKernelGGL((future_target_kernel<DD, PH, WW>), grid, block, 0, st, qq, kk, lse,          \
+#define KVPOP_TARGET_LAUNCH(DD, PH, WW, KS)                                                        \
+  hipLaunchKernelGGL((future_target_kernel<DD, PH, WW, KS>), grid, block, 0, st, qq, kk, lse,      \
                      workspace, run_start, s.Hq, s.Hkv, s.S, window, lookahead, c, geo)
     if (s.D == 128) {
-      if (per_head) { KVPOP_TARGET_LAUNCH(128, true, 8); } else { KVPOP_TARGET_LAUNCH(128, false, 8); }
+      if (per_head) { KVPOP_TARGET_LAUNCH(128, true, kW128, kKS128); }
+      else { KVPOP_TARGET_LAUNCH(128, false, kW128, kKS128); }
     } else {
-      if (per_head) { KVPOP_TARGET_LAUNCH(64, true, 4); } else { KVPOP_TARGET_LAUNCH(64, false, 4); }
+      if (per_head) { KVPOP_TARGET_LAUNCH(64, true, 4, 1); } else { KVPOP_TARGET_LAUNCH(64, false, 4, 1); }
     }
 #undef KVPOP_TARGET_LAUNCH
     hipError_t e = hipGetLastError();

@@ -75,8 +75,9 @@ hipError_t launch_running_topk(int B, int Hkv, int S, int n_sink, int window, in
 constexpr int kTgtMaxChunks = 64;
 
 struct TargetPlan {
-  int waves;      // waves per workgroup: 4 (128-key blocks) or 8 (256-key blocks)
-  int key_block;  // keys per key block (32 per wave)
+  int waves;      // waves per workgroup
+  int ksub;       // 32-key sub-tiles per wave
+  int key_block;  // keys per key block (32 x waves x ksub)
   int n_kb;       // key blocks per (b, KV head)
   int chunk;      // query positions per chunk (multiple of 32)
   int n_chunks;   // ceil(S / chunk) <= kTgtMaxChunks
