@@ -21,7 +21,12 @@
 //     with clamped rows.
 //   * Softmax statistics are kept per lane (a lane owns one query column and
 //     16 key rows of each 32-key sub-tile), in base 2 with the scale folded
-//     into one FMA; the two half-waves of a column merge at the end.
+//     into one FMA; the two half-waves of a column merge at the end.  A
+//     tile's terms are taken relative to the running maximum as it stands,
+//     and the maximum is only found again (and the sums rescaled) when some
+//     lane's terms would sum past 2^64 or it has none yet: a score a little
+//     past the maximum just gives a term above 1, so the common tile costs
+//     one FMA, one exp2 and one add per score and no max.
 //   * Causal rows grow with position, so when the launch holds too few row
 //     blocks to occupy the chip the key range of long rows is split into
 //     pieces of at most kmax keys; each piece writes a partial (max, sum) and
@@ -531,16 +536,13 @@ __global__ __launch_bounds__(kThreads, OUT ? kOutBlocks : KVPOP_FWD_MIN_BLOCKS) 
         }
     }
     if constexpr (OUT) {
-      // one running maximum per query column, shared by its two half-waves
-      float mx = -INFINITY;
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[sub][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mn = fmaxf(m, mx);
-      const float mc = mn > -INFINITY ? mn * c : 0.f;  // masked scores still give 0
-      const float alpha = fast_exp2(fmaf(m, c, -mc));   // 0 while nothing was kept
+      // Terms relative to the running maximum m (one per query column,
+      // shared by its two half-waves).  The maximum and the rescaling of the
+      // sums are only taken again when a tile's terms would not stay small
+      // (above 2^64 in some lane, or m not yet set: the sum is then inf or
+      // NaN; query columns past S do not count); otherwise a term above 1
+      // (a score past m) is kept as it is.
+      float mc = m * c;
       float ts = 0.f;
       bf16x8 pb[2][2];
 #pragma unroll
@@ -551,12 +553,33 @@ __global__ __launch_bounds__(kThreads, OUT ? kOutBlocks : KVPOP_FWD_MIN_BLOCKS) 
           ts += p;
           pb[sub][r >> 3][r & 7] = (__bf16)p;
         }
-      l = l * alpha + ts;
-      m = mn;
+      if (!__all(ts <= 0x1p64f || !valid)) {
+        float mx = -INFINITY;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+        for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[sub][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mn = fmaxf(m, mx);
+        mc = mn > -INFINITY ? mn * c : 0.f;              // masked scores still give 0
+        const float alpha = fast_exp2(fmaf(m, c, -mc));  // 0 while nothing was kept
+        ts = 0.f;
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float p = fast_exp2(fmaf(acc[sub][r], c, -mc));
+            ts += p;
+            pb[sub][r >> 3][r & 7] = (__bf16)p;
+          }
+        l *= alpha;
+        m = mn;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      }
+      l += ts;
       const uint8_t* vtile = vst(J);
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
@@ -568,20 +591,35 @@ __global__ __launch_bounds__(kThreads, OUT ? kOutBlocks : KVPOP_FWD_MIN_BLOCKS) 
                                                                          voff[sub][j])),
                               pb[sub][j], oacc[db]);
     } else {
-      float mx = m;
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[sub][r]);
-      if (mx > -INFINITY) {
-        const float mc = mx * c;
-        float ts = 0.f;
+      // terms relative to the running maximum m; the maximum is only taken
+      // again when the tile's terms would not stay small (as above; query
+      // columns past S never ask for it)
+      float ts = 0.f;
+      {
+        const float mc = m * c;
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
           for (int r = 0; r < 16; ++r) ts += fast_exp2(fmaf(acc[sub][r], c, -mc));
-        l = l * fast_exp2(fmaf(m, c, -mc)) + ts;
-        m = mx;
+      }
+      if (__all(ts <= 0x1p64f || !valid)) {
+        l += ts;
+      } else {
+        float mx = m;
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[sub][r]);
+        if (mx > -INFINITY) {
+          const float mc = mx * c;
+          ts = 0.f;
+#pragma unroll
+          for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) ts += fast_exp2(fmaf(acc[sub][r], c, -mc));
+          l = l * fast_exp2(fmaf(m, c, -mc)) + ts;
+          m = mx;
+        }
       }
     }
   };

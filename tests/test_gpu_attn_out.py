@@ -155,3 +155,54 @@ def test_full_size_sampled_rows(kv, wl, sparse):
     print(f"attention output at {w.name} sparse={sparse}", flush=True)
     _sampled_rows(kv, w, seed=77 if wl == "qwen4b" else 78, n_rows=24 if wl == "qwen4b" else 12,
                   sparse=sparse)
+
+
+def _jump_inputs(seed):
+    """Queries and keys whose scores jump far past every earlier score of
+    their rows: rows d >= 256 of the first query head of each group align
+    with a direction u of their KV head, keys 300 and 301 carry 26 u (about
+    60 above the earlier maximum, so the pass has to take its maximum
+    again) and key 500 carries 34 u (about 18 above that: a term near e^18
+    that the pass keeps relative to the older maximum); key 700 carries 9 u,
+    below both."""
+    B, Hq, Hkv, S, D = 1, 4, 2, 1000, 128
+    G = Hq // Hkv
+    q = synth.normal((B, Hq, S, D), seed)
+    k = synth.normal((B, Hkv, S, D), seed + 1)
+    v = synth.normal((B, Hkv, S, D), seed + 2)
+    u = synth.normal((Hkv, D), seed + 3)
+    u = u / u.norm(dim=1, keepdim=True)
+    for h in range(Hkv):
+        q[0, h * G, 256:] += 26.0 * u[h]
+        for t, a in ((300, 26.0), (301, 26.0), (500, 34.0), (700, 9.0)):
+            k[0, h, t] = a * u[h] + 0.1 * k[0, h, t]
+    return synth.bf16(q), synth.bf16(k), synth.bf16(v)
+
+
+def test_score_jumps_full_parity(kv):
+    """Scores far above a row's earlier maximum (the pass takes the maximum
+    again) and moderately above it (the pass keeps terms above 1): LSE-only,
+    attention output and the sparse modes, every row against the oracle."""
+    q, k, v = _jump_inputs(seed=91)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    _, Hkv, S, _ = k.shape
+    sc = synth.scores((1, Hkv, S), seed=92, kind="normal")
+    n_sink, window, budget = 4, 32, 200
+    until, _ = oracle.running_topk(sc.numpy(), n_sink, window, budget)
+    ud = torch.from_numpy(until).cuda()
+    lse = kv.fwd_lse(qd, kd)
+    lse_o, o = kv.fwd_lse(qd, kd, v=vd)
+    lse_m = kv.fwd_lse_sparse(qd, kd, ud)
+    lse_l = kv.fwd_lse_sparse(qd, kd, ud, budget)
+    lse_mo, o_m = kv.fwd_lse_sparse(qd, kd, ud, 0, v=vd)
+    torch.cuda.synchronize()
+    oo, oa, ol = oracle.attn_out(f32(q), f32(k), f32(v))
+    assert ol.max() > 50.0  # the planted scores are there
+    assert_close(f32(lse), ol, LSE_ATOL, 0, "lse")
+    assert_close(f32(lse_o), ol, LSE_ATOL, 0, "lse with output")
+    _check_o(f32(o), oo, oa, False, "o")
+    so, sa, sl = oracle.attn_out(f32(q), f32(k), f32(v), sc.numpy(), n_sink, window, budget)
+    assert_close(f32(lse_m), sl, LSE_ATOL, 0, "sparse lse (every key tested)")
+    assert_close(f32(lse_l), sl, LSE_ATOL, 0, "sparse lse (listed keys)")
+    assert_close(f32(lse_mo), sl, LSE_ATOL, 0, "sparse lse with output")
+    _check_o(f32(o_m), so, sa, False, "sparse o")
