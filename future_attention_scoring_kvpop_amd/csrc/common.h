@@ -28,6 +28,25 @@ __device__ __forceinline__ uint4 ldg16(const void* p) {
 
 __device__ __forceinline__ void stg16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
 
+// 16-byte load with the non-temporal hint, for data that is streamed once
+// (a plain read of HBM with it ran at 7.1 TB/s on MI355X against 6.3-6.4
+// TB/s without).
+__device__ __forceinline__ uint4 ldg16_nt(const void* p) {
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
+__device__ __forceinline__ void stg16_nt(void* p, uint4 v) {
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  u32x4_t t;
+  t.x = v.x;
+  t.y = v.y;
+  t.z = v.z;
+  t.w = v.w;
+  __builtin_nontemporal_store(t, reinterpret_cast<u32x4_t*>(p));
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
