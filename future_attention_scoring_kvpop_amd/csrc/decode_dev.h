@@ -14,7 +14,9 @@
 //     four DPP adds inside the 16-lane row, so no LDS traffic in the loop.
 //   * Softmax in base 2 with the scale folded into q; each quarter-wave keeps
 //     an online (max, sum, o) state per head over blocks of 4 slots, and the
-//     16 states of a workgroup are merged once through LDS.  Splits are
+//     16 states of a workgroup are merged once through LDS.  The maximum is
+//     only taken again (and l, o rescaled) when a block's terms would sum
+//     past 2^64: a score a little past it just gives a term above 1.  Splits are
 //     merged by a second small kernel with the same log-sum-exp rule.
 //   * Each quarter-wave loads the next iteration's K/V rows before it
 //     computes the current one, so a wave always has a row block in flight.
@@ -145,7 +147,6 @@ __device__ __forceinline__ void decode_row(
 #pragma unroll
       for (int g = 0; g < GC; ++g) {
         float s[kNB];
-        float mx = m[g];
 #pragma unroll
         for (int i = 0; i < kNB; ++i) {
           float d = 0.f;
@@ -153,26 +154,41 @@ __device__ __forceinline__ void decode_row(
           for (int f = 0; f < FPL; ++f) d = fmaf(qv[g][f], kf[i][f], d);
           d = row16_sum(d);
           s[i] = ok[i] ? d : -INFINITY;
-          mx = fmaxf(mx, s[i]);
         }
-        if (mx > -INFINITY) {
-          const float alpha = fast_exp2(m[g] - mx);
-          float psum = 0.f;
-          float p[kNB];
+        // Terms relative to the running maximum as it stands; the maximum
+        // and the rescaling of l and o are only taken again when some
+        // lane's terms would sum past 2^64 or it has no maximum yet (the
+        // sum is then inf or NaN).
+        float p[kNB], psum = 0.f;
+#pragma unroll
+        for (int i = 0; i < kNB; ++i) {
+          p[i] = fast_exp2(s[i] - m[g]);
+          psum += p[i];
+        }
+        if (!__all(psum <= 0x1p64f)) {
+          float mx = m[g];
+#pragma unroll
+          for (int i = 0; i < kNB; ++i) mx = fmaxf(mx, s[i]);
+          const float alpha = mx > -INFINITY ? fast_exp2(m[g] - mx) : 1.f;
+          const float ms = mx > -INFINITY ? mx : 0.f;  // masked slots still give 0
+          psum = 0.f;
 #pragma unroll
           for (int i = 0; i < kNB; ++i) {
-            p[i] = fast_exp2(s[i] - mx);
+            p[i] = fast_exp2(s[i] - ms);
             psum += p[i];
           }
-          l[g] = fmaf(l[g], alpha, psum);
+          l[g] *= alpha;
 #pragma unroll
-          for (int f = 0; f < FPL; ++f) {
-            float acc = o[g][f] * alpha;
-#pragma unroll
-            for (int i = 0; i < kNB; ++i) acc = fmaf(p[i], vf[i][f], acc);
-            o[g][f] = acc;
-          }
+          for (int f = 0; f < FPL; ++f) o[g][f] *= alpha;
           m[g] = mx;
+        }
+        l[g] += psum;
+#pragma unroll
+        for (int f = 0; f < FPL; ++f) {
+          float acc = o[g][f];
+#pragma unroll
+          for (int i = 0; i < kNB; ++i) acc = fmaf(p[i], vf[i][f], acc);
+          o[g][f] = acc;
         }
       }
     }

@@ -46,6 +46,33 @@ def test_decode_attend_parity(kv, B, Hq, Hkv, n, D):
     assert_close(f32(ob), oo, O_ATOL, O_RTOL + 2.0 ** -8, "o bf16")
 
 
+@pytest.mark.parametrize("n", [1000, 4096])
+def test_decode_attend_score_jumps(kv, n):
+    """Slots whose scores rise far past every earlier slot's (the kernel has
+    to take its maximum again) and a little past it (terms above 1 kept as
+    they are), over a short and a long row."""
+    B, Hq, Hkv, D = 2, 8, 2, 128
+    G = Hq // Hkv
+    kc, vc, sp = _cache(B, Hkv, n, D, seed=n + 7, empty_frac=0.1)
+    q = synth.normal((B, Hq, D), n + 8)
+    u = synth.normal((B, Hkv, D), n + 9)
+    u = u / u.norm(dim=-1, keepdim=True)
+    kf = kc.float()
+    for b in range(B):
+        for h in range(Hkv):
+            q[b, h * G:(h + 1) * G] += 20.0 * u[b, h]
+            for j, a in ((n // 3, 30.0), (n // 3 + 70, 30.0), (2 * n // 3, 38.0), (n - 5, 10.0)):
+                kf[b, h, j] = a * u[b, h]
+                sp[b, h, j] = j
+    kc, q = synth.bf16(kf), synth.bf16(q)
+    o, lse = kv.decode_attend(q.cuda(), kc.cuda(), vc.cuda(), sp.cuda())
+    torch.cuda.synchronize()
+    oo, ol = oracle.decode_attend(f32(q), f32(kc), f32(vc), sp.numpy())
+    assert ol.max() > 50.0  # the planted scores are there
+    assert_close(f32(o), oo, O_ATOL, O_RTOL, "o")
+    assert_close(f32(lse), ol, 1e-4, 0, "lse")
+
+
 def test_decode_workload_shape_and_empty_rows(kv):
     """64 sequences x 32/8 heads over 4096 slots, one row fully empty."""
     B, Hq, Hkv, n, D = 64, 32, 8, 4096, 128
