@@ -274,12 +274,11 @@ kvpop_status kvpop_evict_select(int batch, int n_kv_heads, int seq_len, int head
       return KVPOP_ERR_INVALID_ARGUMENT;
   }
   if ((double)seq_len + budget > 2.0e9) return KVPOP_ERR_UNSUPPORTED;
-  hipError_t e = kvpop::launch_select(batch, n_kv_heads, seq_len, n_sink, window, budget, scores,
-                                      slot_pos, slot_score, stream);
-  if (e != hipSuccess) return KVPOP_ERR_DEVICE;
-  if (k)
-    e = kvpop::launch_gather(batch, n_kv_heads, seq_len, head_dim, budget, slot_pos, k, v,
-                             k_cache, v_cache, stream);
+  const hipError_t e =
+      k ? kvpop::launch_select_gather(batch, n_kv_heads, seq_len, head_dim, n_sink, window, budget,
+                                      scores, slot_pos, slot_score, k, v, k_cache, v_cache, stream)
+        : kvpop::launch_select(batch, n_kv_heads, seq_len, n_sink, window, budget, scores, slot_pos,
+                               slot_score, stream);
   return from_hip(e);
 }
 

@@ -256,15 +256,25 @@ future_target_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   }
 
   // Fetch state: the group row (head * S + query position) of the next tile
-  // to fetch, and its head and tile in the run; a head's tiles end hstep
-  // rows before the next head's first tile.
-  int ig = off / nq;
-  int iq = off - ig * nq;
+  // to fetch and the row at which its head's tiles end (fend); the next
+  // head's first tile is hstep rows further.  Past the last head the rows
+  // run on into the range's end, which reads as zero (never computed).
+  const int ig = off / nq;
+  const int iq = off - ig * nq;
   const int hstep = S - kQT * nq;
+  const int d_end = dt0 + kQT * nq;
   int frow = ig * S + dt0 + iq * kQT;
+  int fend = ig * S + d_end;
+  auto next_row = [&](int r) {
+    r += kQT;
+    if (r == fend) {
+      r += hstep;
+      fend += S;
+    }
+    return r;
+  };
   // Compute state: first query position d0 of the tile being computed and
   // its head (cg); a head's tiles end at d_end.
-  const int d_end = dt0 + kQT * nq;
   int d0 = dt0 + iq * kQT, cg = ig;
   // This wave's tiles by d0 (wave-uniform): a tile has allowed pairs when
   // d0 - skip_lo lies in [0, span] (none when the wave's keys start past S)
@@ -283,13 +293,12 @@ future_target_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   }
 
   // DMA of the stage's tiles (the next to fetch and the one after) into
-  // stage J, then advance past them.  Query-row DMA I fetches tile I / NQI;
-  // past the last tile of the group the stage's first tile is fetched again
-  // (never computed).
+  // stage J, then advance past them.  Query-row DMA I fetches tile I / NQI.
   auto issue = [&](auto J) {
     int rows[2];
     rows[0] = frow;
-    rows[1] = iq + 1 < nq ? frow + kQT : ig + 1 < G ? frow + kQT + hstep : frow;
+    rows[1] = TPS == 2 ? next_row(frow) : frow;
+    frow = next_row(rows[TPS - 1]);
     // each lane fetches one 16-byte chunk of a query row; chunks are
     // XOR-swizzled by row in LDS, so the lane holds logical chunk pc ^ row
     // Buffer loads: a query row DMA is the group's range plus this lane's
@@ -308,15 +317,6 @@ future_target_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       const uint32_t l0 = (uint32_t)rows[0] * 4u;
       const uint32_t l1 = TPS == 2 ? (uint32_t)rows[1] * 4u : l0;
       bdma4(rl, (half ? l1 : l0) + col4, lst(J) + wave * 64);
-    }
-#pragma unroll
-    for (int t = 0; t < TPS; ++t) {
-      frow += kQT;
-      if (++iq == nq) {
-        iq = 0;
-        ++ig;
-        frow += hstep;
-      }
     }
   };
 

@@ -127,6 +127,10 @@ hipError_t launch_select(int B, int Hkv, int S, int n_sink, int window, int budg
                          hipStream_t st);
 hipError_t launch_gather(int B, int Hkv, int S, int D, int budget, const int32_t* slot_pos,
                          const void* k, const void* v, void* kc, void* vc, hipStream_t st);
+// selection and compaction (fused into one launch when the rows are few)
+hipError_t launch_select_gather(int B, int Hkv, int S, int D, int n_sink, int window, int budget,
+                                const float* scores, int32_t* slot_pos, float* slot_score,
+                                const void* k, const void* v, void* kc, void* vc, hipStream_t st);
 
 // ---- decode ----
 struct DecodePlan {

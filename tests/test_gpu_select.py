@@ -46,7 +46,7 @@ KINDS = ["normal", "ties", "special", "const", "ramp", "nan"]
 def test_workload_shapes(kv, kind, name):
     w = synth.WORKLOADS[name]
     scores = synth.scores((w.B, w.Hkv, w.S), seed=100 * KINDS.index(kind) + len(name), kind=kind)
-    _compare(kv, scores, w.n_sink, w.window, w.budget, D=w.D if name != "qwen3-8b-prefill" else 0)
+    _compare(kv, scores, w.n_sink, w.window, w.budget, D=w.D)
 
 
 @pytest.mark.parametrize("kind", ["normal", "ties", "special"])
@@ -69,6 +69,19 @@ def test_edges(kv, S, s, w, budget):
     for kind in ("normal", "ties", "special", "nan", "const"):
         scores = synth.scores((2, 3, S), seed=S + budget, kind=kind)
         _compare(kv, scores, s, w, budget, D=128 if S < 10000 else 0, seed=S)
+
+
+@pytest.mark.parametrize("B,Hkv,S,s,w,budget,D", [(24, 8, 2000, 4, 64, 300, 64),
+                                                   (40, 8, 700, 2, 16, 100, 128),
+                                                   (1, 1, 5000, 4, 128, 1024, 128),
+                                                   (1, 2, 33000, 4, 256, 8192, 64)])
+def test_many_and_few_rows_with_compaction(kv, B, Hkv, S, s, w, budget, D):
+    """Selection with compaction when the rows are many (one workgroup per
+    row, compaction in a second launch) and few (every row selected by
+    several workgroups, each compacting a share of its slots)."""
+    for kind in ("normal", "ties"):
+        scores = synth.scores((B, Hkv, S), seed=B + S + budget, kind=kind)
+        _compare(kv, scores, s, w, budget, D=D, seed=S)
 
 
 def test_deterministic(kv):
