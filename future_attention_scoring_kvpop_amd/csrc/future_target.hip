@@ -255,24 +255,25 @@ future_target_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     bare_barrier();
   }
 
-  // Fetch state: the group row (head * S + query position) of the next tile
-  // to fetch and the row at which its head's tiles end (fend); the next
-  // head's first tile is hstep rows further.  Past the last head the rows
-  // run on into the range's end, which reads as zero (never computed).
+  // Fetch state: the stage to fetch next (fst), and a table of the group
+  // rows (head * S + query position) of the tiles of 64 stages, lane l
+  // holding stage tb + l's (rows past the group read as zero and are never
+  // computed); refilled every 64 stages, so a stage's rows cost one
+  // v_readlane each.
   const int ig = off / nq;
   const int iq = off - ig * nq;
-  const int hstep = S - kQT * nq;
   const int d_end = dt0 + kQT * nq;
-  int frow = ig * S + dt0 + iq * kQT;
-  int fend = ig * S + d_end;
-  auto next_row = [&](int r) {
-    r += kQT;
-    if (r == fend) {
-      r += hstep;
-      fend += S;
+  int fst = 0, tb = 0;
+  int trow[TPS];
+  auto fill_rows = [&]() {
+#pragma unroll
+    for (int tt = 0; tt < TPS; ++tt) {
+      const int x = off + TPS * (tb + lane) + tt;  // tile of the run
+      const int hx = x / nq;
+      trow[tt] = min(hx * S + dt0 + (x - hx * nq) * kQT, G * S);
     }
-    return r;
   };
+  fill_rows();
   // Compute state: first query position d0 of the tile being computed and
   // its head (cg); a head's tiles end at d_end.
   int d0 = dt0 + iq * kQT, cg = ig;
@@ -280,6 +281,7 @@ future_target_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   // d0 - skip_lo lies in [0, span] (none when the wave's keys start past S)
   // and needs no mask when d0 - full_lo lies in [0, fspan].
   constexpr int kFar = 1 << 29;
+  const uint32_t la = lookahead < 0 ? 0x7fffffffu : (uint32_t)lookahead;
   int skip_lo = ts + window - (kQT - 1), span = lookahead < 0 ? kFar : 32 * KS + 30 + lookahead;
   if (ts >= S) {
     skip_lo = kFar;
@@ -295,10 +297,14 @@ future_target_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   // DMA of the stage's tiles (the next to fetch and the one after) into
   // stage J, then advance past them.  Query-row DMA I fetches tile I / NQI.
   auto issue = [&](auto J) {
+    if (fst - tb == 64) {
+      tb = fst;
+      fill_rows();
+    }
     int rows[2];
-    rows[0] = frow;
-    rows[1] = TPS == 2 ? next_row(frow) : frow;
-    frow = next_row(rows[TPS - 1]);
+    rows[0] = __builtin_amdgcn_readlane(trow[0], fst - tb);
+    rows[1] = TPS == 2 ? __builtin_amdgcn_readlane(trow[TPS - 1], fst - tb) : rows[0];
+    ++fst;
     // each lane fetches one 16-byte chunk of a query row; chunks are
     // XOR-swizzled by row in LDS, so the lane holds logical chunk pc ^ row
     // Buffer loads: a query row DMA is the group's range plus this lane's
@@ -366,21 +372,23 @@ future_target_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 
   // One step on local stage `si`, which lives in ring slot J; the slot of
   // stage si-1 (J-1 mod kStages) is refilled with stage si+kStages-1.
-  auto step = [&](auto J, int si) {
+  // the last stage holds one tile when the segment's count is odd
+  const int odd = TPS == 2 ? (n_iter & 1) : 0;
+  auto step = [&](auto J, int left) {
     constexpr int j = decltype(J)::value;
     constexpr int jn = (j + kStages - 1) % kStages;
-    // stages issued after this one: min(kStages - 2, n_st - 1 - si)
-    const int later = min(kStages - 2, n_st - 1 - si);
-    if (later >= kStages - 2) wait_vmcnt<PT * (kStages - 2)>();
-    else if (kStages == 4 && later == 1) wait_vmcnt<PT>();
+    // left = stages after this one; min(kStages - 2, left) of them are
+    // already issued
+    if (left >= kStages - 2) wait_vmcnt<PT * (kStages - 2)>();
+    else if (kStages == 4 && left == 1) wait_vmcnt<PT>();
     else wait_vmcnt<0>();
     wait_lgkmcnt0();  // this wave's reads of earlier stages have completed
-    bare_barrier();   // stage si is in LDS for every wave; stage si-1's slot is free
-    if (si + kStages - 1 < n_st) issue(std::integral_constant<int, jn>{});
+    bare_barrier();   // this stage is in LDS for every wave; the previous one's slot is free
+    if (left >= kStages - 1) issue(std::integral_constant<int, jn>{});
 #pragma unroll
     for (int tt = 0; tt < TPS; ++tt) {
-      const int it = si * TPS + tt;
-      if (it >= n_iter) break;
+      if (tt > 0 && left < odd) break;  // a stage holds at least one tile
+      const int it = (n_st - 1 - left) * TPS + tt;
       if ((uint32_t)(d0 - skip_lo) <= (uint32_t)span) {
         const uint8_t* tile = qst(J) + tt * TILE;
         float lraw = lst(J)[wave * 64 + (TPS == 2 ? tt * 32 + col : lane)];
@@ -417,38 +425,29 @@ future_target_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         }
         if constexpr (KVPOP_TGT_SETPRIO == 1) __builtin_amdgcn_s_setprio(0);
         if constexpr (KVPOP_TGT_SETPRIO == 2) __builtin_amdgcn_s_setprio(1);
-        // squares inside the allowed region and the sequence need no test
-        if ((uint32_t)(d0 - full_lo) <= (uint32_t)fspan) {
-          const float nl2 = lraw * -kLog2e;
+        // Squares inside the allowed region and the sequence need no test.
+        // Others first set their disallowed pairs to -inf and their queries
+        // past S to L = +inf; then every square takes one FMA, one exp2 and
+        // one add per pair (a branch around the masking, no two-way split).
+        float nl2 = lraw * -kLog2e;
+        if ((uint32_t)(d0 - full_lo) > (uint32_t)fspan) {
+          if (d0 + col >= S) nl2 = -__builtin_inff();
+          // key row of register r of sub-tile j is ts + 32 j + 4*half +
+          // 8*(r/4) + r%4: the pair is allowed when base - 32 j - (8*(r/4) +
+          // r%4) lies in [0, la] (la = 2^31 - 1 without a lookahead)
+          const int base = d0 + col - ts - window - 4 * half;
 #pragma unroll
           for (int j = 0; j < KS; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) macc[j][r] += fast_exp2(fmaf(acc[j][r], c, nl2));
-        } else {
-          // queries past the sequence end get L = +inf, so their terms vanish
-          const float L2 = d0 + col < S ? lraw * kLog2e : __builtin_inff();
-          // key row of register r of sub-tile j is ts + 32 j + 4*half +
-          // 8*(r/4) + r%4: the pair is allowed when base - 32 j - (8*(r/4) +
-          // r%4) lies in [0, lookahead]
-          const int base = d0 + col - ts - window - 4 * half;
-#pragma unroll
-          for (int j = 0; j < KS; ++j) {
-            if (lookahead < 0) {
-#pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                const float p = fast_exp2(fmaf(acc[j][r], c, -L2));
-                macc[j][r] += base - 32 * j >= 8 * (r >> 2) + (r & 3) ? p : 0.f;
-              }
-            } else {
-#pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                const int diff = base - 32 * j - (8 * (r >> 2) + (r & 3));
-                const float p = fast_exp2(fmaf(acc[j][r], c, -L2));
-                macc[j][r] += (unsigned)diff <= (unsigned)lookahead ? p : 0.f;
-              }
+            for (int r = 0; r < 16; ++r) {
+              const int diff = base - 32 * j - (8 * (r >> 2) + (r & 3));
+              acc[j][r] = (uint32_t)diff <= la ? acc[j][r] : -__builtin_inff();
             }
-          }
         }
+#pragma unroll
+        for (int j = 0; j < KS; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) macc[j][r] += fast_exp2(fmaf(acc[j][r], c, nl2));
       }
       if (PER_HEAD && (d0 + kQT == d_end || it == n_iter - 1)) {
         flush(cg);
@@ -465,11 +464,11 @@ future_target_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     }
   };
 
-  for (int si = 0; si < n_st; si += kStages) {
-    step(I0{}, si);
-    if (si + 1 < n_st) step(I1{}, si + 1);
-    if (kStages > 2 && si + 2 < n_st) step(I2{}, si + 2);
-    if (kStages > 3 && si + 3 < n_st) step(I3{}, si + 3);
+  for (int left = n_st - 1; left >= 0; left -= kStages) {
+    step(I0{}, left);
+    if (left >= 1) step(I1{}, left - 1);
+    if (kStages > 2 && left >= 2) step(I2{}, left - 2);
+    if (kStages > 3 && left >= 3) step(I3{}, left - 3);
   }
   if (!PER_HEAD) flush(0);
 
