@@ -79,7 +79,6 @@ __device__ __forceinline__ void mlstm_row(
     const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, const MlstmWeights& wt,
     float* __restrict__ state, float* __restrict__ slot_score) {
   constexpr int X = 2 * D;           // input length
-  constexpr int XPL = X / 64;        // inputs per lane
   constexpr int NOUT = kP + kE + 2;  // projections of the entering token
   __shared__ float xs[X], xu[X];
   __shared__ float proj[NOUT + kP];  // zk, val, ig, fg, zr
