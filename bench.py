@@ -44,32 +44,32 @@ FP32_VECTOR_PEAK_TFS = 157.3     # MI355X fp32 vector (counts packed FMA; one FM
 # only for the kernel code it was taken on (sources_digest): bench reports
 # null once that changes.
 TRAFFIC_SOURCES = ("future_target.hip", "common.h", "launch.h")
-TRAFFIC = {"sha256": "4542a3bf544551a30468d807beb3b381cb2c8800097f79c1c5808cde80b73395",
-           "fetch_bytes": 2 * (412533.8 + 4319.0) * 1024, "write_bytes": (8576.0 + 1024.0) * 1024}
+TRAFFIC = {"sha256": "ff446841d2a9b05e39f23c2d273b43b3e6c7d014c94552f771d48184f9f6c0ed",
+           "fetch_bytes": 2 * (411734.2 + 4319.0) * 1024, "write_bytes": (8576.0 + 1024.0) * 1024}
 # HBM bytes per dispatch of the HBM-bound kernels the bench reports, from the
 # same pair of counter runs with the same scaling (FETCH_SIZE x 2, WRITE_SIZE
 # x 1), each valid only for the sources it was taken on.
 COUNTERS = {
     "decode_step": {"sources": ("decode_step.hip", "decode_dev.h", "cache_step_dev.h", "mlstm_dev.h",
                                 "common.h", "launch.h"),
-                    "fetch_kib": 536897.4, "write_kib": 825.4,
+                    "fetch_kib": 532938.0, "write_kib": 824.3,
                     "per": "decode_step_kernel<128, 4> launch: one layer-step of 64 sequences x 8 KV "
                            "heads over budget 4096"},
-    "select_prefill": {"sources": ("select.hip", "common.h", "launch.h"),
-                       "fetch_kib": 661.4, "write_kib": 512.0,
-                       "per": "select_kernel<32, true> launch: 8 rows of 32768 scores, budget 8192"},
-    "gather_prefill": {"sources": ("select.hip", "common.h", "launch.h"),
-                       "fetch_kib": 16659.6, "write_kib": 32768.0,
-                       "per": "gather_kernel launch: 8 rows x 8192 slots of K and V"},
+    "select_gather_prefill": {"sources": ("select.hip", "common.h", "launch.h"),
+                              "fetch_kib": 20619.7, "write_kib": 33281.2,
+                              "per": "select_kernel<32, true, true> launch: 8 rows of 32768 scores, "
+                                     "budget 8192, selection and compaction of K and V (32 "
+                                     "workgroups per row)"},
     "select_decode_prefix": {"sources": ("select.hip", "common.h", "launch.h"),
-                             "fetch_kib": 32917.9, "write_kib": 16416.0,
-                             "per": "select_kernel<32, true> launch: 512 rows of 32768 scores, budget 4096"},
+                             "fetch_kib": 32919.4, "write_kib": 16416.0,
+                             "per": "select_kernel<32, true, false> launch: 512 rows of 32768 scores, "
+                                    "budget 4096"},
     "gather_decode_prefix": {"sources": ("select.hip", "common.h", "launch.h"),
-                             "fetch_kib": 532510.7, "write_kib": 1048576.0,
+                             "fetch_kib": 532514.9, "write_kib": 1048659.8,
                              "per": "gather_kernel launch: 512 rows x 4096 slots of K and V"},
 }
-COUNTER_SHA = {"decode": "95e66b3167c19803ca5bc2e0454642ac23c1d242e0701da31d75f1e3e2ae4434",
-               "select": "6d37a8f69e6991588cc2e0d7e53997806efc2dc28d72af9e8731aefffff6f48b"}
+COUNTER_SHA = {"decode": "b99fdf6ad3417f726cdde4ed792957dd0ab5e097189e64c3800b046820eb6bc8",
+               "select": "17e13c3ed9187a5552e1d9b1aa4cf0b5d259330cd7293785bce5de1b38d43288"}
 METRIC = "future-attn target keys/s + MFMA util; bounded-cache decode steps/s + HBM util"
 
 
@@ -275,8 +275,8 @@ def bench_prefill_step(kv, w, steps, warmup):
            "select_gather": {"bytes": sg_bytes, "achieved": sg_bytes / (t_sel / 1e3) / 1e9,
                              "unit": "GB/s",
                              "frac": sg_bytes / (t_sel / 1e3) / 1e9 / HBM_PEAK_GBS,
-                             "counters": _pair_counters("select_prefill", "gather_prefill", t_sel),
-                             "note": "8 rows: bound by the latency of one workgroup per row"},
+                             "counters": _one_counter("select_gather_prefill", t_sel),
+                             "note": "8 rows: bound by the latency of a row's selection"},
            "decode_step": {"ms": t_dec, "sequences": w.B, "slots": w.budget,
                            "entry_point": "kvpop_decode_step"}}
     del st
@@ -630,6 +630,15 @@ def decode_bytes_per_step(w, layers):
     exit_copy = units * 2 * 2 * w.D * 2
     qo = w.B * layers * w.Hq * w.D * 2 * 2
     return cache + append + exit_copy + qo
+
+
+def _one_counter(a, ms):
+    """Counter bytes of one kernel launched once per `ms`."""
+    ba = counter_bytes(a)
+    if ba is None:
+        return None
+    gbs = ba / (ms / 1e3) / 1e9
+    return {"bytes": ba, "achieved": gbs, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS}
 
 
 def _pair_counters(a, b, ms):
