@@ -96,17 +96,19 @@ namespace {
 #ifndef KVPOP_TGT_WPE
 #define KVPOP_TGT_WPE 4
 #endif
-// D = 128: 32-key sub-tiles per wave (1: 32 keys per wave; 2: 64 keys, so
-// each query fragment read from LDS feeds two MFMAs) and waves per workgroup
-#ifndef KVPOP_TGT_KSUB
-#define KVPOP_TGT_KSUB 1
+// D = 128 keeps 256-key blocks in two shapes: eight waves of one 32-key
+// sub-tile (launches that split the list evenly), and, with this set, four
+// waves of two sub-tiles for launches with one run per workgroup (each
+// query fragment read from LDS then feeds two MFMA chains: 2.2% faster on
+// a 32k layer and on the skewed 16k batch, 10% slower on the 4k layer's
+// even split)
+#ifndef KVPOP_TGT_WIDE_ITEMS
+#define KVPOP_TGT_WIDE_ITEMS 1
 #endif
-#ifndef KVPOP_TGT_WAVES128
-#define KVPOP_TGT_WAVES128 8
-#endif
-// waves per SIMD of the two-sub-tile kernel (its keys take 64 registers)
+// waves per SIMD of the two-sub-tile kernel (its keys take 64 registers;
+// three spill)
 #ifndef KVPOP_TGT_WPE_KS2
-#define KVPOP_TGT_WPE_KS2 3
+#define KVPOP_TGT_WPE_KS2 2
 #endif
 // wave priority raised around a tile's MFMA burst (1; ~2% faster than 0:
 // the arbiter then feeds the matrix core first while other waves of the
@@ -608,12 +610,14 @@ static TargetGeom make_geometry(const AttnShape& s, const TargetPlan& p, int win
   return g;
 }
 
-// Resident workgroups of the transposed pass on the whole device (all its
-// variants for this head dim and wave count; the fewest, so a round of
-// shares never exceeds what runs at once).
-constexpr int kW128 = KVPOP_TGT_WAVES128, kKS128 = KVPOP_TGT_KSUB;
+// The D = 128 shapes: eight waves x one sub-tile, four waves x two.
+constexpr int kW128 = 8, kKS128 = 1, kWideW = 4, kWideKS = 2;
+static_assert(32 * kW128 * kKS128 == 32 * kWideW * kWideKS, "both shapes share the key block");
 
-static int target_slots(int D, int waves) {
+// Resident workgroups of the transposed pass on the whole device (all its
+// variants for this head dim; the fewest, so a round of shares never
+// exceeds what runs at once).
+static int target_slots(int D) {
   static std::atomic<int> cached[64][2];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
@@ -621,19 +625,23 @@ static int target_slots(int D, int waves) {
   int n = slot.load(std::memory_order_relaxed);
   if (n > 0) return n;
   int per_cu = 0;
-  auto occ = [&](const void* fn) {
+  auto occ = [&](const void* fn, int waves) {
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, 64 * waves, 0) == hipSuccess && nb > 0)
       per_cu = per_cu == 0 ? nb : std::min(per_cu, nb);
   };
   if (D == 128) {
-    occ((const void*)future_target_kernel<128, false, kW128, kKS128>);
-    occ((const void*)future_target_kernel<128, true, kW128, kKS128>);
+    occ((const void*)future_target_kernel<128, false, kW128, kKS128>, kW128);
+    occ((const void*)future_target_kernel<128, true, kW128, kKS128>, kW128);
+    if (KVPOP_TGT_WIDE_ITEMS) {
+      occ((const void*)future_target_kernel<128, false, kWideW, kWideKS>, kWideW);
+      occ((const void*)future_target_kernel<128, true, kWideW, kWideKS>, kWideW);
+    }
   } else {
-    occ((const void*)future_target_kernel<64, false, 4, 1>);
-    occ((const void*)future_target_kernel<64, true, 4, 1>);
+    occ((const void*)future_target_kernel<64, false, 4, 1>, 4);
+    occ((const void*)future_target_kernel<64, true, 4, 1>, 4);
   }
-  if (per_cu == 0) per_cu = std::max(1, 16 / waves);  // fallback: four waves per SIMD
+  if (per_cu == 0) per_cu = D == 128 ? 2 : 4;  // fallback: four waves per SIMD
   n = device_cu_count() * per_cu;
   slot.store(n, std::memory_order_relaxed);
   return n;
@@ -642,9 +650,10 @@ static int target_slots(int D, int waves) {
 TargetPlan plan_target(const AttnShape& s, int window) {
   TargetPlan p;
   // a 32-query tile is D / 16 1 KB loads: one per wave of eight (D = 128)
-  // or of four (D = 64); four-wave workgroups at D = 128 (128-key blocks)
-  // measured 16% slower on the 4k layer, and 64 keys per wave (two
-  // sub-tiles, four waves) 10% slower there and within 3% on a 32k layer
+  // or of four (D = 64); four-wave workgroups of 32 keys per wave at
+  // D = 128 (128-key blocks) measured 16% slower on the 4k layer.  The
+  // plan's shape is the even split's (the wide shape has the same key
+  // block and, at two workgroups per CU, the same slots).
   p.waves = s.D == 64 ? 4 : kW128;
   p.ksub = s.D == 64 ? 1 : kKS128;
   p.key_block = 32 * p.waves * p.ksub;
@@ -658,7 +667,7 @@ TargetPlan plan_target(const AttnShape& s, int window) {
   p.n_chunks = (int)((s.S + C - 1) / C);
   // the most workgroups any lookahead needs: a launch has at most rounds x
   // slots, and no lookahead gives the most squares and rounds
-  const int slots = target_slots(s.D, p.waves);
+  const int slots = target_slots(s.D);
   p.max_wg = make_geometry(s, p, window, -1, slots).rounds * slots;
   p.runs = (size_t)s.B * s.Hkv * p.n_chunks * p.n_kb;
   p.partial_floats = (p.runs * G + (size_t)p.max_wg) * p.key_block;
@@ -668,7 +677,7 @@ TargetPlan plan_target(const AttnShape& s, int window) {
 }
 
 TargetGeom target_geometry(const AttnShape& s, const TargetPlan& p, int window, int lookahead) {
-  return make_geometry(s, p, window, lookahead, target_slots(s.D, p.waves));
+  return make_geometry(s, p, window, lookahead, target_slots(s.D));
 }
 
 hipError_t launch_future_target(const AttnShape& s, const void* q, const void* k,
@@ -684,11 +693,14 @@ hipError_t launch_future_target(const AttnShape& s, const void* q, const void* k
   auto* qq = (const bf16_t*)q;
   auto* kk = (const bf16_t*)k;
   if (geo.n_wg > 0) {
-    dim3 grid(geo.n_wg), block(64 * p.waves);
+    const dim3 grid(geo.n_wg);
 #define KVPOP_TARGET_LAUNCH(DD, PH, WW, KS)                                                        \
-  hipLaunchKernelGGL((future_target_kernel<DD, PH, WW, KS>), grid, block, 0, st, qq, kk, lse,      \
-                     workspace, run_start, s.Hq, s.Hkv, s.S, window, lookahead, c, geo)
-    if (s.D == 128) {
+  hipLaunchKernelGGL((future_target_kernel<DD, PH, WW, KS>), grid, dim3(64 * WW), 0, st, qq, kk,   \
+                     lse, workspace, run_start, s.Hq, s.Hkv, s.S, window, lookahead, c, geo)
+    if (s.D == 128 && KVPOP_TGT_WIDE_ITEMS && geo.item_mode) {
+      if (per_head) { KVPOP_TARGET_LAUNCH(128, true, kWideW, kWideKS); }
+      else { KVPOP_TARGET_LAUNCH(128, false, kWideW, kWideKS); }
+    } else if (s.D == 128) {
       if (per_head) { KVPOP_TARGET_LAUNCH(128, true, kW128, kKS128); }
       else { KVPOP_TARGET_LAUNCH(128, false, kW128, kKS128); }
     } else {

@@ -162,10 +162,12 @@ def test_qwen8b_prefill_layer(kv):
 
 @pytest.mark.parametrize("wl,per_qhead", [("skewed", False), ("qwen8b", False), ("qwen8b", True)])
 def test_full_size_transposed_pass_sampled_keys(kv, wl, per_qhead):
-    """The transposed pass alone at full size, on one seeded normalizer array
-    handed to both sides: keys at the start (summed over every query chunk),
-    across a key-block boundary, mid-sequence and at the tail, for the first
-    and the last (b, KV head)."""
+    """The transposed pass alone at full size (one run per workgroup, four
+    waves of 64 keys), on one seeded normalizer array handed to both sides:
+    keys at the start (summed over every query chunk), across a key-block
+    boundary, one whole 256-key block (every wave and 32-key sub-tile of
+    it), mid-sequence and at the tail, for the first and the last (b, KV
+    head)."""
     w = synth.SKEWED if wl == "skewed" else synth.QWEN8B
     q, k, _ = synth.attention_inputs(w, seed=31, device="cuda")
     lse = synth.normalizers(w.B, w.Hq, w.S, seed=32).cuda()
@@ -174,6 +176,7 @@ def test_full_size_transposed_pass_sampled_keys(kv, wl, per_qhead):
     torch.cuda.synchronize()
     G = w.Hq // w.Hkv
     keys = np.concatenate([np.arange(0, 24), np.arange(1010, 1040), np.arange(w.S // 2 - 12, w.S // 2 + 12),
+                           np.arange(w.S // 4, w.S // 4 + 256),
                            np.arange(w.S - w.window - 24, w.S)]).astype(np.int64)
     lse_h = lse.cpu().numpy()
     for b, h in ((0, 0), (w.B - 1, w.Hkv - 1)):
