@@ -12,7 +12,9 @@
 //     workgroup for the whole group.
 //   * Each wave keeps 32 query rows resident as MFMA B fragments and streams
 //     64-key tiles of K as A fragments: v_mfma_f32_32x32x16_bf16 gives
-//     S^T[key][query].  K tiles reach LDS by direct buffer->LDS loads into a
+//     S^T[key][query].  Dense LSE-only launches of many rounds keep two
+//     groups of 32 query rows per wave instead (P = 256/G positions per
+//     workgroup), so each K fragment read from LDS feeds two MFMAs.  K tiles reach LDS by direct buffer->LDS loads into a
 //     ring of stages (one LDS object per stage, rows XOR-swizzled), requested
 //     one tile ahead; the register budget allows four workgroups per CU.
 //     A load's address is a 32-bit offset in the KV head's range (the
@@ -82,6 +84,17 @@ namespace {
 #endif
 #ifndef KVPOP_FWD_MIN_BLOCKS
 #define KVPOP_FWD_MIN_BLOCKS (16 / KVPOP_FWD_WAVES)
+#endif
+// Two query groups of 32 rows per wave (each K fragment read from LDS feeds
+// two MFMAs; 187 registers, two workgroups per CU) for dense D = 128
+// LSE-only launches of at least this many rounds of resident row blocks
+// (1 on, 0 off): 3.94-3.98 -> 3.66 ms on a 32k layer; the masked sparse
+// mode measured 1% slower with it and keeps one group
+#ifndef KVPOP_FWD_WIDE
+#define KVPOP_FWD_WIDE 1
+#endif
+#ifndef KVPOP_FWD_WIDE_ROUNDS
+#define KVPOP_FWD_WIDE_ROUNDS 4
 #endif
 // Row blocks below which long causal rows are split into pieces (only
 // launches that cannot occupy the chip gain from the extra merge).
@@ -228,8 +241,8 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const bf16_t* __restri
   }
 }
 
-template <int D, int MODE, bool OUT>
-__global__ __launch_bounds__(kThreads, OUT ? kOutBlocks : KVPOP_FWD_MIN_BLOCKS) void fwd_lse_kernel(
+template <int D, int MODE, bool OUT, int QG>
+__global__ __launch_bounds__(kThreads, OUT ? kOutBlocks : (QG == 2 ? 2 : KVPOP_FWD_MIN_BLOCKS)) void fwd_lse_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const int* __restrict__ keep_until,
     const int2* __restrict__ hdr, const int* __restrict__ lists, int cap, float* __restrict__ lse,
     float2* __restrict__ part, int B, int Hq, int Hkv, int S, float c, float scale, int n_pb,
@@ -238,6 +251,7 @@ __global__ __launch_bounds__(kThreads, OUT ? kOutBlocks : KVPOP_FWD_MIN_BLOCKS) 
   constexpr bool SPARSE = MODE != kDense;
   static_assert(MODE != kListed || kStages == 2, "the listed mode pairs list slots with stages");
   static_assert(!OUT || (MODE != kListed && kStages == 2), "the output mode: dense or masked, two stages");
+  static_assert(QG == 1 || (QG == 2 && !OUT && MODE != kListed), "two query groups: LSE-only, dense or masked");
   constexpr int NS = D / 16;           // MFMA k-slices
   constexpr int CPR = D / 8;           // 16-byte chunks per row
   constexpr int ROWB = D * 2;          // bytes per K row
@@ -279,7 +293,7 @@ __global__ __launch_bounds__(kThreads, OUT ? kOutBlocks : KVPOP_FWD_MIN_BLOCKS) 
   constexpr int DPS = LPW + (SPARSE ? 1 : 0) + (MODE == kListed ? 1 : 0) + VPW;
 
   const int G = Hq / Hkv;
-  const int P = kRows / G;
+  const int P = kRows * QG / G;
   // Blocks go round robin over the 8 XCDs and, within an XCD, over its CUs.
   // Each XCD takes a contiguous range of items (longest first).  When the
   // whole launch is resident at once (snake_cus = CUs per XCD, else 0), the
@@ -329,11 +343,19 @@ __global__ __launch_bounds__(kThreads, OUT ? kOutBlocks : KVPOP_FWD_MIN_BLOCKS) 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
-  const int ci = wave * 32 + col;
-  const int gl = ci / P;
-  const int dpos = p0 + (ci % P);
-  const bool valid = dpos < S;
-  const int g = h * G + gl;
+  // query group qg of the wave: 32 query rows (a lane's column is one of
+  // them), row wave * 32 * QG + 32 qg + col of the block's G x P rows
+  int dposq[QG], gq[QG];
+  bool validq[QG];
+#pragma unroll
+  for (int qg = 0; qg < QG; ++qg) {
+    const int ci = (wave * QG + qg) * 32 + col;
+    dposq[qg] = p0 + (ci % P);
+    validq[qg] = dposq[qg] < S;
+    gq[qg] = h * G + ci / P;
+  }
+  const int dpos = dposq[0], g = gq[0];
+  const bool valid = validq[0];
 
   const bf16_t* kbase = k + ((size_t)b * Hkv + h) * (size_t)S * D;
   const bf16_t* vtbase = OUT ? vt + ((size_t)b * Hkv + h) * (size_t)D * s_pad : nullptr;
@@ -396,11 +418,14 @@ __global__ __launch_bounds__(kThreads, OUT ? kOutBlocks : KVPOP_FWD_MIN_BLOCKS) 
     }
   };
 
-  bf16x8 bq[NS];
-  {
-    const bf16_t* qrow = q + (((size_t)b * Hq + g) * S + (valid ? dpos : 0)) * D + 8 * half;
+  bf16x8 bq[QG][NS];
 #pragma unroll
-    for (int s = 0; s < NS; ++s) bq[s] = as_bf16x8(valid ? ldg16(qrow + 16 * s) : make_uint4(0, 0, 0, 0));
+  for (int qg = 0; qg < QG; ++qg) {
+    const bf16_t* qrow =
+        q + (((size_t)b * Hq + gq[qg]) * S + (validq[qg] ? dposq[qg] : 0)) * D + 8 * half;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      bq[qg][s] = as_bf16x8(validq[qg] ? ldg16(qrow + 16 * s) : make_uint4(0, 0, 0, 0));
   }
 
   using I0 = std::integral_constant<int, 0>;
@@ -419,7 +444,14 @@ __global__ __launch_bounds__(kThreads, OUT ? kOutBlocks : KVPOP_FWD_MIN_BLOCKS) 
     if (2 < n_kt && kStages > 3) issue(I2{}, kt0 + 2);
   }
 
-  float m = -INFINITY, l = 0.f;
+  float mq[QG], lq[QG];
+#pragma unroll
+  for (int qg = 0; qg < QG; ++qg) {
+    mq[qg] = -INFINITY;
+    lq[qg] = 0.f;
+  }
+  float& m = mq[0];  // the output mode's (one query group)
+  float& l = lq[0];
   // A-fragment row of this lane within a 32-key sub-tile.  The output mode
   // swaps bits 2 and 3 of the row, so that result register r of half h holds
   // key 16 (r / 8) + 8 h + r % 8 (eight consecutive keys per 16-key slice,
@@ -465,16 +497,23 @@ __global__ __launch_bounds__(kThreads, OUT ? kOutBlocks : KVPOP_FWD_MIN_BLOCKS) 
     }
     const int t0 = (kt0 + i) * kKT;
     const uint8_t* tile = kst(J);
-    f32x16 acc[2];
+    // each K fragment read from LDS feeds the MFMAs of every query group
+    f32x16 accq[QG][2];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[sub][r] = 0.f;
+      for (int qg = 0; qg < QG; ++qg)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) accq[qg][sub][r] = 0.f;
       const uint8_t* sbase = tile + sub * 32 * ROWB;
 #pragma unroll
-      for (int s = 0; s < NS; ++s)
-        acc[sub] = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(sbase + foff[s])), bq[s], acc[sub]);
+      for (int s = 0; s < NS; ++s) {
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(sbase + foff[s]));
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg) accq[qg][sub] = mfma32(a, bq[qg][s], accq[qg][sub]);
+      }
     }
+    f32x16(&acc)[2] = accq[0];  // the listed and output modes' (one query group)
     if constexpr (MODE == kListed) {
       // key of register r: entry 32 sub + 8 (r/4) + 4 half + r%4 of the
       // tile's list; tiles before ft hold only keys retained for the block
@@ -500,6 +539,10 @@ __global__ __launch_bounds__(kThreads, OUT ? kOutBlocks : KVPOP_FWD_MIN_BLOCKS) 
       // keep_until values are four runs of four consecutive ints.  Below
       // the diagonal (and inside the piece) only keep_until can mask.
       const int* ut = ust(J) + wave * 64;
+#pragma unroll
+      for (int qg = 0; qg < QG; ++qg) {
+      f32x16(&acc)[2] = accq[qg];
+      const int dpos = dposq[qg];
       if (t0 + kKT - 1 > p0 || t0 + kKT > k_end) {  // diagonal, past S or past the piece
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub)
@@ -526,14 +569,17 @@ __global__ __launch_bounds__(kThreads, OUT ? kOutBlocks : KVPOP_FWD_MIN_BLOCKS) 
             acc[sub][4 * r4 + 3] = dpos >= u.w ? -INFINITY : acc[sub][4 * r4 + 3];
           }
       }
+      }
     } else if (t0 + kKT - 1 > p0 || t0 + kKT > k_end) {  // diagonal, past S or past the piece
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
+      for (int qg = 0; qg < QG; ++qg)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int t = t0 + kb4(sub, r >> 2) + (r & 3);
-          acc[sub][r] = ((t > dpos) | (t >= k_end)) ? -INFINITY : acc[sub][r];
-        }
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int t = t0 + kb4(sub, r >> 2) + (r & 3);
+            accq[qg][sub][r] = ((t > dposq[qg]) | (t >= k_end)) ? -INFINITY : accq[qg][sub][r];
+          }
     }
     if constexpr (OUT) {
       // Terms relative to the running maximum m (one per query column,
@@ -594,31 +640,39 @@ __global__ __launch_bounds__(kThreads, OUT ? kOutBlocks : KVPOP_FWD_MIN_BLOCKS) 
       // terms relative to the running maximum m; the maximum is only taken
       // again when the tile's terms would not stay small (as above; query
       // columns past S never ask for it)
-      float ts = 0.f;
-      {
-        const float mc = m * c;
+      float ts[QG];
+      bool small = true;
+#pragma unroll
+      for (int qg = 0; qg < QG; ++qg) {
+        const float mc = mq[qg] * c;
+        ts[qg] = 0.f;
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) ts += fast_exp2(fmaf(acc[sub][r], c, -mc));
+          for (int r = 0; r < 16; ++r) ts[qg] += fast_exp2(fmaf(accq[qg][sub][r], c, -mc));
+        small = small && (ts[qg] <= 0x1p64f || !validq[qg]);
       }
-      if (__all(ts <= 0x1p64f || !valid)) {
-        l += ts;
+      if (__all(small)) {
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg) lq[qg] += ts[qg];
       } else {
-        float mx = m;
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[sub][r]);
-        if (mx > -INFINITY) {
-          const float mc = mx * c;
-          ts = 0.f;
+        for (int qg = 0; qg < QG; ++qg) {
+          float mx = mq[qg];
 #pragma unroll
           for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) ts += fast_exp2(fmaf(acc[sub][r], c, -mc));
-          l = l * fast_exp2(fmaf(m, c, -mc)) + ts;
-          m = mx;
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, accq[qg][sub][r]);
+          if (mx > -INFINITY) {
+            const float mc = mx * c;
+            float t = 0.f;
+#pragma unroll
+            for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) t += fast_exp2(fmaf(accq[qg][sub][r], c, -mc));
+            lq[qg] = lq[qg] * fast_exp2(fmaf(mq[qg], c, -mc)) + t;
+            mq[qg] = mx;
+          }
         }
       }
     }
@@ -658,19 +712,23 @@ __global__ __launch_bounds__(kThreads, OUT ? kOutBlocks : KVPOP_FWD_MIN_BLOCKS) 
     return;
   }
   // merge the two half-waves that share a query column
-  const float mo = __shfl_xor(m, 32);
-  const float lo = __shfl_xor(l, 32);
-  const float M = fmaxf(m, mo);
-  float L = 0.f;
-  if (M > -INFINITY) {
-    const float Mc = M * c;
-    L = (m > -INFINITY ? l * fast_exp2(fmaf(m, c, -Mc)) : 0.f) +
-        (mo > -INFINITY ? lo * fast_exp2(fmaf(mo, c, -Mc)) : 0.f);
-  }
-  if (half == 0 && valid) {
-    const size_t row = ((size_t)b * Hq + g) * S + dpos;
-    if (n_pieces == 1) lse[row] = M * scale + logf(L);
-    else part[(size_t)piece * B * Hq * S + row] = make_float2(M, L);
+#pragma unroll
+  for (int qg = 0; qg < QG; ++qg) {
+    const float mm = mq[qg], ll = lq[qg];
+    const float mo = __shfl_xor(mm, 32);
+    const float lo = __shfl_xor(ll, 32);
+    const float M = fmaxf(mm, mo);
+    float L = 0.f;
+    if (M > -INFINITY) {
+      const float Mc = M * c;
+      L = (mm > -INFINITY ? ll * fast_exp2(fmaf(mm, c, -Mc)) : 0.f) +
+          (mo > -INFINITY ? lo * fast_exp2(fmaf(mo, c, -Mc)) : 0.f);
+    }
+    if (half == 0 && validq[qg]) {
+      const size_t row = ((size_t)b * Hq + gq[qg]) * S + dposq[qg];
+      if (n_pieces == 1) lse[row] = M * scale + logf(L);
+      else part[(size_t)piece * B * Hq * S + row] = make_float2(M, L);
+    }
   }
 }
 
@@ -697,10 +755,11 @@ __global__ __launch_bounds__(256) void fwd_lse_merge_kernel(const float2* __rest
 
 }  // namespace
 
-FwdPlan plan_fwd(const AttnShape& s) {
+// qg query groups of 32 rows per wave (1 or 2)
+static FwdPlan plan_fwd_qg(const AttnShape& s, int qg) {
   FwdPlan p;
   const int G = s.Hq / s.Hkv;
-  p.P = kRows / G;
+  p.P = kRows * qg / G;
   p.n_pb = (s.S + p.P - 1) / p.P;
   const long rowblocks = (long)s.B * s.Hkv * p.n_pb;
   long want = (KVPOP_FWD_TARGET_ITEMS + rowblocks - 1) / rowblocks;
@@ -714,6 +773,8 @@ FwdPlan plan_fwd(const AttnShape& s) {
   p.partial_floats = p.n_pieces > 1 ? (size_t)2 * p.n_pieces * s.B * s.Hq * (size_t)s.S : 0;
   return p;
 }
+
+FwdPlan plan_fwd(const AttnShape& s) { return plan_fwd_qg(s, 1); }
 
 SparsePlan plan_fwd_sparse(const AttnShape& s, int budget) {
   SparsePlan sp;
@@ -741,11 +802,19 @@ hipError_t launch_fwd_lse(const AttnShape& s, const void* q, const void* k, cons
     p.kmax = (s.S + kKT - 1) / kKT * kKT;
     p.n_pieces = 1;
   }
+  const int cus = device_cu_count();
+  // launches of many rounds of whole rows: two query groups per wave
+  bool wide = KVPOP_FWD_WIDE && s.D == 128 && !keep_until && !out && p.n_pieces == 1 &&
+              (long)s.B * s.Hkv * p.n_pb >= (long)KVPOP_FWD_WIDE_ROUNDS * cus * KVPOP_FWD_MIN_BLOCKS;
+  if (wide) {
+    const FwdPlan p2 = plan_fwd_qg(s, 2);
+    if (p2.n_pieces == 1) p = p2;
+    else wide = false;
+  }
   const int n_items = s.B * s.Hkv * p.n_pb * p.n_pieces;
   const float c = s.scale * kLog2e;
   // one resident round: deal each XCD's blocks in a snake
-  const int cus = device_cu_count();
-  const int per_cu = out ? kOutBlocks : KVPOP_FWD_MIN_BLOCKS;
+  const int per_cu = out ? kOutBlocks : wide ? 2 : KVPOP_FWD_MIN_BLOCKS;
   const int snake_cus = n_items <= cus * per_cu && cus % 8 == 0 ? cus / 8 : 0;
   const int s_pad = (s.S + kKT - 1) / kKT * kKT;
   bf16_t* vt = nullptr;
@@ -785,17 +854,18 @@ hipError_t launch_fwd_lse(const AttnShape& s, const void* q, const void* k, cons
                        o_bf16);
   };
   if (s.D == 128) {
-    if (out && keep_until) go(fwd_lse_kernel<128, kMasked, true>);
-    else if (out) go(fwd_lse_kernel<128, kDense, true>);
-    else if (listed) go(fwd_lse_kernel<128, kListed, false>);
-    else if (keep_until) go(fwd_lse_kernel<128, kMasked, false>);
-    else go(fwd_lse_kernel<128, kDense, false>);
+    if (out && keep_until) go(fwd_lse_kernel<128, kMasked, true, 1>);
+    else if (out) go(fwd_lse_kernel<128, kDense, true, 1>);
+    else if (listed) go(fwd_lse_kernel<128, kListed, false, 1>);
+    else if (keep_until) go(fwd_lse_kernel<128, kMasked, false, 1>);
+    else if (wide) go(fwd_lse_kernel<128, kDense, false, 2>);
+    else go(fwd_lse_kernel<128, kDense, false, 1>);
   } else {
-    if (out && keep_until) go(fwd_lse_kernel<64, kMasked, true>);
-    else if (out) go(fwd_lse_kernel<64, kDense, true>);
-    else if (listed) go(fwd_lse_kernel<64, kListed, false>);
-    else if (keep_until) go(fwd_lse_kernel<64, kMasked, false>);
-    else go(fwd_lse_kernel<64, kDense, false>);
+    if (out && keep_until) go(fwd_lse_kernel<64, kMasked, true, 1>);
+    else if (out) go(fwd_lse_kernel<64, kDense, true, 1>);
+    else if (listed) go(fwd_lse_kernel<64, kListed, false, 1>);
+    else if (keep_until) go(fwd_lse_kernel<64, kMasked, false, 1>);
+    else go(fwd_lse_kernel<64, kDense, false, 1>);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_pieces == 1) return e;

@@ -201,6 +201,27 @@ def test_prefill_shape_listed_sparse_lse_sampled_rows(kv):
     assert_close(f32(lse), f32(tested), LSE_ATOL, 0, "32k listed against tested, all rows")
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,S", [(64, 16, 16, 500), (16, 32, 8, 1000)])
+def test_many_row_blocks_full_parity(kv, B, Hq, Hkv, S):
+    """Launches of many rounds of row blocks (the dense pass then keeps two
+    query groups of 32 rows per wave), groups of 1 and 4, ragged last
+    blocks: every dense normalizer and every sparse one (each causal key
+    tested against keep_until) against the oracle."""
+    D = 128
+    q = synth.bf16(synth.normal((B, Hq, S, D), S + Hq))
+    k = synth.bf16(synth.normal((B, Hkv, S, D), S + Hq + 1))
+    sc = synth.scores((B, Hkv, S), seed=S, kind="normal")
+    s, w, budget = 4, 32, 128
+    qd, kd = q.cuda(), k.cuda()
+    u, _ = kv.running_topk(sc.cuda(), s, w, budget)
+    lse = kv.fwd_lse(qd, kd)
+    lsm = kv.fwd_lse_sparse(qd, kd, u)
+    torch.cuda.synchronize()
+    assert_close(f32(lse), oracle.lse(f32(q), f32(k)), LSE_ATOL, 0, "dense lse")
+    assert_close(f32(lsm), oracle.lse_sparse(f32(q), f32(k), sc.numpy(), s, w, budget), LSE_ATOL, 0,
+                 "sparse lse")
+
+
 def test_sparse_equals_dense_when_nothing_is_evicted(kv):
     """A budget covering the whole sequence keeps every key: the sparse pass
     must give the dense pass's normalizers."""
