@@ -116,10 +116,17 @@ namespace {
 #ifndef KVPOP_TGT_SETPRIO
 #define KVPOP_TGT_SETPRIO 1
 #endif
+// the two-sub-tile kernel's ring stages and priority mode (two stages and
+// no priority change measured about 1% faster each on the 32k layer and the
+// skewed 16k batch than the eight-wave kernel's three stages and priority 1)
+#ifndef KVPOP_TGT_STAGES_KS2
+#define KVPOP_TGT_STAGES_KS2 2
+#endif
+#ifndef KVPOP_TGT_SETPRIO_KS2
+#define KVPOP_TGT_SETPRIO_KS2 0
+#endif
 
 constexpr int kQT = 32;                    // queries per LDS tile
-constexpr int kStages = KVPOP_TGT_STAGES;  // query tiles in the LDS ring
-static_assert(kStages >= 2 && kStages <= 4, "stage count");
 
 // One step of the register transpose-reduce: every lane holds 2M values;
 // lanes with bit M set keep the upper half, the others the lower half, each
@@ -147,6 +154,9 @@ future_target_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   constexpr int ROWB = D * 2;               // bytes per query row
   constexpr int TILE = kQT * ROWB;          // bytes per query tile
   constexpr int TPS = KVPOP_TGT_TPS;        // tiles per stage
+  constexpr int kStages = KS == 2 ? KVPOP_TGT_STAGES_KS2 : KVPOP_TGT_STAGES;  // LDS ring stages
+  static_assert(kStages >= 2 && kStages <= 4, "stage count");
+  constexpr int kPrio = KS == 2 ? KVPOP_TGT_SETPRIO_KS2 : KVPOP_TGT_SETPRIO;
   static_assert(TPS == 1 || TPS == 2, "tiles per stage");
   constexpr int NQI = TILE / 1024;          // 1 KB DMA instructions per query tile
   static_assert((TPS * NQI) % WAVES == 0, "every wave loads the same share of a stage");
@@ -402,8 +412,8 @@ future_target_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         // fragment reads in groups of FG, each group issued before one wait
         // (the next group's reads overlap this group's MFMAs)
         constexpr int FG = KVPOP_TGT_FRAG_GROUP;
-        if constexpr (KVPOP_TGT_SETPRIO == 1) __builtin_amdgcn_s_setprio(1);
-        if constexpr (KVPOP_TGT_SETPRIO == 2) __builtin_amdgcn_s_setprio(0);
+        if constexpr (kPrio == 1) __builtin_amdgcn_s_setprio(1);
+        if constexpr (kPrio == 2) __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int s0 = 0; s0 < NS; s0 += FG) {
           u32x4 bu[FG];
@@ -425,8 +435,8 @@ future_target_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
             for (int j = 0; j < KS; ++j) acc[j] = mfma32(ka[j][s0 + s], bq, acc[j]);
           }
         }
-        if constexpr (KVPOP_TGT_SETPRIO == 1) __builtin_amdgcn_s_setprio(0);
-        if constexpr (KVPOP_TGT_SETPRIO == 2) __builtin_amdgcn_s_setprio(1);
+        if constexpr (kPrio == 1) __builtin_amdgcn_s_setprio(0);
+        if constexpr (kPrio == 2) __builtin_amdgcn_s_setprio(1);
         // Squares inside the allowed region and the sequence need no test.
         // Others first set their disallowed pairs to -inf and their queries
         // past S to L = +inf; then every square takes one FMA, one exp2 and
