@@ -91,6 +91,11 @@ namespace {
 #ifndef KVPOP_TGT_FRAG_GROUP
 #define KVPOP_TGT_FRAG_GROUP 4
 #endif
+// the two-sub-tile kernel reads one fragment per wait, which keeps it within
+// the 168 registers of three waves per SIMD
+#ifndef KVPOP_TGT_FRAG_GROUP_KS2
+#define KVPOP_TGT_FRAG_GROUP_KS2 1
+#endif
 // waves per SIMD the kernel is compiled for (sets its register budget:
 // 512 / n registers per lane)
 #ifndef KVPOP_TGT_WPE
@@ -105,10 +110,15 @@ namespace {
 #ifndef KVPOP_TGT_WIDE_ITEMS
 #define KVPOP_TGT_WIDE_ITEMS 1
 #endif
-// waves per SIMD of the two-sub-tile kernel (its keys take 64 registers;
-// three spill)
+// waves per SIMD of the two-sub-tile kernel: three for the summed target
+// (its keys take 64 registers; 3.91 -> 3.78 ms on a 32k layer against two,
+// with one fragment per wait and one register for the query-row DMA
+// offsets), two for the per-head one, whose extra state would spill at three
 #ifndef KVPOP_TGT_WPE_KS2
-#define KVPOP_TGT_WPE_KS2 2
+#define KVPOP_TGT_WPE_KS2 3
+#endif
+#ifndef KVPOP_TGT_WPE_KS2_HEAD
+#define KVPOP_TGT_WPE_KS2_HEAD 2
 #endif
 // wave priority raised around a tile's MFMA burst (1; ~2% faster than 0:
 // the arbiter then feeds the matrix core first while other waves of the
@@ -143,7 +153,8 @@ __device__ __forceinline__ void xreduce_step(float* v, int lane) {
 
 template <int D, bool PER_HEAD, int WAVES, int KS>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(
-    KS == 1 ? KVPOP_TGT_WPE : KVPOP_TGT_WPE_KS2, KS == 1 ? KVPOP_TGT_WPE : KVPOP_TGT_WPE_KS2))) void
+    KS == 1 ? KVPOP_TGT_WPE : PER_HEAD ? KVPOP_TGT_WPE_KS2_HEAD : KVPOP_TGT_WPE_KS2,
+    KS == 1 ? KVPOP_TGT_WPE : PER_HEAD ? KVPOP_TGT_WPE_KS2_HEAD : KVPOP_TGT_WPE_KS2))) void
 future_target_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                      const float* __restrict__ lse, float* __restrict__ partial,
                      int* __restrict__ run_start, int Hq, int Hkv, int S, int window,
@@ -236,15 +247,13 @@ future_target_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
-  // byte offset of this lane's 16-byte chunk within its query-row DMAs'
-  // tile (row and swizzled chunk depend only on the lane and the wave)
-  uint32_t qoff[QPW];
-#pragma unroll
-  for (int j = 0; j < QPW; ++j) {
-    const int I = wave * QPW + j;
-    const int row = (I % NQI) * ROWS_PER_LOAD + lane / CPR;
-    qoff[j] = (uint32_t)(row * ROWB + (((lane % CPR) ^ (row & (CPR - 1))) << 4));
-  }
+  // byte offset of this lane's 16-byte chunk within its first query-row
+  // DMA's tile: wave w issues DMAs w, w + WAVES, ..., whose rows agree with
+  // the first one's modulo the swizzle period, so the others add a
+  // wave-uniform row offset to this one register
+  static_assert((WAVES * ROWS_PER_LOAD) % CPR == 0 && kQT % CPR == 0, "one swizzle phase per wave");
+  const int qrow0 = (wave % NQI) * ROWS_PER_LOAD + lane / CPR;
+  const uint32_t qoff = (uint32_t)(qrow0 * ROWB + (((lane % CPR) ^ (qrow0 & (CPR - 1))) << 4));
   const uint32_t col4 = (uint32_t)col * 4u;
 
   for (bool first = true;; first = false) {
@@ -327,9 +336,10 @@ future_target_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     // come from the group's range the same way.
 #pragma unroll
     for (int j = 0; j < QPW; ++j) {
-      const int I = wave * QPW + j;
+      const int I = wave + WAVES * j;
       const int tt = I / NQI;
-      bdma16(rqg, (uint32_t)rows[tt] * ROWB + qoff[j], qst(J) + I * 1024);
+      const int drow = (I % NQI - wave % NQI) * ROWS_PER_LOAD;
+      bdma16(rqg, (uint32_t)(rows[tt] + drow) * ROWB + qoff, qst(J) + I * 1024);
     }
     {
       const uint32_t l0 = (uint32_t)rows[0] * 4u;
@@ -411,7 +421,7 @@ future_target_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
           for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
         // fragment reads in groups of FG, each group issued before one wait
         // (the next group's reads overlap this group's MFMAs)
-        constexpr int FG = KVPOP_TGT_FRAG_GROUP;
+        constexpr int FG = KS == 2 ? KVPOP_TGT_FRAG_GROUP_KS2 : KVPOP_TGT_FRAG_GROUP;
         if constexpr (kPrio == 1) __builtin_amdgcn_s_setprio(1);
         if constexpr (kPrio == 2) __builtin_amdgcn_s_setprio(0);
 #pragma unroll
@@ -425,8 +435,10 @@ future_target_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                          "v"(bu[6]), "v"(bu[7]), "v"(lraw));
           else if constexpr (FG == 4)
             asm volatile("" ::"v"(bu[0]), "v"(bu[1]), "v"(bu[2]), "v"(bu[3]), "v"(lraw));
-          else
+          else if constexpr (FG == 2)
             asm volatile("" ::"v"(bu[0]), "v"(bu[1]), "v"(lraw));
+          else
+            asm volatile("" ::"v"(bu[0]), "v"(lraw));
 #pragma unroll
           for (int s = 0; s < FG; ++s) {
             bf16x8 bq;
