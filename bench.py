@@ -44,8 +44,8 @@ FP32_VECTOR_PEAK_TFS = 157.3     # MI355X fp32 vector (counts packed FMA; one FM
 # only for the kernel code it was taken on (sources_digest): bench reports
 # null once that changes.
 TRAFFIC_SOURCES = ("future_target.hip", "common.h", "launch.h")
-TRAFFIC = {"sha256": "213f298aff54dd4f3431f49764e19069713925e91b941092af6460a81cd7557d",
-           "fetch_bytes": 2 * (405598.0 + 4319.0) * 1024, "write_bytes": (8576.0 + 1024.0) * 1024}
+TRAFFIC = {"sha256": "c15e63d21d9e4c1e1fb20aa47564ed7aedaa86a497a5b7f1b30bde5ba3347512",
+           "fetch_bytes": 2 * (446589.3 + 4319.0) * 1024, "write_bytes": (8576.0 + 1024.0) * 1024}
 # HBM bytes per dispatch of the HBM-bound kernels the bench reports, from the
 # same pair of counter runs with the same scaling (FETCH_SIZE x 2, WRITE_SIZE
 # x 1), each valid only for the sources it was taken on.
