@@ -10,11 +10,8 @@
 //   * Work item = (b, KV head, slot split).  Each K/V row is read once for
 //     all G query heads of its group.
 //   * A 16-lane quarter-wave owns one slot row at a time (16 bytes per lane,
-//     fully coalesced 256-byte rows; the four quarter-waves of a wave take
-//     consecutive rows, so each load instruction covers 1 KB: 3% faster in a
-//     streaming probe than rows 1 KB apart); the q.k partial dots are
-//     reduced with four DPP adds inside the 16-lane row, so no LDS traffic
-//     in the loop.
+//     fully coalesced 256-byte rows); the q.k partial dots are reduced with
+//     four DPP adds inside the 16-lane row, so no LDS traffic in the loop.
 //   * Softmax in base 2 with the scale folded into q; each quarter-wave keeps
 //     an online (max, sum, o) state per head over blocks of 4 slots, and the
 //     16 states of a workgroup are merged once through LDS.  The maximum is
@@ -79,6 +76,10 @@ __device__ __forceinline__ void unpack<4>(const uint4& u, float* f) {
   f[0] = bf16_lo(u.x); f[1] = bf16_hi(u.x); f[2] = bf16_lo(u.y); f[3] = bf16_hi(u.y);
 }
 
+// slot positions of a quarter-wave's rows read by one 16-byte load (1)
+#ifndef KVPOP_DEC_POS4
+#define KVPOP_DEC_POS4 1
+#endif
 // cache rows are read once per step: non-temporal loads (1) or plain (0)
 #ifndef KVPOP_DEC_NT
 #define KVPOP_DEC_NT 1
@@ -141,18 +142,29 @@ __device__ __forceinline__ void decode_row(
     // iteration r's rows (slots past the split read row j_begin, masked)
     uint4 kb[kRing][kNB], vb[kRing][kNB];
     int pb[kRing][kNB];
-    // iteration jb's rows: quarter-wave qw takes rows jb + 16 i + qw, so
-    // each load instruction of a wave covers four consecutive rows
+    // the quarter-wave's kNB slot positions come as one 16-byte load when
+    // they are aligned and inside the split
+    const bool pos4 = KVPOP_DEC_POS4 && kNB == 4 && ((row0 + j_begin) & 3) == 0;
     auto fetch = [&](auto R, int jb) {
       constexpr int r = decltype(R)::value;
+      const int jq = jb + qw * kNB;
 #pragma unroll
       for (int i = 0; i < kNB; ++i) {
-        const int j = jb + 16 * i + qw;
+        const int j = jq + i;
         const bool in = j < j_end;
         const size_t off = (row0 + (in ? j : j_begin)) * D + ql * FPL;
         kb[r][i] = load_row_part<FPL>(kc + off);
         vb[r][i] = load_row_part<FPL>(vc + off);
-        pb[r][i] = in ? slot_pos[row0 + j] : -1;
+      }
+      if (pos4 && jq + kNB <= j_end) {
+        const int4 pv = *reinterpret_cast<const int4*>(slot_pos + row0 + jq);
+        pb[r][0] = pv.x;
+        pb[r][1] = pv.y;
+        pb[r][2] = pv.z;
+        pb[r][3] = pv.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < kNB; ++i) pb[r][i] = jq + i < j_end ? slot_pos[row0 + jq + i] : -1;
       }
     };
     auto bf2 = [](uint32_t w) { return __builtin_bit_cast(bf16x2_t, w); };
