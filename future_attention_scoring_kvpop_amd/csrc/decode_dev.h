@@ -18,19 +18,11 @@
 //     only taken again (and l, o rescaled) when a block's terms would sum
 //     past 2^64: a score a little past it just gives a term above 1.  Splits are
 //     merged by a second small kernel with the same log-sum-exp rule.
-//   * q.k is taken with bf16 dot-product instructions (v_dot2c_f32_bf16:
-//     K rows and q stay packed, fp32 accumulation, the scale applied to the
-//     sum) and V rows are unpacked one slot at a time, which leaves the
-//     registers free (216 for four query heads, two workgroups per CU).
-//     Each quarter-wave issues the loads of the next iteration before it
-//     computes the current one (two iterations ahead measured the same on
-//     the 64-sequence workload: loads in flight are not what bounds it).
-//     The loads carry the
-//     non-temporal hint (the cache is streamed once per step): 142 -> 158
-//     decode steps/s on the 64-sequence workload.
+//   * Each quarter-wave loads the next iteration's K/V rows before it
+//     computes the current one, so a wave always has a row block in flight.
+//     The loads carry the non-temporal hint (the cache is streamed once per
+//     step): 142 -> 158 decode steps/s on the 64-sequence workload.
 #pragma once
-
-#include <type_traits>
 
 #include "common.h"
 
@@ -38,21 +30,12 @@ namespace kvpop {
 namespace decdev {
 
 constexpr int kThreads = 256;
-#ifndef KVPOP_DEC_NB
-#define KVPOP_DEC_NB 4
+// 1: the next iteration's K/V rows are loaded before this one is computed
+#ifndef KVPOP_DEC_PREFETCH
+#define KVPOP_DEC_PREFETCH 1
 #endif
-constexpr int kNB = KVPOP_DEC_NB;         // slots per quarter-wave per iteration
+constexpr int kNB = 4;                    // slots per quarter-wave per iteration
 constexpr int kSlotsPerIter = 16 * kNB;   // per workgroup
-// iterations of K/V rows in flight ahead of the one being computed (1 or 2;
-// 2 takes the four-head attention kernel past 256 registers), and the
-// register ring that holds them
-#ifndef KVPOP_DEC_DEPTH
-#define KVPOP_DEC_DEPTH 1
-#endif
-constexpr int kDepth = KVPOP_DEC_DEPTH;
-static_assert(kDepth == 1 || kDepth == 2, "prefetch depth");
-constexpr int kRing = kDepth + 1;
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // sum over the 16 lanes of a DPP row; every lane receives the same value
 __device__ __forceinline__ float row16_sum(float x) {
@@ -76,10 +59,6 @@ __device__ __forceinline__ void unpack<4>(const uint4& u, float* f) {
   f[0] = bf16_lo(u.x); f[1] = bf16_hi(u.x); f[2] = bf16_lo(u.y); f[3] = bf16_hi(u.y);
 }
 
-// slot positions of a quarter-wave's rows read by one 16-byte load (1)
-#ifndef KVPOP_DEC_POS4
-#define KVPOP_DEC_POS4 1
-#endif
 // cache rows are read once per step: non-temporal loads (1) or plain (0)
 #ifndef KVPOP_DEC_NT
 #define KVPOP_DEC_NT 1
@@ -116,18 +95,13 @@ __device__ __forceinline__ void decode_row(
   const size_t row0 = (size_t)bh * n_slots;
 
   for (int g0 = 0; g0 < G; g0 += GC) {
-    // the group's queries as packed bf16 pairs: q.k is taken by bf16 dot
-    // products with fp32 accumulation, and the scale applied to the sum
-    uint32_t qp[GC][FPL / 2];
+    float qv[GC][FPL];
 #pragma unroll
     for (int g = 0; g < GC; ++g) {
-      const uint4 u = load_row_part<FPL>(q + ((size_t)b * Hq + h * G + g0 + g) * D + ql * FPL);
-      qp[g][0] = u.x;
-      qp[g][1] = u.y;
-      if constexpr (FPL == 8) {
-        qp[g][2] = u.z;
-        qp[g][3] = u.w;
-      }
+      float t[8];
+      unpack<FPL>(load_row_part<FPL>(q + ((size_t)b * Hq + h * G + g0 + g) * D + ql * FPL), t);
+#pragma unroll
+      for (int f = 0; f < FPL; ++f) qv[g][f] = t[f] * c;
     }
     float m[GC], l[GC], o[GC][FPL];
 #pragma unroll
@@ -138,76 +112,70 @@ __device__ __forceinline__ void decode_row(
       for (int f = 0; f < FPL; ++f) o[g][f] = 0.f;
     }
 
-    // K/V rows of kDepth iterations in flight: ring slot r % kRing holds
-    // iteration r's rows (slots past the split read row j_begin, masked)
-    uint4 kb[kRing][kNB], vb[kRing][kNB];
-    int pb[kRing][kNB];
-    // the quarter-wave's kNB slot positions come as one 16-byte load when
-    // they are aligned and inside the split
-    const bool pos4 = KVPOP_DEC_POS4 && kNB == 4 && ((row0 + j_begin) & 3) == 0;
-    auto fetch = [&](auto R, int jb) {
-      constexpr int r = decltype(R)::value;
-      const int jq = jb + qw * kNB;
+    // rows of iteration jb (prefetched one iteration ahead when enabled)
+    uint4 kn[kNB], vn[kNB];
+    int pn[kNB];
+    auto fetch = [&](int jb) {
 #pragma unroll
       for (int i = 0; i < kNB; ++i) {
-        const int j = jq + i;
+        const int j = jb + qw * kNB + i;
         const bool in = j < j_end;
         const size_t off = (row0 + (in ? j : j_begin)) * D + ql * FPL;
-        kb[r][i] = load_row_part<FPL>(kc + off);
-        vb[r][i] = load_row_part<FPL>(vc + off);
-      }
-      if (pos4 && jq + kNB <= j_end) {
-        const int4 pv = *reinterpret_cast<const int4*>(slot_pos + row0 + jq);
-        pb[r][0] = pv.x;
-        pb[r][1] = pv.y;
-        pb[r][2] = pv.z;
-        pb[r][3] = pv.w;
-      } else {
-#pragma unroll
-        for (int i = 0; i < kNB; ++i) pb[r][i] = jq + i < j_end ? slot_pos[row0 + jq + i] : -1;
+        kn[i] = load_row_part<FPL>(kc + off);
+        vn[i] = load_row_part<FPL>(vc + off);
+        pn[i] = in ? slot_pos[row0 + j] : -1;
       }
     };
-    auto bf2 = [](uint32_t w) { return __builtin_bit_cast(bf16x2_t, w); };
-    // one iteration on ring slot R: first the loads of the iteration
-    // kDepth ahead go out, then this one's rows are consumed
-    auto step = [&](auto R, int jb) {
-      constexpr int r = decltype(R)::value;
-      if (jb + kDepth * kSlotsPerIter < j_end)
-        fetch(std::integral_constant<int, (r + kDepth) % kRing>{}, jb + kDepth * kSlotsPerIter);
-      float p[GC][kNB];
+    if (KVPOP_DEC_PREFETCH) fetch(j_begin);
+    for (int jb = j_begin; jb < j_end; jb += kSlotsPerIter) {
+      uint4 kr[kNB], vr[kNB];
+      bool ok[kNB];
+      if (!KVPOP_DEC_PREFETCH) fetch(jb);
+#pragma unroll
+      for (int i = 0; i < kNB; ++i) {
+        kr[i] = kn[i];
+        vr[i] = vn[i];
+        ok[i] = pn[i] >= 0;
+      }
+      if (KVPOP_DEC_PREFETCH && jb + kSlotsPerIter < j_end) fetch(jb + kSlotsPerIter);
+      float kf[kNB][8], vf[kNB][8];
+#pragma unroll
+      for (int i = 0; i < kNB; ++i) {
+        unpack<FPL>(kr[i], kf[i]);
+        unpack<FPL>(vr[i], vf[i]);
+      }
 #pragma unroll
       for (int g = 0; g < GC; ++g) {
-        float sc[kNB];
+        float s[kNB];
 #pragma unroll
         for (int i = 0; i < kNB; ++i) {
-          const uint32_t kw[4] = {kb[r][i].x, kb[r][i].y, kb[r][i].z, kb[r][i].w};
           float d = 0.f;
 #pragma unroll
-          for (int w = 0; w < FPL / 2; ++w) d = __builtin_amdgcn_fdot2_f32_bf16(bf2(qp[g][w]), bf2(kw[w]), d, false);
-          d = row16_sum(d) * c;
-          sc[i] = pb[r][i] >= 0 ? d : -INFINITY;
+          for (int f = 0; f < FPL; ++f) d = fmaf(qv[g][f], kf[i][f], d);
+          d = row16_sum(d);
+          s[i] = ok[i] ? d : -INFINITY;
         }
         // Terms relative to the running maximum as it stands; the maximum
         // and the rescaling of l and o are only taken again when some
         // lane's terms would sum past 2^64 or it has no maximum yet (the
         // sum is then inf or NaN).
-        float psum = 0.f;
+        float p[kNB], psum = 0.f;
 #pragma unroll
         for (int i = 0; i < kNB; ++i) {
-          p[g][i] = fast_exp2(sc[i] - m[g]);
-          psum += p[g][i];
+          p[i] = fast_exp2(s[i] - m[g]);
+          psum += p[i];
         }
         if (!__all(psum <= 0x1p64f)) {
           float mx = m[g];
 #pragma unroll
-          for (int i = 0; i < kNB; ++i) mx = fmaxf(mx, sc[i]);
+          for (int i = 0; i < kNB; ++i) mx = fmaxf(mx, s[i]);
           const float alpha = mx > -INFINITY ? fast_exp2(m[g] - mx) : 1.f;
           const float ms = mx > -INFINITY ? mx : 0.f;  // masked slots still give 0
           psum = 0.f;
 #pragma unroll
           for (int i = 0; i < kNB; ++i) {
-            p[g][i] = fast_exp2(sc[i] - ms);
-            psum += p[g][i];
+            p[i] = fast_exp2(s[i] - ms);
+            psum += p[i];
           }
           l[g] *= alpha;
 #pragma unroll
@@ -215,27 +183,14 @@ __device__ __forceinline__ void decode_row(
           m[g] = mx;
         }
         l[g] += psum;
+#pragma unroll
+        for (int f = 0; f < FPL; ++f) {
+          float acc = o[g][f];
+#pragma unroll
+          for (int i = 0; i < kNB; ++i) acc = fmaf(p[i], vf[i][f], acc);
+          o[g][f] = acc;
+        }
       }
-      // o += p v, one V row part unpacked at a time (slot order per output)
-#pragma unroll
-      for (int i = 0; i < kNB; ++i) {
-        float vf[8];
-        unpack<FPL>(vb[r][i], vf);
-#pragma unroll
-        for (int g = 0; g < GC; ++g)
-#pragma unroll
-          for (int f = 0; f < FPL; ++f) o[g][f] = fmaf(p[g][i], vf[f], o[g][f]);
-      }
-    };
-    using R0 = std::integral_constant<int, 0>;
-    using R1 = std::integral_constant<int, 1>;
-    using R2 = std::integral_constant<int, 2>;
-    fetch(R0{}, j_begin);
-    if (kDepth > 1 && j_begin + kSlotsPerIter < j_end) fetch(R1{}, j_begin + kSlotsPerIter);
-    for (int jb = j_begin; jb < j_end; jb += kRing * kSlotsPerIter) {
-      step(R0{}, jb);
-      if (jb + kSlotsPerIter < j_end) step(R1{}, jb + kSlotsPerIter);
-      if (kRing > 2 && jb + 2 * kSlotsPerIter < j_end) step(R2{}, jb + 2 * kSlotsPerIter);
     }
 
     // merge the 16 quarter-wave states of this workgroup

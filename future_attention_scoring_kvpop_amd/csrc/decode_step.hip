@@ -19,7 +19,7 @@ namespace kvpop {
 namespace {
 
 template <int D, int GC>
-__global__ __launch_bounds__(decdev::kThreads, GC <= 4 ? 2 : 1) void decode_step_kernel(
+__global__ __launch_bounds__(decdev::kThreads) void decode_step_kernel(
     int n_sink, int window, int budget, int delay, int pos_q, const bf16_t* __restrict__ k_new,
     const bf16_t* __restrict__ v_new, const float* __restrict__ w1, const float* __restrict__ b1,
     const float* __restrict__ w2, const float* __restrict__ b2, int hidden,
@@ -47,7 +47,7 @@ __global__ __launch_bounds__(decdev::kThreads, GC <= 4 ? 2 : 1) void decode_step
 // phase's global writes are ordered before the next phase's reads by a
 // workgroup barrier, as above.
 template <int D, int GC>
-__global__ __launch_bounds__(decdev::kThreads, GC <= 4 ? 2 : 1) void decode_step_mlstm_kernel(
+__global__ __launch_bounds__(decdev::kThreads) void decode_step_mlstm_kernel(
     int n_sink, int window, int budget, int pos_q, const bf16_t* __restrict__ k_new,
     const bf16_t* __restrict__ v_new, MlstmWeights wt, float* __restrict__ state,
     bf16_t* __restrict__ kc, bf16_t* __restrict__ vc, int32_t* __restrict__ slot_pos,
