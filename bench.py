@@ -238,7 +238,7 @@ class PrefillStep:
 def bench_prefill_step(kv, w, steps, warmup):
     """The headline: `steps` timed steps (after `warmup`) of PrefillStep,
     between two events; events around every pass of every layer give the
-    per-pass means (at ~9 ms per layer their cost is negligible).  The
+    per-pass means (at ~7.4 ms per layer their cost is negligible).  The
     roofline of the transposed pass is its flops per call over the mean of
     its calls' event durations in the timed steps."""
     st = PrefillStep(kv, w)
