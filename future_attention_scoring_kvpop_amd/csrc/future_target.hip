@@ -17,13 +17,15 @@
 //     of the list, so the causal triangle leaves no idle tail; launches with
 //     many rounds of runs give each workgroup one run, so the workgroups of
 //     an XCD stream a chunk's query tiles in step and keep them in L2.
-//   * Within a run each wave keeps its 32 keys resident as MFMA A fragments
+//   * Within a run each wave keeps its keys resident as MFMA A fragments
 //     and streams the query tiles of all G heads of the group as B
-//     fragments: v_mfma_f32_32x32x16_bf16 yields S^T[key][query].  About 120
-//     registers per wave keep four waves per SIMD resident, so the MFMA
+//     fragments: v_mfma_f32_32x32x16_bf16 yields S^T[key][query].  A key
+//     block is 256 keys for D = 128: eight waves of 32 keys (about 115
+//     registers, four waves per SIMD) where the list is split evenly, four
+//     waves of 64 keys (two MFMA chains per fragment read, 168 registers,
+//     three waves per SIMD) where each workgroup takes one run.  The MFMA
 //     phase of one wave overlaps the exp2/accumulate phase of the others.
-//   * All waves of a workgroup (8 for D = 128) share each stage of two
-//     query tiles.  Stages reach LDS by direct buffer->LDS loads into a
+//   * All waves of a workgroup share each stage of two query tiles.  Stages reach LDS by direct buffer->LDS loads into a
 //     ring, each wave issuing a fixed share (and its own copy of the tiles'
 //     normalizers); each stage is its own LDS object so the compiler never
 //     drains in-flight prefetches before a read.  A load's address is the
@@ -34,7 +36,8 @@
 //     with their 16-byte chunks XOR-swizzled by row, which keeps the
 //     fragment reads bank-conflict free.  A bare s_barrier plus explicit
 //     vmcnt/lgkmcnt waits orders the ring; B fragments are read in groups of
-//     four before one wait.
+//     four before one wait (one for the 64-key waves, which keeps them in
+//     168 registers).
 //   * Each lane owns one query column and 16 key rows, so per-key sums stay
 //     in registers across every query tile and head of a run; they are
 //     reduced across lanes once per run by a register transpose-reduce.
