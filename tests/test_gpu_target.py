@@ -189,6 +189,34 @@ def test_full_size_transposed_pass_sampled_keys(kv, wl, per_qhead):
                          f"per-head ({b},{h})")
 
 
+def test_many_rows_one_run_per_workgroup_max_lookahead(kv):
+    """384 (b, KV head) rows of S = 4096 at D = 128 make enough runs for one
+    run per workgroup (the four-wave 64-key kernel; per-head sums at two waves
+    per SIMD): MAX over the group with a 512-query lookahead and count
+    normalisation, on one seeded normalizer array handed to both sides.  Keys
+    at the start, across key blocks, mid-row and at the tail (where the
+    lookahead and the sequence end cut the query range) of the first and the
+    last row."""
+    B, Hq, Hkv, S, D, window, la = 48, 32, 8, 4096, 128, 256, 512
+    G = Hq // Hkv
+    q = synth.bf16(synth.normal((B, Hq, S, D), 41, "cuda"))
+    k = synth.bf16(synth.normal((B, Hkv, S, D), 42, "cuda"))
+    lse = synth.normalizers(B, Hq, S, seed=43, device="cuda")
+    m, ph = kv.future_attn_target(q, k, lse, window, lookahead=la, agg="max", count_normalize=True,
+                                  per_qhead=True)
+    torch.cuda.synchronize()
+    keys = np.concatenate([np.arange(0, 40), np.arange(240, 300), np.arange(S // 2 - 16, S // 2 + 16),
+                           np.arange(S - window - la - 40, S)]).astype(np.int64)
+    lse_h = lse.cpu().numpy()
+    for b, h in ((0, 0), (B - 1, Hkv - 1)):
+        qs, ks = group_problem(q, k, b, h)
+        om, oph = oracle.future_mass(qs, ks, lse_h[b:b + 1, h * G:(h + 1) * G], window, lookahead=la,
+                                     agg="max", count_normalize=True, cols=keys, per_head=True)
+        assert_close(f32(m[b, h])[keys], om, MASS_ATOL, MASS_RTOL, f"mass ({b},{h})")
+        assert_close(f32(ph[b, h * G:(h + 1) * G])[:, keys].T, oph, MASS_ATOL, MASS_RTOL,
+                     f"per-head ({b},{h})")
+
+
 def _sampled_lse_rows(q, k, lse, n, seed):
     B, Hq, S, _ = q.shape
     Hkv = k.shape[1]
