@@ -32,7 +32,7 @@ EXPORTS = ("kvpop_abi_version", "kvpop_status_string", "kvpop_workspace_bytes", 
            "kvpop_future_attn_target", "kvpop_evict_select", "kvpop_decode_attend",
            "kvpop_score_mlp", "kvpop_cache_step", "kvpop_decode_step", "kvpop_running_topk",
            "kvpop_fwd_lse_sparse", "kvpop_mlstm_step", "kvpop_decode_step_mlstm",
-           "kvpop_decode_attend_noalloc")
+           "kvpop_decode_attend_noalloc", "kvpop_running_topk_workspace_bytes")
 DECODE_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 
@@ -73,7 +73,8 @@ def lib():
             "kvpop_status_string": (ctypes.c_char_p, [I]),
             "kvpop_workspace_bytes": (Z, [I, DP, I]),
             "kvpop_fwd_lse": (I, [DP, P, P, P, P, P, I, P, Z, P]),
-            "kvpop_running_topk": (I, [I, I, I, I, I, I, P, P, P, P, P]),
+            "kvpop_running_topk": (I, [I, I, I, I, I, I, P, P, P, P, P, Z, P]),
+            "kvpop_running_topk_workspace_bytes": (Z, [I, I, I, I]),
             "kvpop_mlstm_step": (I, [I, I, I, I, I, I, I, P, P, P, P, ctypes.POINTER(MlstmWeights),
                                      P, P, P]),
             "kvpop_decode_step_mlstm": (I, [DP, I, I, I, P, P, ctypes.POINTER(MlstmWeights), P, P, P,
@@ -170,7 +171,7 @@ def fwd_lse(q, k, scale=0.0, out=None, workspace=None, v=None, out_o=None,
 
 
 def running_topk(scores, n_sink, window, budget, log_decay=None, want_cutoff=True, out=None,
-                 out_cutoff=None):
+                 out_cutoff=None, workspace=None):
     """Running top-k retention mask (App. C.1) and its per-query cutoffs
     (App. C.2) with per-head decay priorities (Sec. 3, App. B.3).
 
@@ -190,8 +191,13 @@ def running_topk(scores, n_sink, window, budget, log_decay=None, want_cutoff=Tru
     if want_cutoff:
         cut = out_cutoff if out_cutoff is not None else torch.empty_like(until)
         _need(cut, torch.int32, "cutoff")
+    need = lib().kvpop_running_topk_workspace_bytes(B, Hkv, S, int(n_sink))
+    ws = workspace
+    if need and (ws is None or ws.numel() * ws.element_size() < need):
+        ws = torch.empty(need, dtype=torch.uint8, device=scores.device)
     st = lib().kvpop_running_topk(B, Hkv, S, int(n_sink), int(window), int(budget), _p(scores),
-                                  _p(log_decay), _p(until), _p(cut), _stream())
+                                  _p(log_decay), _p(until), _p(cut), _p(ws) if need else None,
+                                  need, _stream())
     _check("kvpop_running_topk", st)
     return until, cut
 

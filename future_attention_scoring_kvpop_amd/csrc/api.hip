@@ -185,9 +185,16 @@ kvpop_status kvpop_decode_step_mlstm(const kvpop_dims* dims, int n_sink, int win
       o, o_dtype == KVPOP_OUT_BF16 ? 1 : 0, lse, (float*)workspace, stream));
 }
 
+size_t kvpop_running_topk_workspace_bytes(int batch, int n_kv_heads, int seq_len, int n_sink) {
+  if (batch <= 0 || n_kv_heads <= 0 || seq_len <= 0 || n_sink < 0) return 0;
+  if (seq_len > kvpop::running_topk_max_len()) return 0;
+  return kvpop::running_topk_workspace_bytes(batch, n_kv_heads, seq_len, n_sink);
+}
+
 kvpop_status kvpop_running_topk(int batch, int n_kv_heads, int seq_len, int n_sink, int window,
                                 int budget, const float* scores, const float* log_decay,
-                                int32_t* keep_until, int32_t* cutoff, hipStream_t stream) {
+                                int32_t* keep_until, int32_t* cutoff, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
   if (batch <= 0 || n_kv_heads <= 0 || seq_len <= 0 || n_sink < 0 || window < 0)
     return KVPOP_ERR_INVALID_ARGUMENT;
   if (budget < n_sink + window || budget <= 0) return KVPOP_ERR_INVALID_ARGUMENT;
@@ -199,8 +206,14 @@ kvpop_status kvpop_running_topk(int batch, int n_kv_heads, int seq_len, int n_si
   if ((double)seq_len + window + budget > 2.0e9) return KVPOP_ERR_UNSUPPORTED;
   if (seq_len > kvpop::running_topk_max_len()) return KVPOP_ERR_UNSUPPORTED;
   if ((double)batch * n_kv_heads * ((seq_len + 63) / 64) > 2.0e9) return KVPOP_ERR_UNSUPPORTED;
+  const size_t need = kvpop::running_topk_workspace_bytes(batch, n_kv_heads, seq_len, n_sink);
+  if (need) {
+    if (!workspace || !aligned(workspace, 16)) return KVPOP_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < need) return KVPOP_ERR_WORKSPACE_TOO_SMALL;
+  }
   return from_hip(kvpop::launch_running_topk(batch, n_kv_heads, seq_len, n_sink, window, budget,
-                                             scores, log_decay, keep_until, cutoff, stream));
+                                             scores, log_decay, keep_until, cutoff, workspace,
+                                             stream));
 }
 
 kvpop_status kvpop_fwd_lse_sparse(const kvpop_dims* dims, const void* q, const void* k,

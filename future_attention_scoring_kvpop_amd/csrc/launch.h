@@ -66,10 +66,12 @@ hipError_t launch_decode_step_mlstm(const AttnShape& s, int n_sink, int window, 
                                     float* lse, float* workspace, hipStream_t st);
 
 // ---- running top-k mask ----
-int running_topk_max_len();  // longest row the kernel takes
+int running_topk_max_len();  // longest row the kernels take
+// workspace of a launch (0 when its rows take the counting kernel)
+size_t running_topk_workspace_bytes(int B, int Hkv, int S, int n_sink);
 hipError_t launch_running_topk(int B, int Hkv, int S, int n_sink, int window, int budget,
                                const float* scores, const float* log_decay, int* keep_until,
-                               int* cutoff, hipStream_t st);
+                               int* cutoff, void* workspace, hipStream_t st);
 
 // ---- transposed future-attention pass ----
 constexpr int kTgtMaxChunks = 64;

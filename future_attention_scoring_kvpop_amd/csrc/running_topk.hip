@@ -18,10 +18,13 @@
 // Every query whose pool holds at least k tokens lies in exactly one such
 // interval; the others get -1.
 //
-// gfx950 mapping
+// gfx950 mapping: two kernels.  Rows up to KVPOP_RT_LONG_MIN tokens take the
+// counting kernel (O(S^2 / 64) compares, no workspace, one launch of many
+// small workgroups); longer rows the O(S log S) kernel further below (sort,
+// wavelet matrix, one workgroup per row, a workspace).  Counting kernel:
 //   * A workgroup owns 64 consecutive tokens (one per lane) of one row; its
 //     NSEG waves split the scanned positions [s, S) into NSEG segments of at
-//     most 64 chunks of 64 positions (128 chunks for rows past 65536).
+//     most 64 chunks of 64 positions.
 //     Each wave ranks the 64 positions of a
 //     chunk (one per lane), stores their keys in its own 256 bytes of LDS
 //     and reads them back four at a time with broadcast ds_read_b128, so a
@@ -43,10 +46,16 @@
 namespace kvpop {
 namespace {
 
-// chunks of 64 positions per wave at most: 64, or 128 for rows past 65536
-// positions (sixteen waves; the chunk counts then take 128 KB of LDS)
+// chunks of 64 positions per wave at most (sixteen waves: rows up to 65536)
 constexpr int kRtChunksPerSeg = 64;
-constexpr int kRtChunksPerSegLong = 128;
+// rows longer than this take the O(S log S) kernel below (with a workspace);
+// shorter ones the counting kernel, which needs none
+#ifndef KVPOP_RT_LONG_MIN
+#define KVPOP_RT_LONG_MIN 8192
+#endif
+static_assert(KVPOP_RT_LONG_MIN <= 16 * kRtChunksPerSeg * 64, "the counting kernel's longest row");
+// the longest row either kernel takes
+#define KVPOP_RT_MAX_LEN (1 << 24)
 
 __device__ __forceinline__ uint32_t priority_key(float sigma, float lam, int t) {
   // pi = sigma + lambda * t, each operation rounded to fp32: contraction
@@ -191,14 +200,412 @@ __global__ __launch_bounds__(64 * NSEG) void running_topk_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Long rows in O(S log S).  App. C.2 takes the running cutoffs with a
+// Fenwick tree in one sequential sweep per head; here one 1024-thread
+// workgroup per row
+//   1. ranks every token of [s, S) in the retention order by a stable LSD
+//      radix sort of (complemented priority key, position) pairs: four
+//      8-bit digits, counted by LDS atomics into per-wave rows; each wave
+//      ranks its 64 lanes per step by eight ballots, so a pass needs
+//      barriers only around its count scan;
+//   2. builds a wavelet matrix over the ranks in position order: one stable
+//      2-way partition per rank bit (most significant first), each level
+//      keeping its bits and the zeros before every 32 of them;
+//   3. (a second launch, many workgroups per row) takes the cutoff rank
+//      c(d) = the k-th smallest rank among the first |P_d| pool positions
+//      (the pool is a position prefix) by one descent of the matrix per
+//      query; c(d) never increases with d;
+//   4. (a third launch) finds keep_until[t] = the first d >= t + w with
+//      c(d) < rank(t) by binary search (t stays selected while
+//      rank(t) <= c(d)).
+// The workspace holds the sort buffers, the ranks, the matrix and the
+// cutoff ranks.
+constexpr int kRsThreads = 1024;
+constexpr int kRsWaves = kRsThreads / 64;
+constexpr int kRsLdsWords = 2 * 256 * kRsWaves;  // per-wave digit counts and offsets
+// steps of a wave loaded into registers a chunk ahead of their use; a
+// wave's step count is a multiple of it, so no load needs a guard (guarded
+// loads make the compiler wait for every earlier store before a use)
+constexpr int kRsChunk = 8;
+constexpr int kRsBatch = 8;  // queries and searches of a thread in flight together
+
+struct RsLayout {
+  int n, L, cw, nw;  // ranked tokens, matrix levels, elements per wave, words per level
+  long kp0, kp1, rk, v0, v1, wb, wd, zt, cr, stride;  // offsets in 32-bit words
+};
+
+__host__ __device__ inline RsLayout rs_layout(int S, int n_sink) {
+  RsLayout l;
+  l.n = S > n_sink ? S - n_sink : 0;
+  l.L = 1;
+  while ((1L << l.L) < (long)l.n) ++l.L;
+  const int span = kRsThreads * kRsChunk;  // elements of one chunk of steps over the workgroup
+  l.cw = (l.n + span - 1) / span * 64 * kRsChunk;  // 16 cw >= n, cw / 64 a multiple of kRsChunk
+  l.nw = kRsWaves * l.cw / 32 + 1;                 // one word past the elements
+  const long N = (long)kRsWaves * l.cw;
+  long o = 0;
+  auto take = [&o](long words) {
+    const long r = o;
+    o += (words + 63) / 64 * 64;
+    return r;
+  };
+  l.kp0 = take(2 * N);
+  l.kp1 = take(2 * N);
+  l.rk = take(N);
+  l.v0 = take(N);
+  l.v1 = take(N);
+  l.wb = take((long)l.L * l.nw);
+  l.wd = take((long)l.L * l.nw);
+  l.zt = take(l.L);
+  l.cr = take(S);
+  l.stride = o;
+  return l;
+}
+
+// exclusive prefix sum of v over the workgroup, and the total
+__device__ uint32_t rs_block_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t s2 = lane < kRsWaves ? wsum[lane] : 0u;
+#pragma unroll
+    for (int off = 1; off < kRsWaves; off <<= 1) {
+      const uint32_t y = __shfl_up(s2, off);
+      if (lane >= off) s2 += y;
+    }
+    if (lane < kRsWaves) wsum[kRsWaves + lane] = s2;
+  }
+  __syncthreads();
+  const uint32_t before = wave > 0 ? wsum[kRsWaves + wave - 1] : 0u;
+  *total = wsum[2 * kRsWaves - 1];
+  __syncthreads();
+  return before + x - v;
+}
+
+// zeros among the first i elements of a matrix level
+__device__ __forceinline__ uint32_t rs_rank0(const uint32_t* bits, const uint32_t* dir, uint32_t i) {
+  const uint32_t wi = i >> 5, sh = i & 31u;
+  const uint32_t below = sh ? (0xffffffffu >> (32u - sh)) : 0u;
+  return dir[wi] + (uint32_t)__popc(~bits[wi] & below);
+}
+
+__global__ __launch_bounds__(kRsThreads) void running_topk_long_kernel(
+    const float* __restrict__ scores, const float* __restrict__ log_decay,
+    int* __restrict__ keep_until, int* __restrict__ cutoff, uint32_t* __restrict__ ws, int Hkv,
+    int S, int n_sink, int window, int k) {
+  __shared__ uint32_t lds[kRsLdsWords];
+  __shared__ uint32_t wsum[2 * kRsWaves];
+  const long row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float lam = log_decay ? log_decay[row % Hkv] : 0.f;
+  const float* sc = scores + row * S;
+  int* until = keep_until + row * S;
+  int* cut = cutoff ? cutoff + row * S : nullptr;
+  const RsLayout ly = rs_layout(S, n_sink);
+  const int n = ly.n, L = ly.L, nw = ly.nw;
+  if (k == 0 || n == 0) {  // no pool ranking: tokens leave with the window
+    for (int t = tid; t < S; t += kRsThreads) {
+      until[t] = t >= n_sink ? min(S, t + window) : S;
+      if (cut) cut[t] = -1;
+    }
+    return;
+  }
+  uint32_t* w = ws + row * ly.stride;
+  uint2* kp0 = reinterpret_cast<uint2*>(w + ly.kp0);
+  uint2* kp1 = reinterpret_cast<uint2*>(w + ly.kp1);
+  uint32_t* rk = w + ly.rk;
+  uint32_t* v0 = w + ly.v0;
+  uint32_t* v1 = w + ly.v1;
+  uint32_t* wb = w + ly.wb;
+  uint32_t* wd = w + ly.wd;
+  uint32_t* zt = w + ly.zt;
+  const int steps = ly.cw / 64;  // a multiple of kRsChunk
+  const int ebase = wave * ly.cw + lane;  // this lane's element of step m: ebase + 64 m
+  const uint64_t lt = (1ull << lane) - 1ull;
+  // Runs proc(m, value) over the wave's steps in order, the values of step
+  // m loaded by load(m); each chunk's loads go out before the previous
+  // chunk is processed.
+  auto each = [&](auto load, auto proc) {
+    using V = decltype(load(0));
+    V cur[kRsChunk], nxt[kRsChunk];
+#pragma unroll
+    for (int j = 0; j < kRsChunk; ++j) cur[j] = load(j);
+    for (int m0 = 0; m0 < steps; m0 += kRsChunk) {
+      const int mn = m0 + kRsChunk < steps ? m0 + kRsChunk : m0;  // the last chunk reloads itself
+#pragma unroll
+      for (int j = 0; j < kRsChunk; ++j) nxt[j] = load(mn + j);
+#pragma unroll
+      for (int j = 0; j < kRsChunk; ++j) proc(m0 + j, cur[j]);
+#pragma unroll
+      for (int j = 0; j < kRsChunk; ++j) cur[j] = nxt[j];
+    }
+  };
+
+  // 1. sort pairs (complemented priority key: ascending = best first;
+  //    positions ascending on equal keys); slots past the row sort last
+  each([&](int m) {
+         const int i = ebase + 64 * m;
+         return sc[n_sink + min(i, n - 1)];
+       },
+       [&](int m, float sg) {
+         const int i = ebase + 64 * m;
+         const int p = n_sink + i;
+         kp0[i] = i < n ? make_uint2(~priority_key(sg, lam, p), (uint32_t)p)
+                        : make_uint2(0xffffffffu, 0xffffffffu);
+       });
+  __syncthreads();
+  uint32_t* cnt = lds;                    // [wave][digit] counts
+  uint32_t* run = lds + 256 * kRsWaves;   // [wave][digit] running offsets
+  for (int pass = 0; pass < 4; ++pass) {
+    const int sh = 8 * pass;
+    const uint2* src = (pass & 1) ? kp1 : kp0;
+    uint2* dst = (pass & 1) ? kp0 : kp1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) cnt[wave * 256 + 64 * q + lane] = 0u;  // this wave's row
+    each([&](int m) { return src[ebase + 64 * m].x; },
+         [&](int, uint32_t kx) { atomicAdd(&cnt[wave * 256 + ((kx >> sh) & 255u)], 1u); });
+    __syncthreads();
+    // exclusive offsets in (digit, wave) order; thread t owns entries 4t..4t+3
+    uint32_t e4[4], tot = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = 4 * tid + q;  // digit e / 16, wave e % 16
+      e4[q] = cnt[(e % kRsWaves) * 256 + e / kRsWaves];
+      tot += e4[q];
+    }
+    uint32_t total;
+    uint32_t at = rs_block_scan(tot, wsum, &total);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = 4 * tid + q;
+      run[(e % kRsWaves) * 256 + e / kRsWaves] = at;
+      at += e4[q];
+    }
+    __syncthreads();
+    each([&](int m) { return src[ebase + 64 * m]; },
+         [&](int, uint2 e) {
+           const uint32_t d = (e.x >> sh) & 255u;
+           uint64_t mk = ~0ull;  // lanes of this step with the same digit
+#pragma unroll
+           for (int b = 0; b < 8; ++b) {
+             const uint64_t bb = __ballot((d >> b) & 1u);
+             mk &= ((d >> b) & 1u) ? bb : ~bb;
+           }
+           const uint32_t below = (uint32_t)__popcll(mk & lt);
+           const uint32_t off = run[wave * 256 + d];
+           dst[off + below] = e;
+           if (below == 0) run[wave * 256 + d] = off + (uint32_t)__popcll(mk);
+         });
+    __syncthreads();
+  }
+  // four passes end in kp0: index = rank
+
+  // 2. ranks in position order, then the wavelet matrix over them
+  each([&](int m) { return kp0[ebase + 64 * m].y; },
+       [&](int m, uint32_t p) {
+         const int r = ebase + 64 * m;
+         if (r < n) rk[p - (uint32_t)n_sink] = (uint32_t)r;
+       });
+  __syncthreads();
+  each([&](int m) { return rk[min(ebase + 64 * m, n - 1)]; },
+       [&](int m, uint32_t x) {
+         const int i = ebase + 64 * m;
+         v0[i] = i < n ? x : 0xffffffffu;
+       });
+  __syncthreads();
+  uint32_t* wz = lds;  // zeros per wave
+  for (int lv = 0; lv < L; ++lv) {
+    const int bit = L - 1 - lv;
+    const uint32_t* src = (lv & 1) ? v1 : v0;
+    uint32_t* dst = (lv & 1) ? v0 : v1;
+    uint32_t z = 0;
+    each([&](int m) { return src[ebase + 64 * m]; },
+         [&](int, uint32_t x) { z += (uint32_t)__popcll(~__ballot((x >> bit) & 1u)); });
+    if (lane == 0) wz[wave] = z;
+    __syncthreads();
+    uint32_t zr = 0, Z = 0;
+    for (int q = 0; q < kRsWaves; ++q) {
+      const uint32_t zq = wz[q];
+      zr += q < wave ? zq : 0u;
+      Z += zq;
+    }
+    uint32_t orun = (uint32_t)(wave * ly.cw) - zr;
+    uint32_t* bl = wb + (long)lv * nw;
+    uint32_t* dl = wd + (long)lv * nw;
+    each([&](int m) { return src[ebase + 64 * m]; },
+         [&](int m, uint32_t x) {
+           const bool one = (x >> bit) & 1u;
+           const uint64_t B = __ballot(one);
+           // lanes 0..3 write the two bit words and the two zero counts
+           const int wi = (wave * ly.cw + 64 * m) >> 5;
+           const uint32_t z0 = (uint32_t)__popc(~(uint32_t)B);
+           if (lane < 4) {
+             uint32_t* tp = lane < 2 ? bl : dl;
+             const uint32_t val = lane == 0 ? (uint32_t)B : lane == 1 ? (uint32_t)(B >> 32)
+                                : lane == 2 ? zr : zr + z0;
+             tp[wi + (lane & 1)] = val;
+           }
+           if (one) dst[Z + orun + (uint32_t)__popcll(B & lt)] = x;
+           else dst[zr + (uint32_t)__popcll(~B & lt)] = x;
+           zr += (uint32_t)__popcll(~B);
+           orun += (uint32_t)__popcll(B);
+         });
+    if (tid == 0) {
+      bl[nw - 1] = 0xffffffffu;
+      dl[nw - 1] = Z;
+      zt[lv] = Z;
+    }
+    __syncthreads();
+  }
+
+}
+
+// 3. cutoff ranks (n while the pool holds fewer than k tokens) and the
+// cutoff tokens, by one descent of the matrix per query; kRsBatch queries
+// of a thread descend together.  Many workgroups per row.
+#ifndef KVPOP_RQ_THREADS
+#define KVPOP_RQ_THREADS 128
+#endif
+#ifndef KVPOP_RQ_BATCH
+#define KVPOP_RQ_BATCH 2
+#endif
+constexpr int kRqThreads = KVPOP_RQ_THREADS;
+constexpr int kRqBatch = KVPOP_RQ_BATCH;  // queries (searches) of a thread in flight together
+__global__ __launch_bounds__(kRqThreads) void running_topk_cut_kernel(
+    int* __restrict__ cutoff, uint32_t* __restrict__ ws, int S, int n_sink, int window, int k,
+    int blocks_per_row) {
+  const long row = blockIdx.x / blocks_per_row;
+  const int blk = blockIdx.x - (int)(row * blocks_per_row);
+  const RsLayout ly = rs_layout(S, n_sink);
+  const int n = ly.n, L = ly.L, nw = ly.nw;
+  if (k == 0 || n == 0) return;  // the first kernel wrote the row
+  uint32_t* w = ws + row * ly.stride;
+  const uint2* kp0 = reinterpret_cast<const uint2*>(w + ly.kp0);
+  const uint32_t* B = w + ly.wb;
+  const uint32_t* Dd = w + ly.wd;
+  const uint32_t* Zt = w + ly.zt;
+  uint32_t* cr = w + ly.cr;
+  int* cut = cutoff ? cutoff + row * S : nullptr;
+  const uint32_t uk = (uint32_t)k;
+  const int d0 = blk * kRqThreads * kRqBatch + (int)threadIdx.x;
+  uint32_t lo[kRqBatch], hi[kRqBatch], kk[kRqBatch], val[kRqBatch];
+  bool act[kRqBatch];
+#pragma unroll
+  for (int j = 0; j < kRqBatch; ++j) {
+    const long d = (long)d0 + (long)j * kRqThreads;
+    const long pool = min((long)n, max(0L, d - window - n_sink + 1));
+    act[j] = d < S && pool >= (long)uk;
+    lo[j] = 0;
+    hi[j] = (uint32_t)pool;
+    kk[j] = uk;
+    val[j] = 0;
+  }
+  for (int lv = 0; lv < L; ++lv) {
+    const uint32_t Z = Zt[lv];
+    const uint32_t* Bl = B + (long)lv * nw;
+    const uint32_t* Dl = Dd + (long)lv * nw;
+#pragma unroll
+    for (int j = 0; j < kRqBatch; ++j) {
+      const uint32_t zl = rs_rank0(Bl, Dl, lo[j]), zh = rs_rank0(Bl, Dl, hi[j]);
+      const uint32_t zc = zh - zl;
+      const bool down = kk[j] <= zc;  // the k-th smallest has this bit clear
+      kk[j] = down ? kk[j] : kk[j] - zc;
+      lo[j] = down ? zl : Z + lo[j] - zl;
+      hi[j] = down ? zh : Z + hi[j] - zh;
+      val[j] |= down ? 0u : 1u << (L - 1 - lv);
+    }
+  }
+  uint32_t tok[kRqBatch];
+#pragma unroll
+  for (int j = 0; j < kRqBatch; ++j) tok[j] = kp0[act[j] ? val[j] : 0u].y;
+#pragma unroll
+  for (int j = 0; j < kRqBatch; ++j) {
+    const long d = (long)d0 + (long)j * kRqThreads;
+    if (d < S) {
+      cr[d] = act[j] ? val[j] : (uint32_t)n;
+      if (cut) cut[d] = act[j] ? (int)tok[j] : -1;
+    }
+  }
+}
+
+// 4. keep_until[t] = the first d >= t + w with c(d) < rank(t) (c never
+// increases), by binary search; kRqBatch tokens of a thread search together.
+__global__ __launch_bounds__(kRqThreads) void running_topk_until_kernel(
+    int* __restrict__ keep_until, const uint32_t* __restrict__ ws, int S, int n_sink, int window,
+    int k, int blocks_per_row) {
+  const long row = blockIdx.x / blocks_per_row;
+  const int blk = blockIdx.x - (int)(row * blocks_per_row);
+  const RsLayout ly = rs_layout(S, n_sink);
+  const int n = ly.n;
+  if (k == 0 || n == 0) return;
+  const uint32_t* w = ws + row * ly.stride;
+  const uint32_t* rk = w + ly.rk;
+  const uint32_t* C = w + ly.cr;
+  int* until = keep_until + row * S;
+  const int t0 = blk * kRqThreads * kRqBatch + (int)threadIdx.x;
+  int lo[kRqBatch], hi[kRqBatch];
+  uint32_t r[kRqBatch];
+#pragma unroll
+  for (int j = 0; j < kRqBatch; ++j) {
+    const int t = t0 + j * kRqThreads;
+    const bool srch = t < S && t >= n_sink && (long)t + window < S;
+    r[j] = rk[srch ? t - n_sink : 0];
+    lo[j] = srch ? t + window : S;
+    hi[j] = S;
+  }
+  for (int it = 0; it < 32; ++it) {  // intervals below 2^31 close within 31 halvings
+    bool more = false;
+#pragma unroll
+    for (int j = 0; j < kRqBatch; ++j) {
+      if (lo[j] < hi[j]) {
+        const int mid = (lo[j] + hi[j]) >> 1;
+        if (C[mid] >= r[j]) lo[j] = mid + 1;
+        else hi[j] = mid;
+      }
+      more = more || lo[j] < hi[j];
+    }
+    if (!__any(more)) break;
+  }
+#pragma unroll
+  for (int j = 0; j < kRqBatch; ++j) {
+    const int t = t0 + j * kRqThreads;
+    if (t < S) until[t] = lo[j];
+  }
+}
+
 }  // namespace
 
-int running_topk_max_len() { return 16 * kRtChunksPerSegLong * 64; }
+int running_topk_max_len() { return KVPOP_RT_MAX_LEN; }
+
+size_t running_topk_workspace_bytes(int B, int Hkv, int S, int n_sink) {
+  if (S <= KVPOP_RT_LONG_MIN) return 0;
+  return (size_t)B * Hkv * (size_t)rs_layout(S, n_sink).stride * sizeof(uint32_t);
+}
 
 hipError_t launch_running_topk(int B, int Hkv, int S, int n_sink, int window, int budget,
                                const float* scores, const float* log_decay, int* keep_until,
-                               int* cutoff, hipStream_t st) {
+                               int* cutoff, void* workspace, hipStream_t st) {
   const int k = budget - n_sink - window;
+  if (S > KVPOP_RT_LONG_MIN) {
+    uint32_t* ws = static_cast<uint32_t*>(workspace);
+    const long rows = (long)B * Hkv;
+    hipLaunchKernelGGL(running_topk_long_kernel, dim3((unsigned)rows), dim3(kRsThreads), 0, st,
+                       scores, log_decay, keep_until, cutoff, ws, Hkv, S, n_sink, window, k);
+    const int bpr = (S + kRqThreads * kRqBatch - 1) / (kRqThreads * kRqBatch);
+    hipLaunchKernelGGL(running_topk_cut_kernel, dim3((unsigned)(rows * bpr)), dim3(kRqThreads), 0,
+                       st, cutoff, ws, S, n_sink, window, k, bpr);
+    hipLaunchKernelGGL(running_topk_until_kernel, dim3((unsigned)(rows * bpr)), dim3(kRqThreads), 0,
+                       st, keep_until, ws, S, n_sink, window, k, bpr);
+    return hipGetLastError();
+  }
   const int blocks_per_row = (S + 63) / 64;
   const long grid = (long)B * Hkv * blocks_per_row;
   const int n_chunks = (S - (n_sink & ~63) + 63) / 64;
@@ -214,8 +621,7 @@ hipError_t launch_running_topk(int B, int Hkv, int S, int n_sink, int window, in
   int nseg = n_chunks <= 4 * kRtChunksPerSeg ? 4 : n_chunks <= 8 * kRtChunksPerSeg ? 8 : 16;
   const long waves_cap = 4L * 4 * device_cu_count();
   while (nseg < 16 && grid * nseg * 2 <= waves_cap && n_chunks >= nseg * 4) nseg *= 2;
-  if (n_chunks > 16 * kRtChunksPerSeg) go(running_topk_kernel<16, kRtChunksPerSegLong>, 16);
-  else if (nseg == 4) go(running_topk_kernel<4, kRtChunksPerSeg>, 4);
+  if (nseg == 4) go(running_topk_kernel<4, kRtChunksPerSeg>, 4);
   else if (nseg == 8) go(running_topk_kernel<8, kRtChunksPerSeg>, 8);
   else go(running_topk_kernel<16, kRtChunksPerSeg>, 16);
   return hipGetLastError();

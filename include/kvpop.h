@@ -127,14 +127,21 @@ kvpop_status kvpop_fwd_lse(const kvpop_dims* dims, const void* q, const void* k,
  *   cutoff:     nullable int32 [B][Hkv][S]: cutoff[d] = the k-th best token
  *               of P_d (the teacher's cutoff token), -1 while |P_d| < k or
  *               when k = 0.
+ *   workspace:  kvpop_running_topk_workspace_bytes(batch, n_kv_heads,
+ *               seq_len, n_sink) bytes, 16-byte aligned, no initialisation
+ *               needed (sort buffers, the rank structure and the cutoff
+ *               ranks of rows past 8192 tokens, which take O(S log S) work
+ *               like App. C.2's Fenwick sweep); NULL when that size is 0.
  * Errors: INVALID_ARGUMENT for non-positive sizes, s < 0, w < 0,
- * budget < s + w, a NULL scores or keep_until, misaligned pointers;
- * UNSUPPORTED for seq_len > 131072.
+ * budget < s + w, a NULL scores or keep_until, misaligned pointers, a
+ * missing workspace; WORKSPACE_TOO_SMALL; UNSUPPORTED for seq_len > 2^24.
  * The result is exact (integer outputs, no rounding-order dependence).
  */
+size_t kvpop_running_topk_workspace_bytes(int batch, int n_kv_heads, int seq_len, int n_sink);
 kvpop_status kvpop_running_topk(int batch, int n_kv_heads, int seq_len, int n_sink, int window,
                                 int budget, const float* scores, const float* log_decay,
-                                int32_t* keep_until, int32_t* cutoff, hipStream_t stream);
+                                int32_t* keep_until, int32_t* cutoff, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
 
 /*
  * kvpop_fwd_lse_sparse -- main causal pass with the sparse normalizer (and

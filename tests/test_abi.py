@@ -203,15 +203,24 @@ def test_python_binding_rejects_host_tensors():
 def test_running_topk_and_sparse_lse_validation(lib):
     # every call below fails its host-side checks before any launch
     rt = lib.kvpop_running_topk
-    assert rt(1, 8, 4096, 4, 128, 100, GOOD, None, GOOD, None, None) == 1   # budget < s + w
-    assert rt(1, 8, 4096, -1, 128, 1024, GOOD, None, GOOD, None, None) == 1
-    assert rt(1, 8, 4096, 4, -2, 1024, GOOD, None, GOOD, None, None) == 1
-    assert rt(0, 8, 4096, 4, 128, 1024, GOOD, None, GOOD, None, None) == 1
-    assert rt(1, 8, 4096, 4, 128, 1024, None, None, GOOD, None, None) == 1
-    assert rt(1, 8, 4096, 4, 128, 1024, GOOD, None, None, None, None) == 1
-    assert rt(1, 8, 4096, 4, 128, 1024, P(0x10002), None, GOOD, None, None) == 1  # misaligned
-    assert rt(1, 8, 4096, 4, 128, 1024, GOOD, P(0x10001), GOOD, None, None) == 1
-    assert rt(1, 8, 131073, 4, 128, 1024, GOOD, None, GOOD, None, None) == 2    # longest row 131072
+    assert rt(1, 8, 4096, 4, 128, 100, GOOD, None, GOOD, None, None, 0, None) == 1   # budget < s + w
+    assert rt(1, 8, 4096, -1, 128, 1024, GOOD, None, GOOD, None, None, 0, None) == 1
+    assert rt(1, 8, 4096, 4, -2, 1024, GOOD, None, GOOD, None, None, 0, None) == 1
+    assert rt(0, 8, 4096, 4, 128, 1024, GOOD, None, GOOD, None, None, 0, None) == 1
+    assert rt(1, 8, 4096, 4, 128, 1024, None, None, GOOD, None, None, 0, None) == 1
+    assert rt(1, 8, 4096, 4, 128, 1024, GOOD, None, None, None, None, 0, None) == 1
+    assert rt(1, 8, 4096, 4, 128, 1024, P(0x10002), None, GOOD, None, None, 0, None) == 1  # misaligned
+    assert rt(1, 8, 4096, 4, 128, 1024, GOOD, P(0x10001), GOOD, None, None, 0, None) == 1
+    assert rt(1, 8, (1 << 24) + 1, 4, 128, 1024, GOOD, None, GOOD, None, None, 0, None) == 2  # longest row 2^24
+    # rows up to 8192 tokens need no workspace; longer rows do
+    wsb = lib.kvpop_running_topk_workspace_bytes
+    assert wsb(1, 8, 8192, 4) == 0 and wsb(1, 8, 4096, 4) == 0
+    need = wsb(1, 8, 16384, 4)
+    assert need >= 8 * 16384 * 4 * 8 and wsb(2, 8, 16384, 4) == 2 * need
+    assert wsb(1, 8, (1 << 24) + 1, 4) == 0 and wsb(0, 8, 16384, 4) == 0
+    assert rt(1, 8, 16384, 4, 128, 1024, GOOD, None, GOOD, None, None, 0, None) == 1     # no workspace
+    assert rt(1, 8, 16384, 4, 128, 1024, GOOD, None, GOOD, None, P(0x10008), need, None) == 1  # misaligned
+    assert rt(1, 8, 16384, 4, 128, 1024, GOOD, None, GOOD, None, GOOD, need - 16, None) == 3   # too small
     sp = lib.kvpop_fwd_lse_sparse
     d = kv.dims(1, 32, 8, 4096, 128)
     assert sp(ctypes.byref(d), GOOD, GOOD, None, None, 0, GOOD, None, 0, None, 0, None) == 1     # no mask

@@ -88,12 +88,14 @@ def test_running_topk_full_size(kv, S, budget, w):
 
 @pytest.mark.parametrize("S,budget,w,s", [(40000, 5000, 256, 4), (65536, 6000, 128, 70),
                                           (33000, 300, 16, 0), (65600, 4000, 64, 4),
-                                          (100000, 9000, 256, 4), (131072, 8192, 256, 130)])
+                                          (100000, 9000, 256, 4), (131072, 8192, 256, 130),
+                                          (300000, 20000, 512, 4), (8193, 1000, 64, 4),
+                                          (40000, 37000, 256, 4)])
 def test_running_topk_longest_rows(kv, S, budget, w, s):
-    """Rows past 32768 positions take 16 segment waves per token block, rows
-    past 65536 segments of 128 chunks (the longest rows the kernel takes are
-    131072); a small budget makes most tokens leave early, a large one keeps
-    many to the end."""
+    """Rows past 8192 tokens take the sort + wavelet-matrix kernel: rank
+    structures past LDS (S > 38912), the shortest such row, a budget above
+    most of the row; a small budget makes most tokens leave early, a large
+    one keeps many to the end."""
     sc = synth.scores((1, 2, S), seed=S + budget, kind="ties" if S == 33000 else "normal")
     u, c, ou, oc = _topk(kv, sc, s, w, budget, [0.0, 2e-5])
     assert np.array_equal(u, ou)
@@ -101,7 +103,7 @@ def test_running_topk_longest_rows(kv, S, budget, w, s):
 
 
 def test_running_topk_rejects_rows_past_its_limit(kv):
-    sc = torch.zeros((1, 1, 131073), dtype=torch.float32, device="cuda")
+    sc = torch.zeros((1, 1, (1 << 24) + 1), dtype=torch.float32, device="cuda")
     with pytest.raises(kv.KvpopError):
         kv.running_topk(sc, 4, 16, 64)
 
@@ -300,9 +302,9 @@ def test_sparse_abi_errors(kv):
     u = torch.zeros((1, 1, 64), dtype=torch.int32, device="cuda")
     p = ctypes.c_void_p(sc.data_ptr())
     pu = ctypes.c_void_p(u.data_ptr())
-    assert L.kvpop_running_topk(1, 1, 64, 4, 16, 10, p, None, pu, None, None) == 1  # budget < s + w
-    assert L.kvpop_running_topk(1, 1, 64, 4, 16, 30, None, None, pu, None, None) == 1
-    assert L.kvpop_running_topk(0, 1, 64, 4, 16, 30, p, None, pu, None, None) == 1
+    assert L.kvpop_running_topk(1, 1, 64, 4, 16, 10, p, None, pu, None, None, 0, None) == 1  # budget < s + w
+    assert L.kvpop_running_topk(1, 1, 64, 4, 16, 30, None, None, pu, None, None, 0, None) == 1
+    assert L.kvpop_running_topk(0, 1, 64, 4, 16, 30, p, None, pu, None, None, 0, None) == 1
     d = kv.dims(1, 2, 1, 64, 96)
     assert L.kvpop_fwd_lse_sparse(ctypes.byref(d), p, p, None, pu, 0, p, None, 0, None, 0, None) == 2  # D = 96
     d = kv.dims(1, 2, 1, 64, 64)
