@@ -44,19 +44,19 @@ FP32_VECTOR_PEAK_TFS = 157.3     # MI355X fp32 vector (counts packed FMA; one FM
 # only for the kernel code it was taken on (sources_digest): bench reports
 # null once that changes.
 TRAFFIC_SOURCES = ("future_target.hip", "common.h", "launch.h")
-TRAFFIC = {"sha256": "c15e63d21d9e4c1e1fb20aa47564ed7aedaa86a497a5b7f1b30bde5ba3347512",
-           "fetch_bytes": 2 * (446589.3 + 4319.0) * 1024, "write_bytes": (8576.0 + 1024.0) * 1024}
+TRAFFIC = {"sha256": "ea2334b72027295d40a618d36fbedd75f07b2ac8d2ca5c0c104302f44d1dc79d",
+           "fetch_bytes": 2 * (446061.5 + 4319.0) * 1024, "write_bytes": (8576.0 + 1024.0) * 1024}
 # HBM bytes per dispatch of the HBM-bound kernels the bench reports, from the
 # same pair of counter runs with the same scaling (FETCH_SIZE x 2, WRITE_SIZE
 # x 1), each valid only for the sources it was taken on.
 COUNTERS = {
     "decode_step": {"sources": ("decode_step.hip", "decode_dev.h", "cache_step_dev.h", "mlstm_dev.h",
                                 "common.h", "launch.h"),
-                    "fetch_kib": 532938.0, "write_kib": 824.3,
+                    "fetch_kib": 532937.5, "write_kib": 824.3,
                     "per": "decode_step_kernel<128, 4> launch: one layer-step of 64 sequences x 8 KV "
                            "heads over budget 4096"},
     "select_gather_prefill": {"sources": ("select.hip", "common.h", "launch.h"),
-                              "fetch_kib": 20619.7, "write_kib": 33281.2,
+                              "fetch_kib": 20619.6, "write_kib": 33281.6,
                               "per": "select_kernel<32, true, true> launch: 8 rows of 32768 scores, "
                                      "budget 8192, selection and compaction of K and V (32 "
                                      "workgroups per row)"},
@@ -65,11 +65,11 @@ COUNTERS = {
                              "per": "select_kernel<32, true, false> launch: 512 rows of 32768 scores, "
                                     "budget 4096"},
     "gather_decode_prefix": {"sources": ("select.hip", "common.h", "launch.h"),
-                             "fetch_kib": 532514.9, "write_kib": 1048659.8,
+                             "fetch_kib": 532515.1, "write_kib": 1048649.4,
                              "per": "gather_kernel launch: 512 rows x 4096 slots of K and V"},
 }
-COUNTER_SHA = {"decode": "b99fdf6ad3417f726cdde4ed792957dd0ab5e097189e64c3800b046820eb6bc8",
-               "select": "17e13c3ed9187a5552e1d9b1aa4cf0b5d259330cd7293785bce5de1b38d43288"}
+COUNTER_SHA = {"decode": "e13a93995337dc717550ad10a07325b82b8cdc39af6460c184f22176236abdfc",
+               "select": "5ce051bb1a59368f64d107b40b90e5b731dc660263b2d45f59f60d506ae08149"}
 METRIC = "future-attn target keys/s + MFMA util; bounded-cache decode steps/s + HBM util"
 
 
